@@ -1,0 +1,185 @@
+"""Seeded synthetic inputs for dense MLA decode.
+
+This module only draws and lays out inputs; it holds none of the attention
+arithmetic.  Both the CPU oracle (tests) and the GPU path consume what it
+returns, so the two sides always see bit-identical bf16 data.
+
+Shapes follow the problem statement on the FlashMLA overview page
+("[DeepSeek-3] FlashMLA", section 3, tensor shapes for dense decode):
+
+    q             [batch, s_q, h_q, 576]            bf16
+    kv_cache      [num_blocks, 64, 1, 576]           bf16 (K = all 576, V = first 512)
+    block_table   [batch, max_blocks_per_seq]        int32
+    cache_seqlens [batch]                            int32
+
+bf16 tensors are carried as numpy ``uint16`` bit patterns.
+
+Recipe (all seeded by ``numpy.random.default_rng(seed)``), in draw order:
+  1. sequence lengths (fixed lists, or integers uniform on [lo, hi] inclusive);
+  2. a random permutation of the physical page pool; pages are dealt to the
+     requests in order, no page is shared between requests;
+  3. q as fp32 N(0,1) rounded to bf16 (round to nearest even);
+  4. the whole page pool as fp32 N(0,1) rounded to bf16.
+Then every byte the method must never read is overwritten with a poison
+value: unused pages, the tail tokens of each request's last page
+(token >= L), and the padding entries of the block table, which point at an
+unused (poisoned) page.  A leak through any of these shows as a gross error.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+PAGE = 64          # tokens per KV page
+D_QK = 576         # 512 latent + 64 RoPE dims, used by QK^T
+D_V = 512          # latent dims, used by PV
+POISON = 1.0e4     # fp32 value written where no read may land (bf16 -> 9984)
+SOFTMAX_SCALE = float(np.float32(192.0 ** -0.5))  # original q head = 128 + 64 dims
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest, ties to even); return uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    r = r.astype(np.uint16)
+    if nan.any():
+        r[nan] = 0x7FC0
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to fp32."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+POISON_BITS = int(f32_to_bf16_bits(np.array([POISON], np.float32))[0])
+
+
+@dataclasses.dataclass
+class MlaInputs:
+    name: str
+    q: np.ndarray             # uint16 [b, s_q, h_q, 576]
+    kv_cache: np.ndarray      # uint16 [num_blocks, 64, 1, 576]
+    block_table: np.ndarray   # int32 [b, max_blocks]
+    cache_seqlens: np.ndarray  # int32 [b]
+    softmax_scale: float
+
+    @property
+    def batch(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def s_q(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def h_q(self) -> int:
+        return int(self.q.shape[2])
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.kv_cache.shape[0])
+
+    @property
+    def max_blocks(self) -> int:
+        return int(self.block_table.shape[1])
+
+
+# The five synthetic workloads (tiny parity case, TP-sharded memory-bound
+# decode, compute-bound decode, ragged MTP decode, long-context decode).
+CONFIGS = {
+    1: dict(name="tiny_b2_hq16_L100_257", batch=2, s_q=1, h_q=16, seqlens=[100, 257],
+            pool=16, max_blocks=5),
+    2: dict(name="membound_b16_hq16_L1024-4096", batch=16, s_q=1, h_q=16, seqlens=(1024, 4096),
+            pool=1024, max_blocks=64),
+    3: dict(name="compute_b64_hq128_L4096", batch=64, s_q=1, h_q=128, seqlens=[4096] * 64,
+            pool=4096, max_blocks=64),
+    4: dict(name="mtp_b128_sq2_hq128_L512-16384", batch=128, s_q=2, h_q=128,
+            seqlens=(512, 16384), pool=None, max_blocks=256),
+    5: dict(name="long_b2_hq128_L131072_65537", batch=2, s_q=1, h_q=128,
+            seqlens=[131072, 65537], pool=3073, max_blocks=2048),
+}
+
+
+def _draw_normal_bf16(rng: np.random.Generator, shape, chunk_elems: int = 1 << 24) -> np.ndarray:
+    """fp32 N(0,1) draws rounded to bf16, generated in fixed-size chunks."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, chunk_elems):
+        e = min(n, s + chunk_elems)
+        out[s:e] = f32_to_bf16_bits(rng.standard_normal(e - s, dtype=np.float32))
+    return out.reshape(shape)
+
+
+def make_inputs(batch: int, s_q: int, h_q: int, seqlens, pool: int | None, max_blocks: int,
+                seed: int, softmax_scale: float = SOFTMAX_SCALE, name: str = "custom",
+                tail_poison: float = POISON) -> MlaInputs:
+    """Draw one seeded workload following the recipe in the module docstring.
+
+    ``seqlens`` is a list of lengths or a ``(lo, hi)`` pair for integers
+    uniform on [lo, hi].  ``pool`` is the physical page count; it is raised,
+    if needed, so that at least one page stays unused (the poisoned target of
+    block-table padding).
+    """
+    rng = np.random.default_rng(seed)
+    if isinstance(seqlens, tuple):
+        lo, hi = seqlens
+        lens = rng.integers(lo, hi + 1, size=batch).astype(np.int32)
+    else:
+        lens = np.asarray(seqlens, dtype=np.int32)
+        assert lens.shape == (batch,)
+    npages = [(int(L) + PAGE - 1) // PAGE for L in lens]
+    need = sum(npages)
+    if max(npages, default=0) > max_blocks:
+        raise ValueError("a sequence needs more pages than max_blocks")
+    pool = max(pool or 0, need + 1)
+    perm = rng.permutation(pool).astype(np.int32)
+    spare = int(perm[need])  # first unused page: target of block-table padding
+    block_table = np.full((batch, max_blocks), spare, dtype=np.int32)
+    at = 0
+    for b, n in enumerate(npages):
+        block_table[b, :n] = perm[at:at + n]
+        at += n
+    q = _draw_normal_bf16(rng, (batch, s_q, h_q, D_QK))
+    kv = _draw_normal_bf16(rng, (pool, PAGE, 1, D_QK))
+    poison = int(f32_to_bf16_bits(np.array([tail_poison], np.float32))[0])
+    used = np.zeros(pool, dtype=bool)
+    used[perm[:need]] = True
+    kv[~used] = poison
+    for b, n in enumerate(npages):
+        tail = int(lens[b]) - (n - 1) * PAGE
+        if n and tail < PAGE:
+            kv[block_table[b, n - 1], tail:] = poison
+    return MlaInputs(name=name, q=q, kv_cache=kv, block_table=block_table,
+                     cache_seqlens=lens, softmax_scale=float(softmax_scale))
+
+
+def config_inputs(index: int) -> MlaInputs:
+    """Workload ``index`` (1..5) with seed ``index``."""
+    c = CONFIGS[index]
+    return make_inputs(c["batch"], c["s_q"], c["h_q"], c["seqlens"], c["pool"],
+                       c["max_blocks"], seed=index, name=c["name"])
+
+
+def algorithmic_work(seqlens, s_q: int, h_q: int) -> tuple[float, float]:
+    """(FLOPs, bytes) the method must do for one decode call.
+
+    FLOPs = 2 * s_q * h_q * sum(L) * (576 + 512): the QK^T and PV products.
+    Bytes = bf16 KV read once per request, q read, out written (bf16), lse
+    written (fp32).  Masked tail tokens, split partials and the block table
+    are overhead and are not counted.
+    """
+    sl = np.asarray(seqlens, dtype=np.int64)
+    R = s_q * h_q
+    total = int(sl.sum())
+    b = int(sl.shape[0])
+    flops = 2.0 * R * total * (D_QK + D_V)
+    nbytes = 2.0 * (total * D_QK + b * R * D_QK + b * R * D_V) + 4.0 * b * R
+    return flops, nbytes
+
+
+def pages_needed(L: int) -> int:
+    return int(math.ceil(int(L) / PAGE))

@@ -1,0 +1,194 @@
+"""CPU oracle for dense MLA decode (weight-absorbed, paged).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything under
+``oracle/``.  The GPU library never links, imports or falls back to it, and it
+shares no code with the GPU path: its only inputs are the seeded arrays that
+``decode_attention_mla_amd.workloads`` draws.
+
+Arithmetic is float64 throughout (bf16 inputs widen exactly).  The
+functions follow these passages (page titles as on the web):
+
+* "[DeepSeek-3] FlashMLA" (xutianle.me), section 3: the reference computation
+  score = q @ kv[..., :576]^T, score *= softmax_scale, prob = softmax(score),
+  out = prob @ kv[..., :512]; out is [b, s_q, h_q, 512], lse is [b, h_q, s_q].
+* same page, section 4: a request's logical page j lives in physical block
+  block_table[b][j]; cache_seqlens[b] is the number of valid tokens.
+* "3.4 Attention kernel" (liuzhe1218.github.io), section on online softmax:
+  running (m, l, o~) updated with the factor e^(m - m') when the max grows,
+  and the merge of two partial states over disjoint key sets.
+* same page, FlashAttention section: the log-sum-exp written out is m + log l.
+* "[DeepSeek-3] FlashMLA", section 7, and the split-KV blog (0539edu.com),
+  section 3.2/3.3: a split whose key set is empty (l = 0, m = -inf) is
+  skipped in the merge; if every split is empty the output is 0.
+
+Readings of points the pages leave open (each one is listed with its
+justification in the design notes):
+  * softmax_scale multiplies the scores (the overview's reference code);
+  * lse is the natural log of sum(exp(scaled scores));
+  * an empty request (L = 0) gives out = 0 and lse = -inf;
+  * queries are not causally masked: every query token sees all L keys.
+
+Pins (tests/test_oracle.py): closed forms for L = 1, identical scores and
+softmax_scale = 0, a position-encoded cache under uniform weights, the
+worked QK partial sums printed on the multi-rail GEMM page, the e^(3-5)
+rescale printed on the attention-kernel page, page-permutation invariance,
+linearity, naive = online = split-then-merge, and brute force in exact
+rational arithmetic on tiny inputs.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+PAGE = 64
+D_QK = 576
+D_V = 512
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to float64 exactly."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def request_keys(kv_cache: np.ndarray, block_table_row: np.ndarray, L: int) -> np.ndarray:
+    """Gather the L valid cache rows of one request, in logical order.
+
+    Logical token t sits in page block_table_row[t // 64] at slot t % 64
+    (overview page, section 4).  Returns float64 [L, 576]; rows 0..L-1 only,
+    so tail slots of the last page and unused table entries are never read.
+    """
+    L = int(L)
+    if L == 0:
+        return np.zeros((0, D_QK), dtype=np.float64)
+    npages = (L + PAGE - 1) // PAGE
+    pages = kv_cache[np.asarray(block_table_row[:npages], dtype=np.int64)]  # [n, 64, 1, 576]
+    rows = pages.reshape(npages * PAGE, D_QK)[:L]
+    return bf16_to_f64(rows)
+
+
+def attend(qrows: np.ndarray, keys: np.ndarray, softmax_scale: float):
+    """Softmax attention of R query rows over one request's keys.
+
+    qrows float64 [R, 576]; keys float64 [L, 576] (V = keys[:, :512]).
+    Returns (out [R, 512], lse [R]).  Plain definition: scores over all 576
+    dims times softmax_scale, max-subtracted exponentials, normalised sum of
+    the first 512 dims.
+    """
+    R = qrows.shape[0]
+    if keys.shape[0] == 0:
+        return np.zeros((R, D_V)), np.full(R, -np.inf)
+    scores = (qrows @ keys.T) * softmax_scale          # [R, L]
+    m = scores.max(axis=1)
+    p = np.exp(scores - m[:, None])
+    l = p.sum(axis=1)
+    out = (p @ keys[:, :D_V]) / l[:, None]
+    lse = m + np.log(l)
+    return out, lse
+
+
+def mla_decode(q, kv_cache, block_table, cache_seqlens, softmax_scale, requests=None):
+    """Dense MLA decode for every (request, query token, head).
+
+    q uint16 [b, s_q, h_q, 576] (bf16 bits); kv_cache uint16 [nb, 64, 1, 576];
+    block_table int32 [b, max_blocks]; cache_seqlens int32 [b].
+    Returns out float64 [b, s_q, h_q, 512] and lse float64 [b, h_q, s_q].
+    ``requests`` restricts the work to a subset of request indices (the
+    other entries are left as NaN).
+    """
+    b, s_q, h_q, d = q.shape
+    assert d == D_QK
+    out = np.full((b, s_q, h_q, D_V), np.nan)
+    lse = np.full((b, h_q, s_q), np.nan)
+    todo = range(b) if requests is None else requests
+    for i in todo:
+        keys = request_keys(kv_cache, block_table[i], int(cache_seqlens[i]))
+        qrows = bf16_to_f64(q[i].reshape(s_q * h_q, D_QK))   # row r = s * h_q + h
+        o, ls = attend(qrows, keys, softmax_scale)
+        out[i] = o.reshape(s_q, h_q, D_V)
+        lse[i] = ls.reshape(s_q, h_q).T
+    return out, lse
+
+
+def mla_decode_rows(q, kv_cache, block_table, cache_seqlens, softmax_scale, picks):
+    """Outputs for a sample of (request, query token, head) triples.
+
+    Returns out float64 [n, 512] and lse float64 [n] in the order of ``picks``.
+    """
+    outs, lses = [], []
+    cache = {}
+    for (i, s, h) in picks:
+        if i not in cache:
+            cache[i] = request_keys(kv_cache, block_table[i], int(cache_seqlens[i]))
+        o, ls = attend(bf16_to_f64(q[i, s, h])[None, :], cache[i], softmax_scale)
+        outs.append(o[0])
+        lses.append(ls[0])
+    return np.array(outs), np.array(lses)
+
+
+# ---------------------------------------------------------------------------
+# Online softmax and the merge of partial states (attention-kernel page,
+# online-softmax section; overview page, section 7).
+
+def online_attend(qrows: np.ndarray, keys: np.ndarray, softmax_scale: float, block: int = PAGE):
+    """Same result as ``attend`` reached block by block with running (m, l, o~).
+
+    For each key block: m' = max(m, blockmax), l' = e^(m-m') l + sum e^(s-m'),
+    o~' = e^(m-m') o~ + sum e^(s-m') v; at the end out = o~ / l and
+    lse = m + log l.
+    """
+    R = qrows.shape[0]
+    m = np.full(R, -np.inf)
+    l = np.zeros(R)
+    acc = np.zeros((R, D_V))
+    for j in range(0, keys.shape[0], block):
+        kb = keys[j:j + block]
+        s = (qrows @ kb.T) * softmax_scale
+        m_new = np.maximum(m, s.max(axis=1))
+        scale_old = np.exp(m - m_new)          # e^(m - m'), 0 on the first block
+        p = np.exp(s - m_new[:, None])
+        l = scale_old * l + p.sum(axis=1)
+        acc = scale_old[:, None] * acc + p @ kb[:, :D_V]
+        m = m_new
+    if keys.shape[0] == 0:
+        return np.zeros((R, D_V)), np.full(R, -np.inf)
+    return acc / l[:, None], m + np.log(l)
+
+
+def rescale_factor(m_old: float, m_new: float) -> float:
+    """Factor applied to the old running sum and output when the max moves."""
+    return math.exp(m_old - m_new)
+
+
+def merge_partials(outs: np.ndarray, lses: np.ndarray):
+    """Merge split results (normalised O_i, lse_i) over disjoint key sets.
+
+    outs [n, R, 512], lses [n, R].  With M = max_i lse_i and w_i = e^(lse_i - M):
+    out = sum_i w_i O_i / sum_i w_i, lse = M + log sum_i w_i.  Splits with
+    lse_i = -inf (empty key set) get weight 0; if all are empty, out = 0 and
+    lse = -inf.
+    """
+    outs = np.asarray(outs, dtype=np.float64)
+    lses = np.asarray(lses, dtype=np.float64)
+    M = lses.max(axis=0)                                # [R]
+    empty = np.isneginf(M)
+    Ms = np.where(empty, 0.0, M)
+    w = np.exp(lses - Ms[None, :])                       # exp(-inf) = 0
+    wsum = w.sum(axis=0)
+    safe = np.where(empty, 1.0, wsum)
+    out = np.einsum("nr,nrc->rc", w, outs) / safe[:, None]
+    out[empty] = 0.0
+    lse = np.where(empty, -np.inf, Ms + np.log(safe))
+    return out, lse
+
+
+def split_then_merge(qrows: np.ndarray, keys: np.ndarray, softmax_scale: float, bounds):
+    """Attend separately over keys[bounds[k]:bounds[k+1]] and merge the parts."""
+    outs, lses = [], []
+    for a, e in zip(bounds[:-1], bounds[1:]):
+        o, ls = attend(qrows, keys[a:e], softmax_scale)
+        outs.append(o)
+        lses.append(ls)
+    return merge_partials(np.stack(outs), np.stack(lses))

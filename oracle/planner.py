@@ -1,0 +1,115 @@
+"""Reference split-KV tile planner (integer work).
+
+TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and
+``bench.py``'s ``cpu_baseline`` leg may use anything under ``oracle/``.
+
+Follows the tile-scheduler description on the FlashMLA new-kernel deep-dive
+page (nxmr.cn, section "Tile Scheduler"): count each request's KV blocks
+from its sequence length, set a per-part work cap
+payload = ceil(total / num_parts) + fixed_overhead, then walk the requests
+in order filling each part greedily, cutting a request across parts when it
+does not fit, and record how many pieces (splits) each request ends up in so
+the combine step can find them.
+
+Readings taken where the page is silent:
+  * "total" counts every request's blocks plus one fixed overhead per
+    request, and every piece a part takes costs its blocks plus the fixed
+    overhead;
+  * the last part takes whatever is left, so every block is always covered;
+  * a request with no blocks (L = 0) is still placed in a part as an empty
+    piece, so that its output (zeros, lse = -inf) is written;
+  * ``force_splits = k > 0`` replaces the greedy walk: each request is cut
+    into min(k, n_b) page-aligned pieces (at least one), earlier pieces one
+    block longer when n_b is not a multiple, one part per piece.
+
+Output layout (shared with the GPU library's planner, which must agree bit
+for bit): one row of 8 int32 per part
+  [begin_req, end_req (inclusive), begin_block (in begin_req),
+   end_block (exclusive, in end_req), begin_piece (index of begin_req's piece
+   in this part among that request's pieces), 0, 0, 0]
+and ``num_splits`` as an exclusive prefix sum over requests, length b + 1:
+request b owns partial slots [num_splits[b], num_splits[b+1]).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+PAGE = 64
+SCHED_INTS = 8
+
+
+def blocks_of(seqlens) -> list[int]:
+    return [(int(L) + PAGE - 1) // PAGE for L in seqlens]
+
+
+def plan(seqlens, num_parts: int, fixed_overhead: int = 0, force_splits: int = 0):
+    """Return (sched int32 [parts, 8], num_splits int32 [b + 1])."""
+    n = blocks_of(seqlens)
+    b = len(n)
+    if b == 0 or num_parts <= 0:
+        raise ValueError("need at least one request and one part")
+    if force_splits > 0:
+        return _plan_forced(n, force_splits)
+    F = int(fixed_overhead)
+    total = sum(nb + F for nb in n)
+    payload = -(-total // num_parts) + F            # ceil_div + fixed overhead
+    parts = []
+    pieces = [0] * b
+    req, blk = 0, 0
+    for p in range(num_parts):
+        if req >= b:
+            break
+        last_part = p == num_parts - 1
+        cap = payload
+        begin = (req, blk, pieces[req])
+        end_req, end_blk = -1, -1
+        while req < b:
+            rem = n[req] - blk
+            if last_part or rem + F <= cap:         # rest of the request fits
+                cap -= rem + F
+                pieces[req] += 1
+                end_req, end_blk = req, n[req]
+                req, blk = req + 1, 0
+                continue
+            take = cap - F
+            if take > 0:                             # cut the request here
+                blk += take
+                pieces[req] += 1
+                end_req, end_blk = req, blk
+            break
+        if end_req < 0:                              # nothing fitted: close the walk
+            continue
+        parts.append([begin[0], end_req, begin[1], end_blk, begin[2], 0, 0, 0])
+    num_splits = np.zeros(b + 1, dtype=np.int32)
+    num_splits[1:] = np.cumsum(pieces)
+    return np.array(parts, dtype=np.int32).reshape(-1, SCHED_INTS), num_splits
+
+
+def _plan_forced(n, k):
+    parts = []
+    pieces = []
+    for r, nb in enumerate(n):
+        cnt = max(1, min(k, nb))
+        q, extra = divmod(nb, cnt)
+        start = 0
+        for i in range(cnt):
+            size = q + (1 if i < extra else 0)
+            parts.append([r, r, start, start + size, i, 0, 0, 0])
+            start += size
+        pieces.append(cnt)
+    num_splits = np.zeros(len(n) + 1, dtype=np.int32)
+    num_splits[1:] = np.cumsum(pieces)
+    return np.array(parts, dtype=np.int32).reshape(-1, SCHED_INTS), num_splits
+
+
+def pieces_of(sched: np.ndarray, seqlens):
+    """Expand a plan into (part, request, block_begin, block_end, piece) tuples."""
+    n = blocks_of(seqlens)
+    out = []
+    for p, row in enumerate(np.asarray(sched)):
+        br, er, bb, eb, bp = (int(x) for x in row[:5])
+        for r in range(br, er + 1):
+            lo = bb if r == br else 0
+            hi = eb if r == er else n[r]
+            out.append((p, r, lo, hi, bp if r == br else 0))
+    return out
