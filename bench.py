@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of dense MLA decode on one MI355X; prints one JSON line.
+
+A step is one dense MLA decode call (split-KV kernel + combine kernel) over
+one batch of the synthetic workload, inputs resident in HBM.  The tile plan
+is made once per decode step and reused by every call of that step (as the
+pages prescribe for all layers of a decode step); its host time is measured
+and reported separately as ``plan_us``.  Several copies of q and the KV pool
+are rotated between steps so that the 256 MB memory-side cache cannot serve
+one step's pages to the next.
+
+Headline workload: TP-sharded memory-bound decode (batch 16, h_q 16,
+L ~ U[1024, 4096]) -> effective HBM GB/s.  The h_q = 128 workloads
+(compute-bound, ragged MTP, long context) are reported under ``extra`` in
+TFLOP/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "MLA decode TFLOPs (h_q=128) and effective HBM GB/s (h_q=16), 1 MI355X"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SRC = os.path.join(ROOT, "decode_attention_mla_amd", "csrc", "mla_decode.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(config_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except ValueError:
+        return None
+    e = d.get(config_name)
+    if not e or e.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6):
+    import torch
+    import decode_attention_mla_amd as mla
+    from decode_attention_mla_amd import workloads as W
+
+    t = time.perf_counter()
+    inp = W.config_inputs(idx)
+    log(f"[bench] config {idx} {inp.name}: inputs drawn in {time.perf_counter() - t:.1f}s")
+    flops, nbytes = W.algorithmic_work(inp.cache_seqlens, inp.s_q, inp.h_q)
+    dev = torch.device("cuda", 0)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    kv0, q0 = bf16(inp.kv_cache), bf16(inp.q)
+    kv_bytes = kv0.numel() * 2
+    rot = int(min(8, max(1, np.ceil(min_rot_bytes / kv_bytes))))
+    kvs = [kv0] + [kv0.clone() for _ in range(rot - 1)]
+    qs = [q0] + [q0.clone() for _ in range(rot - 1)]
+    bt = torch.from_numpy(inp.block_table).to(dev)
+    sl = torch.from_numpy(inp.cache_seqlens).to(dev)
+
+    # Plan once per decode step (host), timed separately.
+    reps = 50
+    t = time.perf_counter()
+    for _ in range(reps):
+        sched_np, ns_np, total = mla.get_mla_metadata_host(inp.cache_seqlens, inp.h_q, inp.s_q)
+    plan_us = (time.perf_counter() - t) / reps * 1e6
+    sched = torch.from_numpy(sched_np).to(dev)
+    ns = torch.from_numpy(ns_np).to(dev)
+    b = inp.batch
+    out = torch.empty((b, inp.s_q, inp.h_q, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((b, inp.h_q, inp.s_q), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(256, mla.mla_workspace_bytes(sched.shape[0] + b - 1, inp.h_q, inp.s_q)),
+                     dtype=torch.uint8, device=dev)
+
+    def step(i):
+        mla.mla_decode_fwd(qs[i % rot], kvs[i % rot], bt, sl, inp.softmax_scale, sched, ns, out=out, lse=lse,
+                           workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    mla.profile_start(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    main_ms, comb_ms, calls = mla.profile_stop()
+    gpu_ms = ev0.elapsed_time(ev1)
+    assert calls == steps, (calls, steps)
+    ms_per_step = wall_ms / steps
+    main_avg = main_ms / calls
+    comb_avg = comb_ms / calls
+    res = dict(
+        workload=inp.name, batch=b, s_q=inp.s_q, h_q=inp.h_q, sum_seqlen=int(inp.cache_seqlens.sum()),
+        parts=int(sched.shape[0]), total_splits=int(total), rotating_copies=rot,
+        flops=flops, bytes=nbytes, ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / steps,
+        main_kernel_ms=main_avg, combine_kernel_ms=comb_avg, plan_us=plan_us,
+        tflops=flops / (ms_per_step * 1e-3) / 1e12, gbs=nbytes / (ms_per_step * 1e-3) / 1e9,
+        main_kernel_tflops=flops / (main_avg * 1e-3) / 1e12, main_kernel_gbs=nbytes / (main_avg * 1e-3) / 1e9,
+    )
+    log(f"[bench] config {idx}: {json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()})}")
+    del kvs, qs
+    torch.cuda.empty_cache()
+    return inp, res
+
+
+def cpu_baseline(inp, work: float, scale: float, unit: str, budget_s: float = 10.0):
+    """The oracle, as it stands, on this host: whole passes over the workload
+    until ~budget_s of CPU work; returns work * passes / seconds / scale."""
+    import oracle
+    threads = 1
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()
+                             if i.get("user_api") == "blas"])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        pass
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.mla_decode(inp.q, inp.kv_cache, inp.block_table, inp.cache_seqlens, inp.softmax_scale)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or passes >= 20:
+            break
+    return dict(value=work * passes / el / scale, unit=unit, cores=threads, kind="oracle",
+                sample=f"{passes} full pass(es) of the workload in {el:.1f}s (numpy fp64, BLAS threads={threads})")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="headline workload (1..5)")
+    ap.add_argument("--no-extra", action="store_true", help="skip the h_q=128 workloads")
+    ap.add_argument("--extra-steps", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the decode path is single-GPU); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import decode_attention_mla_amd as mla
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mla.lib()
+
+    inp, head = run_workload(args.config, args.steps, args.warmup)
+    bound_hbm = head["h_q"] * head["s_q"] <= 64
+    traffic = measured_traffic(head["workload"])
+    if bound_hbm:
+        achieved = head["bytes"] / (head["main_kernel_ms"] * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,
+                    traffic=traffic)
+        value, unit = head["gbs"], "GB/s"
+    else:
+        achieved = head["flops"] / (head["main_kernel_ms"] * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=achieved, peak=MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=achieved / MFMA_PEAK_TFLOPS, traffic=traffic)
+        value, unit = head["tflops"], "TFLOP/s"
+    roof["kernel"] = "mla_splitkv_kernel"
+    cpu = None
+    if not args.no_cpu:
+        cpu = (cpu_baseline(inp, head["bytes"], 1e9, "GB/s") if bound_hbm
+               else cpu_baseline(inp, head["flops"], 1e12, "TFLOP/s"))
+    del inp
+
+    extra = {}
+    if not args.no_extra:
+        for idx in (3, 4, 5):
+            if idx == args.config:
+                continue
+            _, r = run_workload(idx, args.extra_steps, max(2, args.extra_steps // 5))
+            extra[f"config{idx}"] = dict(
+                workload=r["workload"], tflops=r["tflops"], frac_mfma_peak=r["tflops"] / MFMA_PEAK_TFLOPS,
+                gbs=r["gbs"], frac_hbm_peak=r["gbs"] / HBM_PEAK_GBS, ms_per_step=r["ms_per_step"],
+                main_kernel_ms=r["main_kernel_ms"], combine_kernel_ms=r["combine_kernel_ms"],
+                parts=r["parts"], total_splits=r["total_splits"], plan_us=r["plan_us"])
+
+    line = dict(
+        metric=METRIC, value=value, unit=unit, n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=head["ms_per_step"], higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16", data="synthetic",
+        config=dict(workload=head["workload"], batch=head["batch"], s_q=head["s_q"], h_q=head["h_q"],
+                    d_qk=576, d_v=512, page=64, sum_seqlen=head["sum_seqlen"], parts=head["parts"],
+                    total_splits=head["total_splits"], rotating_kv_copies=head["rotating_copies"]),
+        roofline=roof, cpu_baseline=cpu,
+        detail=dict(gpu_ms_per_step=head["gpu_ms_per_step"], main_kernel_ms=head["main_kernel_ms"],
+                    combine_kernel_ms=head["combine_kernel_ms"], plan_us=head["plan_us"],
+                    algorithmic_bytes=head["bytes"], algorithmic_flops=head["flops"],
+                    kernel_sha256_16=kernel_hash()),
+        extra=extra,
+    )
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+"""Thin ctypes binding of ``libmla_decode.so`` (argument marshalling only).
+
+Every step of the decode runs in the HIP library; this module checks Python
+arguments, allocates outputs and scratch with PyTorch (device memory and
+streams only) and calls the C ABI declared in ``include/mla_decode.h``.
+There is no fallback: if the library is missing, every entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmla_decode.so")
+SCHED_INTS = 8
+PAGE = 64
+D_QK = 576
+D_V = 512
+
+# Every symbol include/mla_decode.h declares.
+EXPORTED = ("mla_plan", "mla_get_metadata", "mla_max_parts", "mla_workspace_bytes",
+            "mla_decode_fwd", "mla_profile_start", "mla_profile_stop", "mla_last_error")
+
+_lib = None
+
+
+class MlaError(RuntimeError):
+    """A non-zero return code from the library, with its message."""
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "or python -m decode_attention_mla_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    ip = ctypes.POINTER(ctypes.c_int)
+    vp = ctypes.c_void_p
+    L.mla_plan.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, i32p,
+                           ctypes.c_int, i32p, ip]
+    L.mla_plan.restype = ctypes.c_int
+    L.mla_get_metadata.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, i32p, ctypes.c_int, i32p, ip, ip]
+    L.mla_get_metadata.restype = ctypes.c_int
+    L.mla_max_parts.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.mla_max_parts.restype = ctypes.c_int
+    L.mla_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.mla_workspace_bytes.restype = ctypes.c_size_t
+    L.mla_decode_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int, ctypes.c_float, vp, ctypes.c_int, vp, vp, ctypes.c_size_t,
+                                 vp, vp, vp]
+    L.mla_decode_fwd.restype = ctypes.c_int
+    L.mla_profile_start.argtypes = [ctypes.c_int]
+    L.mla_profile_start.restype = ctypes.c_int
+    fp = ctypes.POINTER(ctypes.c_float)
+    L.mla_profile_stop.argtypes = [fp, fp, ip]
+    L.mla_profile_stop.restype = ctypes.c_int
+    L.mla_last_error.argtypes = []
+    L.mla_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(rc: int, name: str) -> None:
+    if rc != 0:
+        raise MlaError(f"{name} returned {rc}: {lib().mla_last_error().decode()}")
+
+
+def _i32_host(x) -> np.ndarray:
+    if hasattr(x, "detach"):            # torch tensor (host or device)
+        x = x.detach().to("cpu").numpy()
+    a = np.ascontiguousarray(np.asarray(x), dtype=np.int32)
+    return a
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+# ---------------------------------------------------------------------------
+# Planning (host)
+
+def mla_plan(cache_seqlens, num_parts: int, fixed_overhead: int = 0, force_splits: int = 0):
+    """Host planner with explicit parts / overhead: (sched int32 [P, 8], num_splits int32 [b + 1])."""
+    sl = _i32_host(cache_seqlens)
+    b = int(sl.shape[0])
+    cap = max(1, num_parts) if force_splits <= 0 else int(sum(max(1, min(force_splits, (int(L) + PAGE - 1) // PAGE)) for L in sl))
+    sched = np.zeros((cap, SCHED_INTS), dtype=np.int32)
+    ns = np.zeros(b + 1, dtype=np.int32)
+    nparts = ctypes.c_int(0)
+    _check(lib().mla_plan(_ptr(sl), b, int(num_parts), int(fixed_overhead), int(force_splits), _ptr(sched), cap,
+                          _ptr(ns), ctypes.byref(nparts)), "mla_plan")
+    return sched[:nparts.value].copy(), ns
+
+
+def get_mla_metadata_host(cache_seqlens, h_q: int, s_q: int, num_cus: int = 0, force_splits: int = 0):
+    """mla_get_metadata on host arrays: (sched [P, 8], num_splits [b + 1], total_splits)."""
+    sl = _i32_host(cache_seqlens)
+    b = int(sl.shape[0])
+    L = lib()
+    cap = L.mla_max_parts(_ptr(sl), b, int(h_q), int(s_q), int(num_cus), int(force_splits))
+    _check(cap if cap < 0 else 0, "mla_max_parts")
+    sched = np.zeros((max(cap, 1), SCHED_INTS), dtype=np.int32)
+    ns = np.zeros(b + 1, dtype=np.int32)
+    nparts = ctypes.c_int(0)
+    total = ctypes.c_int(0)
+    _check(L.mla_get_metadata(_ptr(sl), b, int(h_q), int(s_q), int(num_cus), int(force_splits), _ptr(sched),
+                              sched.shape[0], _ptr(ns), ctypes.byref(nparts), ctypes.byref(total)),
+           "mla_get_metadata")
+    return sched[:nparts.value].copy(), ns, int(total.value)
+
+
+def get_mla_metadata(cache_seqlens, h_q: int, s_q: int, num_cus: int = 0, force_splits: int = 0,
+                     device=None):
+    """Plan one decode step; returns (sched, num_splits) as int32 device tensors.
+
+    The plan is reusable for every call with the same batch, s_q, h_q and
+    cache_seqlens (e.g. every layer of one decode step).  ``cache_seqlens``
+    may be a host array or a tensor; the planner reads it on the host.
+    """
+    import torch
+    sched, ns, _ = get_mla_metadata_host(cache_seqlens, h_q, s_q, num_cus, force_splits)
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    return (torch.from_numpy(sched).to(dev, non_blocking=False),
+            torch.from_numpy(ns).to(dev, non_blocking=False))
+
+
+def mla_workspace_bytes(total_splits: int, h_q: int, s_q: int) -> int:
+    return int(lib().mla_workspace_bytes(int(total_splits), int(h_q), int(s_q)))
+
+
+# ---------------------------------------------------------------------------
+# Decode
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def mla_decode_fwd(q, kv_cache, block_table, cache_seqlens, softmax_scale: float, sched, num_splits,
+                   out=None, lse=None, workspace=None):
+    """Dense MLA decode.  Returns (out bf16 [b, s_q, h_q, 512], lse fp32 [b, h_q, s_q]).
+
+    q bf16 [b, s_q, h_q, 576]; kv_cache bf16 [num_blocks, 64, 1, 576];
+    block_table int32 [b, max_blocks]; cache_seqlens int32 [b];
+    sched / num_splits from get_mla_metadata for the same cache_seqlens.
+    All tensors on the same GPU, contiguous.  Enqueued on the current stream.
+    """
+    import torch
+    _need(q.dim() == 4 and q.shape[3] == D_QK, f"q must be [b, s_q, h_q, 576], got {tuple(q.shape)}")
+    b, s_q, h_q = (int(x) for x in q.shape[:3])
+    _need(kv_cache.dim() == 4 and tuple(kv_cache.shape[1:]) == (PAGE, 1, D_QK),
+          f"kv_cache must be [num_blocks, 64, 1, 576], got {tuple(kv_cache.shape)}")
+    _need(block_table.dim() == 2 and block_table.shape[0] == b, "block_table must be [b, max_blocks]")
+    _need(cache_seqlens.dim() == 1 and cache_seqlens.shape[0] == b, "cache_seqlens must be [b]")
+    _need(sched.dim() == 2 and sched.shape[1] == SCHED_INTS and sched.shape[0] > 0, "sched must be [P, 8]")
+    _need(num_splits.dim() == 1 and num_splits.shape[0] == b + 1, "num_splits must be [b + 1]")
+    for name, t, dt in (("q", q, torch.bfloat16), ("kv_cache", kv_cache, torch.bfloat16),
+                        ("block_table", block_table, torch.int32), ("cache_seqlens", cache_seqlens, torch.int32),
+                        ("sched", sched, torch.int32), ("num_splits", num_splits, torch.int32)):
+        _need(t.dtype == dt, f"{name} must be {dt}, got {t.dtype}")
+        _need(t.is_cuda and t.device == q.device, f"{name} must be on {q.device}")
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+    num_parts = int(sched.shape[0])
+    if out is None:
+        out = torch.empty((b, s_q, h_q, D_V), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((b, h_q, s_q), dtype=torch.float32, device=q.device)
+    _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (b, s_q, h_q, D_V) and out.is_contiguous(),
+          "out must be contiguous bf16 [b, s_q, h_q, 512]")
+    _need(lse.dtype == torch.float32 and tuple(lse.shape) == (b, h_q, s_q) and lse.is_contiguous(),
+          "lse must be contiguous fp32 [b, h_q, s_q]")
+    ws_bytes = mla_workspace_bytes(num_parts + b - 1, h_q, s_q)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    _need(workspace.numel() * workspace.element_size() >= ws_bytes, f"workspace needs {ws_bytes} bytes")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib().mla_decode_fwd(q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(), cache_seqlens.data_ptr(),
+                              b, s_q, h_q, int(kv_cache.shape[0]), int(block_table.shape[1]),
+                              float(softmax_scale), sched.data_ptr(), num_parts, num_splits.data_ptr(),
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                              out.data_ptr(), lse.data_ptr(), stream)
+    _check(rc, "mla_decode_fwd")
+    return out, lse
+
+
+def profile_start(max_calls: int) -> None:
+    """Record per-kernel HIP events for the next max_calls mla_decode_fwd calls."""
+    _check(lib().mla_profile_start(int(max_calls)), "mla_profile_start")
+
+
+def profile_stop():
+    """Return (main_ms_total, combine_ms_total, calls) for the recorded calls."""
+    a, c, n = ctypes.c_float(0), ctypes.c_float(0), ctypes.c_int(0)
+    _check(lib().mla_profile_stop(ctypes.byref(a), ctypes.byref(c), ctypes.byref(n)), "mla_profile_stop")
+    return float(a.value), float(c.value), int(n.value)

@@ -1,0 +1,647 @@
+// Dense MLA decode for MI355X (gfx950): split-KV main kernel, log-sum-exp
+// combine kernel and the C ABI around them.
+//
+// What is computed (the "[DeepSeek-3] FlashMLA" overview page, sections 3-7):
+// each request's s_q*h_q query rows (576 dims, weight-absorbed) attend over the
+// request's paged 576-dim cache rows; QK^T uses all 576 dims, PV the first 512.
+// A part of the launch grid walks a range of (request, 64-token block) work
+// from the host planner; every piece is reduced with online softmax and either
+// written out directly or, when its request is split across parts, stored as
+// a normalised partial (O_i, lse_i) that the combine kernel merges.
+//
+// Kernel design (gfx950, not a translation of the pages' Hopper kernel):
+//   * One workgroup per (part, group of up to 128 query rows), one wave per
+//     SIMD; wave w owns a 32-row tile of queries.
+//   * KV pages are copied HBM -> LDS with global_load_lds_dwordx4 (16 B per
+//     lane straight into LDS), double buffered (2 x 72 KiB).  In LDS a page is
+//     stored as 9 blocks of 64 dims; block b holds a 128-byte row per token
+//     (dims 64b..64b+63) whose eight 16-byte chunks are permuted by a function
+//     of the token so that both LDS read patterns below hit distinct banks.
+//   * QK^T is computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+//     K fragments come from LDS (ds_read_b128), Q fragments stay in registers
+//     for the whole piece.  In the accumulator layout every lane then holds
+//     one query row, so row max / row sum need one cross-half exchange and
+//     the probabilities are already laid out as the B operand of the PV MFMA.
+//   * PV is computed as O^T = V^T P^T; V^T fragments are read with
+//     ds_read_b64_tr_b16 (transposing LDS read) from the same LDS page.
+//   * Softmax runs in base 2 with log2(e) folded into the score scale (the
+//     exp2 detail of the FlashMLA new-kernel deep-dive page).  Instead of
+//     moving the running max every page and rescaling O (which would drag the
+//     256-register accumulator through VALU each page), each piece keeps the
+//     first page's row max as its reference: probabilities are 2^(s - m_ref)
+//     and may exceed 1.  This is the online-softmax algebra with a fixed
+//     reference, exact up to rounding.  If a row's max ever rises more than
+//     64 (log2) above its reference, the workgroup restarts the piece with the
+//     largest max seen so far as the new reference (a slow path that ordinary
+//     inputs never take), so nothing can overflow.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "mla_internal.h"
+
+namespace mla {
+
+static thread_local std::string g_last_error;
+
+int set_error(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+#define LDS_PTR(T) __attribute__((address_space(3))) T*
+
+constexpr int kChunks = kDqk / 8;                  // 72 sixteen-byte chunks per token row
+constexpr int kRowBytes = kDqk * 2;                // 1152
+constexpr int kPageBytes = kPage * kRowBytes;      // 73728
+constexpr int kSlices = kPageBytes / 1024;         // 72 wave-wide 1 KiB copies per page
+constexpr int kKSteps = kDqk / 16;                 // 36 MFMA k-steps for QK^T
+constexpr int kColTiles = kDv / 32;                // 16 output column tiles
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRefHeadroom = 64.0f;              // log2 units a row max may exceed its reference
+constexpr int kMaxRestarts = 16;                   // restarts per piece before giving up on headroom
+
+struct Params {
+  const unsigned char* q;      // bf16 [batch, R, 576]
+  const unsigned char* kv;     // bf16 [num_blocks, 64, 576]
+  const int32_t* block_table;  // [batch, max_blocks]
+  const int32_t* seqlens;      // [batch]
+  const int32_t* sched;        // [num_parts, 8]
+  const int32_t* num_splits;   // [batch + 1] exclusive prefix
+  unsigned short* out;         // bf16 [batch, R, 512]
+  float* lse;                  // [batch, h_q, s_q]
+  float* oacc;                 // [slots, row_tiles, 16, 64, 16] normalised partial O
+  float* lacc;                 // [slots, row_tiles * 32] partial lse, base 2
+  int R, h_q, s_q, max_blocks, num_parts, row_groups, row_tiles;
+  float scale_log2;            // softmax_scale * log2(e)
+};
+
+// Chunk permutation of token row t inside an LDS column block: logical chunk
+// c (0..7) of the row sits at position c ^ chunk_xor(t) (an involution).  It
+// is a function of (t >> 1) & 7 chosen so that 16 consecutive tokens at one
+// chunk, and the 4-token x 2-chunk footprint of a transposing read, each fall
+// on distinct 16-byte bank groups (row stride 128 B = 8 groups of 16 B).
+__device__ __forceinline__ int chunk_xor(int t) {
+  const int x = (t >> 1) & 7;
+  return ((x & 1) << 2) | (x >> 1);
+}
+
+constexpr int kBlockBytes = kPage * 128;           // one 64-dim column block of a page (8 KiB)
+
+__device__ __forceinline__ unsigned short f32_to_bf16(float f) {
+  unsigned u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);  // round to nearest even
+  return (unsigned short)(u >> 16);
+}
+
+constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0), expcnt and lgkmcnt not waited
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Asserts to the compiler that a pointer is the same in every lane (it is
+// derived from wave-uniform values) so it can live in SGPRs.
+__device__ __forceinline__ const unsigned char* uniform_ptr(const unsigned char* p) {
+  const unsigned long long v = (unsigned long long)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return (const unsigned char*)(((unsigned long long)hi << 32) | lo);
+}
+
+// Per-lane global byte offset, inside a page, of the 16 bytes that lane l
+// copies for an LDS slice of parity `par`: slice i (1 KiB = 64 x 16 B) of the
+// LDS image is column block i / 8, tokens 8 (i % 8) + l / 8, chunk position
+// l % 8; the token's permutation only depends on i % 2 and l / 16.
+__device__ __forceinline__ unsigned dma_lane_offset(int lane, int par) {
+  // Token 8 (i % 8) + lane / 8 has the same permutation as 8 par + lane / 8.
+  const int cx = chunk_xor(8 * par + (lane >> 3));
+  return (unsigned)((lane >> 3) * kRowBytes + (((lane & 7) ^ cx) << 4));
+}
+
+// Copy one 64x576 bf16 page to LDS: wave w issues slices w, w + NW, ...
+template <int NW>
+__device__ __forceinline__ void issue_page(const unsigned char* page_any, unsigned lds_base,
+                                           const unsigned dma_off[2], int wave) {
+  const unsigned char* page = uniform_ptr(page_any);
+#pragma unroll
+  for (int k = 0; k < kSlices / NW; ++k) {
+    const int i = wave + k * NW;
+    // The opaque copy keeps the compiler from hoisting all 72/NW offsets out
+    // of the page loop (they would stay live in VGPRs for the whole kernel).
+    unsigned lane_off = dma_off[i & 1];
+    asm volatile("" : "+v"(lane_off));
+    const unsigned voff = lane_off + (unsigned)((i & 7) * 8 * kRowBytes + (i >> 3) * 128);
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_base + (unsigned)i * 1024u);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(page), "s"(m0)
+                 : "memory");
+  }
+}
+
+// Wave-uniform read of read-only metadata through the constant address
+// space, so it becomes a scalar load (lgkmcnt) and never waits on vmcnt,
+// which counts the page copies in flight.
+template <class T>
+__device__ __forceinline__ T ld_uniform(const T* ptr) {
+  return *(const __attribute__((address_space(4))) T*)ptr;
+}
+
+__device__ __forceinline__ void map_block(const Params& p, int& part, int& rg) {
+  const int id = blockIdx.x;
+  if (p.row_groups == 1) {
+    part = id;
+    rg = 0;
+    return;
+  }
+  // Keep the row groups of one part on the same XCD (workgroups are dealt to
+  // the 8 XCDs round robin) and adjacent in dispatch order, so the second
+  // reader of every KV page finds it in that XCD's L2.
+  const int xcd = id & 7, slot = id >> 3;
+  rg = slot % p.row_groups;
+  part = (slot / p.row_groups) * 8 + xcd;
+}
+
+template <int NW>
+__global__ void __launch_bounds__(NW * 64, 1) mla_splitkv_kernel(Params p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kPageBytes];
+  __shared__ int restart_flag[NW];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int part, rg;
+  map_block(p, part, rg);
+  if (part >= p.num_parts) return;
+
+  const int32_t* sp = p.sched + part * MLA_SCHED_INTS;
+  const int begin_req = ld_uniform(sp), end_req = ld_uniform(sp + 1), begin_blk = ld_uniform(sp + 2),
+            end_blk = ld_uniform(sp + 3), begin_piece = ld_uniform(sp + 4);
+
+  const int rt = rg * NW + wave;            // this wave's 32-row query tile
+  const int h = lane >> 5;                  // which half of the MFMA k / row slots
+  const int col = lane & 31;                // MFMA column = query row within the tile
+  const int r = rt * 32 + col;              // this lane's query row
+  const bool tile_ok = rt < p.row_tiles;
+  const bool row_ok = r < p.R;
+
+  const unsigned lds0 = (unsigned)(size_t)(LDS_PTR(unsigned char))smem;
+  LDS_PTR(unsigned char) lds = (LDS_PTR(unsigned char))smem;
+  const unsigned dma_off[2] = {dma_lane_offset(lane, 0), dma_lane_offset(lane, 1)};
+
+  // QK^T A fragment of k-step ks, token tile tau: token col + 32 tau, logical
+  // chunk 2 ks + h, i.e. block ks / 4, in-block chunk 2 (ks % 4) + h.
+  const int qk_sw = chunk_xor(col);
+  int qk_base[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) qk_base[b] = col * 128 + (((2 * b + h) ^ qk_sw) << 4);
+
+  // Transposing V reads: 16-lane group G, lane Lq in it reads 8 bytes of
+  // token 16 kk + 4 h + Lq / 4 (and + 8) at columns 32 ct + 16 (G & 1) + 4 (Lq & 3),
+  // i.e. block ct / 2, in-block chunk 4 (ct % 2) + 2 (G & 1) + (Lq & 3) / 2.
+  const int G = lane >> 4, Lq = lane & 15;
+  const int rsub = 4 * (G >> 1) + (Lq >> 2);
+  const int cc0 = 2 * (G & 1) + ((Lq & 3) >> 1);
+  const int hb = (Lq & 1) * 8;
+  int pv_base[2][2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    pv_base[par][0] = rsub * 128 + (((4 * par + cc0) ^ chunk_xor(rsub)) << 4) + hb;
+    pv_base[par][1] = (rsub + 8) * 128 + (((4 * par + cc0) ^ chunk_xor(rsub + 8)) << 4) + hb;
+  }
+
+  for (int req = begin_req; req <= end_req; ++req) {
+    const int L = ld_uniform(p.seqlens + req);
+    const int nblk = (L + kPage - 1) / kPage;
+    const int lo = (req == begin_req) ? begin_blk : 0;
+    const int hi = (req == end_req) ? end_blk : nblk;
+    const int piece = (req == begin_req) ? begin_piece : 0;
+    const int slot0 = ld_uniform(p.num_splits + req);
+    const bool split = (ld_uniform(p.num_splits + req + 1) - slot0) > 1;
+    const int32_t* bt = p.block_table + (size_t)req * p.max_blocks;
+
+    f32x16 o[kColTiles];
+    float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
+    bf16x8 qf[kKSteps];
+    for (int restarts = 0;; ++restarts) {
+    if (lo < hi) issue_page<NW>(p.kv + (size_t)ld_uniform(bt + (lo)) * kPageBytes, lds0, dma_off, wave);
+    // Q^T fragments (B operand): row r, dims 16 ks + 8 h .. + 7.
+    {
+      const unsigned char* qrow = p.q + ((size_t)req * p.R + (row_ok ? r : 0)) * kRowBytes + h * 16;
+      const unsigned keep = row_ok ? ~0u : 0u;
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        u32x4 v = *(const u32x4*)(qrow + ks * 32);
+        v &= keep;
+        qf[ks] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+    // Wait (visibly to the compiler) for Q and the first page, so that it
+    // inserts no vmcnt(0) inside the page loop, where that would also wait
+    // for the next page's copy.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if (lo + 1 < hi) issue_page<NW>(p.kv + (size_t)ld_uniform(bt + (lo + 1)) * kPageBytes, lds0 + kPageBytes, dma_off, wave);
+#pragma unroll
+    for (int ct = 0; ct < kColTiles; ++ct) o[ct] = f32x16{};
+    l_run = 0.f;
+    bool restart = false;
+
+    for (int j = lo; j < hi; ++j) {
+      const int bsel = (j - lo) & 1;
+      LDS_PTR(unsigned char) buf = lds + bsel * kPageBytes;
+      if (j + 1 < hi) wait_vmcnt<(kSlices / NW < 63 ? kSlices / NW : 63)>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      const int valid = min(kPage, L - j * kPage);
+      if (valid < kPage) {
+        // Tokens past the sequence end: zero their rows in every column block
+        // so that masked probabilities (exactly 0) never meet non-finite
+        // cache contents.
+        const int per_blk = (kPage - valid) * 8;
+        for (int u = threadIdx.x; u < per_blk * 9; u += NW * 64) {
+          const int b = u / per_blk, w = u - b * per_blk;
+          *(LDS_PTR(u32x4))(buf + b * kBlockBytes + valid * 128 + w * 16) = u32x4{0, 0, 0, 0};
+        }
+        lds_barrier();
+      }
+
+      // ---- S^T = K Q^T for token tiles 0 (tokens 0..31) and 1 (32..63)
+      f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        LDS_PTR(unsigned char) a = buf + (ks >> 2) * kBlockBytes + qk_base[ks & 3];
+        const u32x4 k0 = *(LDS_PTR(u32x4))(a);
+        const u32x4 k1 = *(LDS_PTR(u32x4))(a + 32 * 128);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k0), qf[ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k1), qf[ks], s1, 0, 0, 0);
+      }
+
+      // ---- online softmax (base 2).  Lane holds tokens 8(v/4) + 4h + v%4 (+32).
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        s0[v] *= p.scale_log2;
+        s1[v] *= p.scale_log2;
+      }
+      if (valid < kPage) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int tok = 8 * (v >> 2) + 4 * h + (v & 3);
+          if (tok >= valid) s0[v] = -INFINITY;
+          if (tok + 32 >= valid) s1[v] = -INFINITY;
+        }
+      }
+      float mloc = fmaxf(s0[0], s1[0]);
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mloc = fmaxf(mloc, fmaxf(s0[v], s1[v]));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      m_seen = fmaxf(m_seen, mloc);
+      if (j == lo && restarts == 0) m_ref = mloc;
+      const int wave_bad = __any(mloc > m_ref + kRefHeadroom) && restarts < kMaxRestarts;
+      i16x8 pk[4];
+      float lsum = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const unsigned short b0 = f32_to_bf16(__builtin_amdgcn_exp2f(s0[v] - m_ref));
+        const unsigned short b1 = f32_to_bf16(__builtin_amdgcn_exp2f(s1[v] - m_ref));
+        lsum += __uint_as_float((unsigned)b0 << 16) + __uint_as_float((unsigned)b1 << 16);
+        pk[v >> 3][v & 7] = (short)b0;
+        pk[2 + (v >> 3)][v & 7] = (short)b1;
+      }
+      l_run += lsum;
+
+      // ---- O^T += V^T P^T over the 4 sixteen-token k-steps of the page.
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[kk]);
+#pragma unroll
+        for (int ct = 0; ct < kColTiles; ++ct) {
+          LDS_PTR(unsigned char) a = buf + (ct >> 1) * kBlockBytes + kk * 16 * 128;
+          const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv_base[ct & 1][0]));
+          const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv_base[ct & 1][1]));
+          const i16x8 av = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb, o[ct], 0, 0, 0);
+        }
+      }
+
+      if (lane == 0) restart_flag[wave] = wave_bad;
+      lds_barrier();  // every wave is done with this buffer
+      int any_bad = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) any_bad |= restart_flag[w];
+      if (any_bad) {
+        // Slow path: a row outgrew its reference max.  Drain the copy in
+        // flight, then redo the piece from its first page with the largest
+        // max seen so far as the reference.
+        wait_vmcnt<0>();
+        lds_barrier();
+        restart = true;
+        break;
+      }
+      if (j + 2 < hi)
+        issue_page<NW>(p.kv + (size_t)ld_uniform(bt + (j + 2)) * kPageBytes, lds0 + bsel * kPageBytes, dma_off, wave);
+    }
+    if (!restart) break;
+    m_ref = m_seen;
+    }
+
+    // ---- epilogue: normalise and write out / lse, or the partial slot.
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse2 = l_tot > 0.f ? m_ref + __builtin_amdgcn_logf(l_tot) : -INFINITY;
+    if (!tile_ok) continue;
+    if (!split) {
+      if (row_ok) {
+        unsigned short* orow = p.out + ((size_t)req * p.R + r) * kDv;
+#pragma unroll
+        for (int ct = 0; ct < kColTiles; ++ct) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            u32x2 w;
+            w[0] = (unsigned)f32_to_bf16(o[ct][4 * g + 0] * inv) | ((unsigned)f32_to_bf16(o[ct][4 * g + 1] * inv) << 16);
+            w[1] = (unsigned)f32_to_bf16(o[ct][4 * g + 2] * inv) | ((unsigned)f32_to_bf16(o[ct][4 * g + 3] * inv) << 16);
+            *(u32x2*)(orow + 32 * ct + 8 * g + 4 * h) = w;
+          }
+        }
+        if (h == 0) {
+          const int s = r / p.h_q, hh = r - s * p.h_q;
+          p.lse[((size_t)req * p.h_q + hh) * p.s_q + s] = lse2 * kLn2;
+        }
+      }
+    } else {
+      const int slot = slot0 + piece;
+      float* dst = p.oacc + ((((size_t)slot * p.row_tiles + rt) * kColTiles) * 64 + lane) * 16;
+#pragma unroll
+      for (int ct = 0; ct < kColTiles; ++ct) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 w = {o[ct][4 * g] * inv, o[ct][4 * g + 1] * inv, o[ct][4 * g + 2] * inv, o[ct][4 * g + 3] * inv};
+          *(f32x4*)(dst + (size_t)ct * 64 * 16 + 4 * g) = w;
+        }
+      }
+      if (h == 0) p.lacc[(size_t)slot * p.row_tiles * 32 + r] = lse2;
+    }
+  }
+}
+
+// Merge the partial (O_i, lse_i) of every split request (the log-sum-exp
+// merge of the attention-kernel page and the overview page, section 7):
+// M = max lse_i, w_i = 2^(lse_i - M), out = sum w_i O_i / sum w_i,
+// lse = M + log2(sum w_i) (then converted to natural log).  One wave per
+// (request, 32-row tile, 32-column tile); lane = accumulator lane of the
+// main kernel, so partial reads are contiguous 64-byte rows.
+__global__ void __launch_bounds__(64) mla_combine_kernel(Params p) {
+  const int per_req = p.row_tiles * kColTiles;
+  const int req = blockIdx.x / per_req;
+  const int rem = blockIdx.x - req * per_req;
+  const int rt = rem / kColTiles, ct = rem - rt * kColTiles;
+  const int slot0 = p.num_splits[req];
+  const int n = p.num_splits[req + 1] - slot0;
+  if (n <= 1) return;
+  const int lane = threadIdx.x;
+  const int h = lane >> 5;
+  const int r = rt * 32 + (lane & 31);
+  if (r >= p.R) return;
+  const size_t rows_p = (size_t)p.row_tiles * 32;
+
+  float M = -INFINITY;
+  for (int i = 0; i < n; ++i) M = fmaxf(M, p.lacc[(size_t)(slot0 + i) * rows_p + r]);
+  float acc[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  float wsum = 0.f;
+  if (M != -INFINITY) {
+    for (int i = 0; i < n; ++i) {
+      const float w = __builtin_amdgcn_exp2f(p.lacc[(size_t)(slot0 + i) * rows_p + r] - M);
+      const float* src = p.oacc + ((((size_t)(slot0 + i) * p.row_tiles + rt) * kColTiles + ct) * 64 + lane) * 16;
+      wsum += w;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 v = *(const f32x4*)(src + 4 * g);
+        acc[4 * g] += w * v[0];
+        acc[4 * g + 1] += w * v[1];
+        acc[4 * g + 2] += w * v[2];
+        acc[4 * g + 3] += w * v[3];
+      }
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  unsigned short* orow = p.out + ((size_t)req * p.R + r) * kDv;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    u32x2 w;
+    w[0] = (unsigned)f32_to_bf16(acc[4 * g] * inv) | ((unsigned)f32_to_bf16(acc[4 * g + 1] * inv) << 16);
+    w[1] = (unsigned)f32_to_bf16(acc[4 * g + 2] * inv) | ((unsigned)f32_to_bf16(acc[4 * g + 3] * inv) << 16);
+    *(u32x2*)(orow + 32 * ct + 8 * g + 4 * h) = w;
+  }
+  if (ct == 0 && h == 0) {
+    const int s = r / p.h_q, hh = r - s * p.h_q;
+    p.lse[((size_t)req * p.h_q + hh) * p.s_q + s] =
+        (M == -INFINITY || !(wsum > 0.f)) ? -INFINITY : (M + __builtin_amdgcn_logf(wsum)) * kLn2;
+  }
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+}  // namespace mla
+
+using namespace mla;
+
+extern "C" const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" int mla_plan(const int32_t* cache_seqlens, int batch, int num_parts, int fixed_overhead,
+                        int force_splits, int32_t* sched_out, int max_parts, int32_t* num_splits_out,
+                        int* num_parts_out) {
+  return plan(cache_seqlens, batch, num_parts, fixed_overhead, force_splits, sched_out, max_parts,
+              num_splits_out, num_parts_out);
+}
+
+static int policy(const int32_t* seqlens, int batch, int h_q, int s_q, int* num_cus, int* parts, int* F) {
+  if (batch <= 0 || h_q <= 0 || s_q <= 0 || !seqlens)
+    return set_error(MLA_ERR_INVALID, "mla_get_metadata: batch=%d h_q=%d s_q=%d seqlens=%p", batch, h_q, s_q,
+                     (const void*)seqlens);
+  if (*num_cus <= 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return set_error(MLA_ERR_HIP, "mla_get_metadata: cannot query the CU count");
+  }
+  const Geometry g = geometry(h_q, s_q);
+  *parts = *num_cus / g.row_groups;
+  if (*parts < 1) *parts = 1;
+  *F = g.R <= 32 ? 1 : 2;
+  return MLA_OK;
+}
+
+extern "C" int mla_max_parts(const int32_t* cache_seqlens, int batch, int h_q, int s_q, int num_cus,
+                             int force_splits) {
+  int parts, F;
+  int rc = policy(cache_seqlens, batch, h_q, s_q, &num_cus, &parts, &F);
+  if (rc) return rc;
+  if (force_splits <= 0) return parts;
+  long long total = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int n = (cache_seqlens[b] + kPage - 1) / kPage;
+    total += n < 1 ? 1 : (n < force_splits ? n : force_splits);
+  }
+  return (int)total;
+}
+
+extern "C" int mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q, int s_q, int num_cus,
+                                int force_splits, int32_t* sched_out, int max_parts,
+                                int32_t* num_splits_out, int* num_parts_out, int* total_splits_out) {
+  int parts, F;
+  int rc = policy(cache_seqlens, batch, h_q, s_q, &num_cus, &parts, &F);
+  if (rc) return rc;
+  if (!total_splits_out) return set_error(MLA_ERR_INVALID, "mla_get_metadata: null total_splits_out");
+  rc = plan(cache_seqlens, batch, parts, F, force_splits, sched_out, max_parts, num_splits_out, num_parts_out);
+  if (rc) return rc;
+  *total_splits_out = num_splits_out[batch];
+  return MLA_OK;
+}
+
+extern "C" size_t mla_workspace_bytes(int total_splits, int h_q, int s_q) {
+  if (total_splits <= 0 || h_q <= 0 || s_q <= 0) return 0;
+  const Geometry g = geometry(h_q, s_q);
+  const size_t rows = (size_t)total_splits * g.row_tiles * 32;
+  return align256(rows * kDv * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+// Event recording for mla_profile_start / mla_profile_stop (benchmarks only).
+namespace mla {
+namespace {
+struct Profile {
+  bool on = false;
+  int cap = 0, used = 0;
+  std::vector<hipEvent_t> ev;  // 3 per call: before main, after main, after combine
+};
+Profile g_prof;
+std::mutex g_prof_mu;
+}  // namespace
+}  // namespace mla
+
+extern "C" int mla_profile_start(int max_calls) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (max_calls <= 0 || g_prof.on) return set_error(MLA_ERR_INVALID, "mla_profile_start: max_calls=%d on=%d", max_calls, (int)g_prof.on);
+  g_prof.ev.assign((size_t)max_calls * 3, nullptr);
+  for (auto& e : g_prof.ev)
+    if (hipEventCreate(&e) != hipSuccess) return set_error(MLA_ERR_HIP, "mla_profile_start: hipEventCreate failed");
+  g_prof.cap = max_calls;
+  g_prof.used = 0;
+  g_prof.on = true;
+  return MLA_OK;
+}
+
+extern "C" int mla_profile_stop(float* main_ms, float* combine_ms, int* calls) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof.on || !main_ms || !combine_ms || !calls) return set_error(MLA_ERR_INVALID, "mla_profile_stop: not started or null output");
+  float a = 0.f, c = 0.f;
+  int rc = MLA_OK;
+  if (g_prof.used > 0 && hipEventSynchronize(g_prof.ev[(size_t)g_prof.used * 3 - 1]) != hipSuccess)
+    rc = set_error(MLA_ERR_HIP, "mla_profile_stop: hipEventSynchronize failed");
+  for (int i = 0; rc == MLA_OK && i < g_prof.used; ++i) {
+    float t0 = 0.f, t1 = 0.f;
+    if (hipEventElapsedTime(&t0, g_prof.ev[i * 3], g_prof.ev[i * 3 + 1]) != hipSuccess ||
+        hipEventElapsedTime(&t1, g_prof.ev[i * 3 + 1], g_prof.ev[i * 3 + 2]) != hipSuccess)
+      rc = set_error(MLA_ERR_HIP, "mla_profile_stop: hipEventElapsedTime failed");
+    a += t0;
+    c += t1;
+  }
+  *main_ms = a;
+  *combine_ms = c;
+  *calls = g_prof.used;
+  for (auto e : g_prof.ev) hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.on = false;
+  return rc;
+}
+
+static hipEvent_t* profile_slot() {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof.on || g_prof.used >= g_prof.cap) return nullptr;
+  return &g_prof.ev[(size_t)(g_prof.used++) * 3];
+}
+
+extern "C" int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* block_table,
+                              const int32_t* cache_seqlens, int batch, int s_q, int h_q, int num_blocks,
+                              int max_blocks_per_seq, float softmax_scale, const int32_t* sched,
+                              int num_parts, const int32_t* num_splits, void* workspace,
+                              size_t workspace_bytes, void* out, float* lse, void* stream) {
+  if (!q || !kv_cache || !block_table || !cache_seqlens || !sched || !num_splits || !out || !lse)
+    return set_error(MLA_ERR_INVALID, "mla_decode_fwd: null pointer argument");
+  if (batch <= 0 || s_q <= 0 || h_q <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || num_parts <= 0)
+    return set_error(MLA_ERR_INVALID,
+                     "mla_decode_fwd: batch=%d s_q=%d h_q=%d num_blocks=%d max_blocks_per_seq=%d num_parts=%d",
+                     batch, s_q, h_q, num_blocks, max_blocks_per_seq, num_parts);
+  if (!std::isfinite(softmax_scale))
+    return set_error(MLA_ERR_INVALID, "mla_decode_fwd: softmax_scale is not finite");
+  const Geometry g = geometry(h_q, s_q);
+  const int slots = num_parts + batch - 1;
+  const size_t need = mla_workspace_bytes(slots, h_q, s_q);
+  if (!workspace || workspace_bytes < need)
+    return set_error(MLA_ERR_WORKSPACE, "mla_decode_fwd: workspace %zu bytes < %zu needed", workspace_bytes, need);
+
+  Params prm;
+  prm.q = (const unsigned char*)q;
+  prm.kv = (const unsigned char*)kv_cache;
+  prm.block_table = block_table;
+  prm.seqlens = cache_seqlens;
+  prm.sched = sched;
+  prm.num_splits = num_splits;
+  prm.out = (unsigned short*)out;
+  prm.lse = lse;
+  const size_t rows = (size_t)slots * g.row_tiles * 32;
+  prm.oacc = (float*)workspace;
+  prm.lacc = (float*)((char*)workspace + align256(rows * kDv * sizeof(float)));
+  prm.R = g.R;
+  prm.h_q = h_q;
+  prm.s_q = s_q;
+  prm.max_blocks = max_blocks_per_seq;
+  prm.num_parts = num_parts;
+  prm.row_groups = g.row_groups;
+  prm.row_tiles = g.row_tiles;
+  prm.scale_log2 = softmax_scale * kLog2e;
+
+  hipStream_t st = (hipStream_t)stream;
+  hipEvent_t* ev = profile_slot();
+  if (ev) hipEventRecord(ev[0], st);
+  const int grid = g.row_groups == 1 ? num_parts : 8 * g.row_groups * ((num_parts + 7) / 8);
+  switch (g.waves) {
+    case 1: hipLaunchKernelGGL(mla_splitkv_kernel<1>, dim3(grid), dim3(64), 0, st, prm); break;
+    case 2: hipLaunchKernelGGL(mla_splitkv_kernel<2>, dim3(grid), dim3(128), 0, st, prm); break;
+    case 3: hipLaunchKernelGGL(mla_splitkv_kernel<3>, dim3(grid), dim3(192), 0, st, prm); break;
+    default: hipLaunchKernelGGL(mla_splitkv_kernel<4>, dim3(grid), dim3(256), 0, st, prm); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(MLA_ERR_HIP, "mla_decode_fwd: main kernel launch: %s", hipGetErrorString(e));
+  if (ev) hipEventRecord(ev[1], st);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(batch * g.row_tiles * kColTiles), dim3(64), 0, st, prm);
+  e = hipGetLastError();
+  if (e != hipSuccess) return set_error(MLA_ERR_HIP, "mla_decode_fwd: combine launch: %s", hipGetErrorString(e));
+  if (ev) hipEventRecord(ev[2], st);
+  return MLA_OK;
+}

@@ -1,0 +1,92 @@
+// Host split-KV tile planner for dense MLA decode.
+//
+// Follows the tile-scheduler description on the FlashMLA new-kernel deep-dive
+// page (nxmr.cn, section "Tile Scheduler"): count every request's 64-token KV
+// blocks, cap each part at payload = ceil(total / parts) + fixed overhead, and
+// walk the requests in order, filling parts greedily and cutting a request
+// at a block boundary when it does not fit; the per-request piece counts let
+// the combine step find each request's partial results.  The pages run this
+// as a single-warp GPU kernel; here it is plain host code, O(batch + parts).
+#include "mla_internal.h"
+
+#include <algorithm>
+#include <vector>
+
+namespace mla {
+
+static inline int blocks_of(int32_t L) { return (L + kPage - 1) / kPage; }
+
+int plan(const int32_t* seqlens, int batch, int num_parts, int fixed_overhead, int force_splits,
+         int32_t* sched, int max_parts, int32_t* num_splits, int* parts_out) {
+  if (!seqlens || !sched || !num_splits || !parts_out)
+    return set_error(MLA_ERR_INVALID, "mla_plan: null pointer argument");
+  if (batch <= 0 || num_parts <= 0 || fixed_overhead < 0 || force_splits < 0)
+    return set_error(MLA_ERR_INVALID, "mla_plan: batch=%d num_parts=%d fixed_overhead=%d force_splits=%d",
+                     batch, num_parts, fixed_overhead, force_splits);
+  std::vector<int> n(batch);
+  for (int b = 0; b < batch; ++b) {
+    if (seqlens[b] < 0) return set_error(MLA_ERR_INVALID, "mla_plan: cache_seqlens[%d] = %d < 0", b, seqlens[b]);
+    n[b] = blocks_of(seqlens[b]);
+  }
+  std::vector<int> pieces(batch, 0);
+  int np = 0;
+  auto emit = [&](int br, int er, int bb, int eb, int bp) -> bool {
+    if (np >= max_parts) return false;
+    int32_t* row = sched + (size_t)np * MLA_SCHED_INTS;
+    row[0] = br; row[1] = er; row[2] = bb; row[3] = eb; row[4] = bp;
+    row[5] = row[6] = row[7] = 0;
+    ++np;
+    return true;
+  };
+  if (force_splits > 0) {
+    for (int r = 0; r < batch; ++r) {
+      int cnt = std::max(1, std::min(force_splits, n[r]));
+      int q = n[r] / cnt, extra = n[r] % cnt, start = 0;
+      for (int i = 0; i < cnt; ++i) {
+        int size = q + (i < extra ? 1 : 0);
+        if (!emit(r, r, start, start + size, i))
+          return set_error(MLA_ERR_CAPACITY, "mla_plan: more than max_parts=%d parts", max_parts);
+        start += size;
+      }
+      pieces[r] = cnt;
+    }
+  } else {
+    const long long F = fixed_overhead;
+    long long total = 0;
+    for (int b = 0; b < batch; ++b) total += n[b] + F;
+    const long long payload = (total + num_parts - 1) / num_parts + F;
+    int req = 0, blk = 0;
+    for (int p = 0; p < num_parts && req < batch; ++p) {
+      const bool last_part = (p == num_parts - 1);
+      long long cap = payload;
+      const int br = req, bb = blk, bp = pieces[req];
+      int er = -1, eb = -1;
+      while (req < batch) {
+        const long long rem = n[req] - blk;
+        if (last_part || rem + F <= cap) {   // the rest of this request fits
+          cap -= rem + F;
+          pieces[req] += 1;
+          er = req; eb = n[req];
+          ++req; blk = 0;
+          continue;
+        }
+        const long long take = cap - F;
+        if (take > 0) {                      // cut the request at a block boundary
+          blk += (int)take;
+          pieces[req] += 1;
+          er = req; eb = blk;
+        }
+        break;
+      }
+      if (er < 0) continue;
+      if (!emit(br, er, bb, eb, bp))
+        return set_error(MLA_ERR_CAPACITY, "mla_plan: more than max_parts=%d parts", max_parts);
+    }
+  }
+  num_splits[0] = 0;
+  for (int b = 0; b < batch; ++b) num_splits[b + 1] = num_splits[b] + pieces[b];
+  *parts_out = np;
+  return MLA_OK;
+}
+
+}  // namespace mla

@@ -1,0 +1,165 @@
+/*
+ * mla_decode.h — C ABI of the MI355X (gfx950) dense MLA decode library.
+ *
+ * Computes weight-absorbed Multi-head Latent Attention decode over a paged
+ * KV cache, as defined on the "[DeepSeek-3] FlashMLA" overview page
+ * (xutianle.me), sections 3 and 4:
+ *
+ *   for every request b, query token s < s_q, head h < h_q:
+ *     L       = cache_seqlens[b]
+ *     K_b[t]  = kv_cache[block_table[b][t / 64], t % 64, 0, 0:576]   (t < L)
+ *     score_t = softmax_scale * dot(q[b,s,h,0:576], K_b[t])
+ *     out[b,s,h,c] = sum_t softmax(score)_t * K_b[t][c]               (c < 512)
+ *     lse[b,h,s]   = log(sum_t exp(score_t))                         (natural log)
+ *
+ * Work is cut into split-KV pieces by a tile planner (FlashMLA new-kernel
+ * deep-dive page, nxmr.cn, section "Tile Scheduler"), each piece is reduced
+ * with online softmax, and pieces of one request are merged with the
+ * log-sum-exp rule (attention-kernel page, online-softmax section).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensors are dense, row-major, with exactly the shapes given.
+ *   - bf16 data is passed as raw 16-bit patterns (void* / uint16_t*).
+ *   - "device" pointers are HIP device memory owned by the caller; the
+ *     library never frees or retains them past the call.
+ *   - Entry points return 0 on success or a negative MLA_ERR_* code; the
+ *     message for the last failure on the calling thread is returned by
+ *     mla_last_error().  Nothing is launched when an argument check fails.
+ *   - Query row r = s * h_q + h (the pages' s_q*h_q rows per KV head).
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID = -1,    /* bad dimension, null pointer, negative length */
+  MLA_ERR_CAPACITY = -2,   /* an output buffer is too small */
+  MLA_ERR_WORKSPACE = -3,  /* workspace smaller than mla_workspace_bytes() */
+  MLA_ERR_HIP = -4         /* a HIP runtime call or kernel launch failed */
+};
+
+/* Rows of the per-part schedule table: 8 int32 per part,
+ *   [begin_req, end_req (inclusive), begin_block (within begin_req),
+ *    end_block (exclusive, within end_req), begin_piece, 0, 0, 0]
+ * begin_piece is the index, among begin_req's pieces, of the piece this part
+ * holds.  num_splits is an exclusive prefix sum of pieces per request,
+ * length batch + 1: request b owns partial slots [num_splits[b], num_splits[b+1]). */
+#define MLA_SCHED_INTS 8
+
+/*
+ * mla_plan — split/tile planner (host only, no GPU call).
+ *
+ * Follows the tile-scheduler description on the new-kernel deep-dive page:
+ * n_b = ceil(L_b / 64) KV blocks per request; payload =
+ * ceil(sum_b (n_b + F) / num_parts) + F; requests are walked in order and
+ * each part is filled up to the payload, a request that does not fit being
+ * cut at a block boundary (every piece costs its blocks plus F).  The last
+ * part takes whatever remains.  force_splits > 0 instead cuts every request
+ * into min(force_splits, n_b) (at least 1) page-aligned pieces, one part each.
+ *
+ *   cache_seqlens  host int32 [batch], each >= 0
+ *   num_parts      > 0, number of parts the walk may fill
+ *   fixed_overhead F >= 0, per-piece overhead in blocks
+ *   sched_out      host int32 [max_parts * 8]
+ *   num_splits_out host int32 [batch + 1]
+ *   num_parts_out  parts actually written (<= num_parts, or pieces when forced)
+ * Errors: MLA_ERR_INVALID (batch <= 0, a length < 0, null pointer),
+ *         MLA_ERR_CAPACITY (more parts than max_parts).
+ */
+int mla_plan(const int32_t* cache_seqlens, int batch, int num_parts, int fixed_overhead,
+             int force_splits, int32_t* sched_out, int max_parts, int32_t* num_splits_out,
+             int* num_parts_out);
+
+/*
+ * mla_get_metadata — plan one decode step (the pages' get_mla_metadata).
+ *
+ * Chooses num_parts and the fixed overhead from the CU count and the
+ * query-row count R = s_q * h_q, then calls mla_plan.  The plan stays valid
+ * for every call (e.g. every layer of one decode step) with the same batch,
+ * s_q, h_q and cache_seqlens ("[DeepSeek-3] FlashMLA", section 5).
+ *
+ *   cache_seqlens  host int32 [batch]
+ *   num_cus        CUs to fill; 0 = query the current HIP device
+ *   force_splits   0 = greedy planner, k > 0 = k pieces per request (testing)
+ *   sched_out      host int32 [max_parts * 8]; max_parts >= mla_max_parts(...)
+ *   num_splits_out host int32 [batch + 1]
+ *   num_parts_out, total_splits_out  parts written, partial slots needed
+ * Errors: MLA_ERR_INVALID, MLA_ERR_CAPACITY, MLA_ERR_HIP (device query).
+ */
+int mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q, int s_q, int num_cus,
+                     int force_splits, int32_t* sched_out, int max_parts,
+                     int32_t* num_splits_out, int* num_parts_out, int* total_splits_out);
+
+/* Upper bound on the parts mla_get_metadata can emit for these sizes. */
+int mla_max_parts(const int32_t* cache_seqlens, int batch, int h_q, int s_q, int num_cus,
+                  int force_splits);
+
+/*
+ * mla_workspace_bytes — device scratch needed by mla_decode_fwd for a plan
+ * with total_splits partial slots: fp32 partial outputs
+ * [total_splits, ceil(R/32)*32, 512] and fp32 partial lse
+ * [total_splits, ceil(R/32)*32], each region 256-byte aligned (the split-KV
+ * workspace of the split-KV blog, 0539edu.com, section 3.1).  Any plan has
+ * total_splits <= num_parts + batch - 1.
+ */
+size_t mla_workspace_bytes(int total_splits, int h_q, int s_q);
+
+/*
+ * mla_decode_fwd — dense MLA decode forward (the pages' flash_mla_with_kvcache,
+ * dense path, non-causal, bf16, one KV head, head_dim_v = 512).
+ *
+ *   q             device bf16 [batch, s_q, h_q, 576]
+ *   kv_cache      device bf16 [num_blocks, 64, 1, 576]; K = all 576 dims,
+ *                 V = the first 512 dims of the same rows
+ *   block_table   device int32 [batch, max_blocks_per_seq]; entries for
+ *                 logical pages >= ceil(L/64) are never read
+ *   cache_seqlens device int32 [batch]; must equal the lengths the plan was
+ *                 made from, and L <= 64 * max_blocks_per_seq
+ *   softmax_scale multiplies the q.k scores
+ *   sched         device int32 [num_parts, 8] from mla_get_metadata/mla_plan
+ *   num_splits    device int32 [batch + 1] from the same plan
+ *   workspace     device, >= mla_workspace_bytes(num_parts + batch - 1, h_q, s_q)
+ *                 bytes (the bound on partial slots of any plan with num_parts)
+ *   out           device bf16 [batch, s_q, h_q, 512] (written)
+ *   lse           device fp32 [batch, h_q, s_q] (written; -inf when L = 0)
+ *   stream        hipStream_t to enqueue on (NULL = the null stream)
+ *
+ * Enqueues the split-KV kernel, then the combine kernel (whose workgroups
+ * return at once for requests that are not split); returns without
+ * synchronising and allocates nothing.  Block-table
+ * entries must lie in [0, num_blocks) and the device lengths must match the
+ * plan: neither is checked on the device (undefined behaviour otherwise).
+ * Errors: MLA_ERR_INVALID, MLA_ERR_WORKSPACE, MLA_ERR_HIP.
+ */
+int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* block_table,
+                   const int32_t* cache_seqlens, int batch, int s_q, int h_q, int num_blocks,
+                   int max_blocks_per_seq, float softmax_scale, const int32_t* sched,
+                   int num_parts, const int32_t* num_splits, void* workspace,
+                   size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/*
+ * Kernel timing for benchmarks.  mla_profile_start(max_calls) makes the next
+ * max_calls mla_decode_fwd calls (any thread) record HIP events on their
+ * stream around the split-KV kernel and around the combine kernel.
+ * mla_profile_stop waits for the last recorded event and returns the summed
+ * device milliseconds of each kernel and the number of calls recorded, then
+ * releases the events.  Errors: MLA_ERR_INVALID (max_calls <= 0, null
+ * outputs, start while started), MLA_ERR_HIP.
+ */
+int mla_profile_start(int max_calls);
+int mla_profile_stop(float* main_ms, float* combine_ms, int* calls);
+
+/* Message for the last non-zero return on this thread ("" if none). */
+const char* mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_DECODE_H */

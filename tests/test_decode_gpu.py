@@ -1,0 +1,178 @@
+"""GPU parity tests: the HIP path through the C ABI against the CPU oracle on
+the same seeded inputs, element by element, for the five workloads (full or
+sampled), ragged and edge-case shapes, poisoned memory, the restart slow
+path, page-permutation invariance and run-to-run determinism."""
+import numpy as np
+import pytest
+
+from decode_attention_mla_amd import workloads as W
+import oracle
+from gpu_util import assert_parity, max_err, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _ref(inp, requests=None):
+    return oracle.mla_decode(inp.q, inp.kv_cache, inp.block_table, inp.cache_seqlens, inp.softmax_scale,
+                             requests=requests)
+
+
+@pytest.mark.parametrize("force", [0, 1, 2, 3])
+def test_tiny_config(force):
+    inp = W.config_inputs(1)
+    ref_out, ref_lse = _ref(inp)
+    out, lse = run_gpu(inp, force_splits=force)
+    assert_parity(out, lse, ref_out, ref_lse, f"config1 force_splits={force}")
+
+
+def test_tiny_config_two_parts():
+    # The other reading of "num_splits = 2": two parts, so only request 1 is cut.
+    inp = W.config_inputs(1)
+    ref_out, ref_lse = _ref(inp)
+    out, lse = run_gpu(inp, num_cus=2)
+    assert_parity(out, lse, ref_out, ref_lse, "config1 two parts")
+
+
+def test_memory_bound_config_full():
+    inp = W.config_inputs(2)
+    ref_out, ref_lse = _ref(inp)
+    out, lse = run_gpu(inp)
+    assert_parity(out, lse, ref_out, ref_lse, "config2 full")
+
+
+@pytest.mark.parametrize("idx", [3, 5])
+def test_h128_configs_full(idx):
+    inp = W.config_inputs(idx)
+    ref_out, ref_lse = _ref(inp)
+    out, lse = run_gpu(inp)
+    assert_parity(out, lse, ref_out, ref_lse, f"config{idx} full")
+
+
+def test_mtp_config_sampled_requests():
+    inp = W.config_inputs(4)
+    sl = inp.cache_seqlens
+    picks = sorted(set([int(np.argmax(sl)), int(np.argmin(sl)), 0, inp.batch - 1] +
+                       np.random.default_rng(0).choice(inp.batch, 8, replace=False).tolist()))
+    ref_out, ref_lse = _ref(inp, requests=picks)
+    out, lse = run_gpu(inp)
+    assert_parity(out[picks], lse[picks], ref_out[picks], ref_lse[picks], f"config4 requests {picks}")
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+
+EDGE_LENS = [0, 1, 2, 63, 64, 65, 127, 128, 129, 200, 1000]
+
+
+@pytest.mark.parametrize("h_q,s_q", [(16, 1), (128, 1), (64, 2), (8, 1), (24, 1), (48, 2), (80, 2)])
+@pytest.mark.parametrize("force", [0, 2])
+def test_edge_lengths_and_head_counts(h_q, s_q, force):
+    inp = W.make_inputs(len(EDGE_LENS), s_q, h_q, EDGE_LENS, pool=None, max_blocks=17, seed=h_q * 10 + s_q)
+    ref_out, ref_lse = _ref(inp)
+    out, lse = run_gpu(inp, force_splits=force)
+    assert_parity(out, lse, ref_out, ref_lse, f"edge lengths h_q={h_q} s_q={s_q} force={force}")
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))     # L = 0
+
+
+def test_many_parts_on_few_blocks():
+    # More parts than blocks: most parts get nothing; requests of one block each.
+    inp = W.make_inputs(5, 1, 128, [64, 1, 3, 64, 10], pool=None, max_blocks=1, seed=77)
+    ref_out, ref_lse = _ref(inp)
+    out, lse = run_gpu(inp)
+    assert_parity(out, lse, ref_out, ref_lse, "tiny requests, 256 parts")
+
+
+def test_nan_in_page_tails_and_unused_pages():
+    inp = W.make_inputs(4, 1, 64, [70, 129, 1, 250], pool=20, max_blocks=4, seed=12, tail_poison=float("nan"))
+    assert np.isnan(W.bf16_bits_to_f32(inp.kv_cache)).any()
+    ref_out, ref_lse = _ref(inp)
+    assert np.all(np.isfinite(ref_out))
+    for force in (0, 2):
+        out, lse = run_gpu(inp, force_splits=force)
+        assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+        assert_parity(out, lse, ref_out, ref_lse, f"NaN tails force={force}")
+
+
+def test_restart_when_later_page_outgrows_first_max():
+    # First page scores ~0, a later page ~ +150 (far beyond the 2^64 headroom):
+    # the kernel must take its restart path and still match.
+    rng = np.random.default_rng(3)
+    L = 64 * 5 + 7
+    keys = (0.01 * rng.standard_normal((L, W.D_QK))).astype(np.float32)
+    keys[64 * 3 + 5, :] = 0.5          # one token with a huge score
+    keys[64 * 4 + 1, :] = -0.5
+    q = np.abs(rng.standard_normal((1, 1, 32, W.D_QK))).astype(np.float32)
+    inp = W.make_inputs(1, 1, 32, [L], pool=8, max_blocks=6, seed=5)
+    kv = inp.kv_cache.copy()
+    for t in range(L):
+        kv[inp.block_table[0, t // 64], t % 64, 0] = W.f32_to_bf16_bits(keys[t])
+    inp.kv_cache = kv
+    inp.q = W.f32_to_bf16_bits(q)
+    inp.softmax_scale = 1.0
+    ref_out, ref_lse = _ref(inp)
+    assert ref_lse.max() > 100
+    for force in (0, 1):
+        out, lse = run_gpu(inp, force_splits=force)
+        assert_parity(out, lse, ref_out, ref_lse, f"restart path force={force}")
+
+
+def test_identical_scores_closed_form_on_gpu():
+    rng = np.random.default_rng(21)
+    L = 300
+    inp = W.make_inputs(1, 1, 16, [L], pool=8, max_blocks=5, seed=21)
+    kv = inp.kv_cache.copy()
+    rope = rng.standard_normal(64).astype(np.float32)
+    for t in range(L):
+        row = rng.standard_normal(W.D_QK).astype(np.float32)
+        row[512:] = rope
+        kv[inp.block_table[0, t // 64], t % 64, 0] = W.f32_to_bf16_bits(row)
+    q = rng.standard_normal((1, 1, 16, W.D_QK)).astype(np.float32)
+    q[..., :512] = 0
+    inp.kv_cache, inp.q = kv, W.f32_to_bf16_bits(q)
+    out, lse = run_gpu(inp)
+    vals = np.stack([W.bf16_bits_to_f32(kv[inp.block_table[0, t // 64], t % 64, 0, :512]) for t in range(L)])
+    mean_v = vals.astype(np.float64).mean(axis=0)
+    qr = W.bf16_bits_to_f32(inp.q[0, 0, :, 512:]).astype(np.float64)
+    expect_lse = inp.softmax_scale * (qr @ W.bf16_bits_to_f32(W.f32_to_bf16_bits(rope)).astype(np.float64)) + np.log(L)
+    assert max_err(out[0, 0], np.broadcast_to(mean_v, (16, 512))) <= 1e-2
+    assert max_err(lse[0, :, 0], expect_lse) <= 1e-3
+
+
+def test_page_permutation_is_bitwise_invariant_and_deterministic():
+    inp = W.config_inputs(2)
+    out1, lse1 = run_gpu(inp)
+    out1b, lse1b = run_gpu(inp)
+    assert np.array_equal(out1, out1b) and np.array_equal(lse1, lse1b), "run-to-run difference"
+    perm = np.random.default_rng(9).permutation(inp.num_blocks)
+    kv2 = np.empty_like(inp.kv_cache)
+    kv2[perm] = inp.kv_cache
+    inp2 = W.MlaInputs(inp.name, inp.q, kv2, perm[inp.block_table].astype(np.int32), inp.cache_seqlens,
+                       inp.softmax_scale)
+    out2, lse2 = run_gpu(inp2)
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2), "page permutation changed the result"
+
+
+def test_plan_reuse_across_calls_and_scale_zero():
+    import torch
+    import decode_attention_mla_amd as mla
+    inp = W.config_inputs(1)
+    d = to_device(inp)
+    sched, ns = mla.get_mla_metadata(inp.cache_seqlens, inp.h_q, inp.s_q)
+    ref_out, ref_lse = oracle.mla_decode(inp.q, inp.kv_cache, inp.block_table, inp.cache_seqlens, 0.0)
+    for _ in range(3):    # one plan, several "layers"
+        out, lse = mla.mla_decode_fwd(d["q"], d["kv"], d["bt"], d["sl"], 0.0, sched, ns)
+    torch.cuda.synchronize()
+    assert_parity(out.float().cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, "scale 0, reused plan")
+
+
+def test_python_argument_checks():
+    import torch
+    import decode_attention_mla_amd as mla
+    inp = W.config_inputs(1)
+    d = to_device(inp)
+    sched, ns = mla.get_mla_metadata(inp.cache_seqlens, inp.h_q, inp.s_q)
+    with pytest.raises(ValueError, match="bfloat16"):
+        mla.mla_decode_fwd(d["q"].float(), d["kv"], d["bt"], d["sl"], 0.1, sched, ns)
+    with pytest.raises(ValueError, match="num_splits"):
+        mla.mla_decode_fwd(d["q"], d["kv"], d["bt"], d["sl"], 0.1, sched, ns[:-1])
+    with pytest.raises(ValueError, match="workspace"):
+        mla.mla_decode_fwd(d["q"], d["kv"], d["bt"], d["sl"], 0.1, sched, ns,
+                           workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
