@@ -7,7 +7,7 @@ import pytest
 
 from decode_attention_mla_amd import workloads as W
 import oracle
-from gpu_util import assert_parity, max_err, run_gpu, to_device
+from gpu_util import assert_parity, max_err, out_tol_bound, run_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -68,7 +68,8 @@ def test_edge_lengths_and_head_counts(h_q, s_q, force):
     inp = W.make_inputs(len(EDGE_LENS), s_q, h_q, EDGE_LENS, pool=None, max_blocks=17, seed=h_q * 10 + s_q)
     ref_out, ref_lse = _ref(inp)
     out, lse = run_gpu(inp, force_splits=force)
-    assert_parity(out, lse, ref_out, ref_lse, f"edge lengths h_q={h_q} s_q={s_q} force={force}")
+    assert_parity(out, lse, ref_out, ref_lse, f"edge lengths h_q={h_q} s_q={s_q} force={force}",
+                  out_tol=out_tol_bound(inp))
     assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))     # L = 0
 
 
@@ -77,7 +78,7 @@ def test_many_parts_on_few_blocks():
     inp = W.make_inputs(5, 1, 128, [64, 1, 3, 64, 10], pool=None, max_blocks=1, seed=77)
     ref_out, ref_lse = _ref(inp)
     out, lse = run_gpu(inp)
-    assert_parity(out, lse, ref_out, ref_lse, "tiny requests, 256 parts")
+    assert_parity(out, lse, ref_out, ref_lse, "tiny requests, 256 parts", out_tol=out_tol_bound(inp))
 
 
 def test_nan_in_page_tails_and_unused_pages():
@@ -88,7 +89,7 @@ def test_nan_in_page_tails_and_unused_pages():
     for force in (0, 2):
         out, lse = run_gpu(inp, force_splits=force)
         assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
-        assert_parity(out, lse, ref_out, ref_lse, f"NaN tails force={force}")
+        assert_parity(out, lse, ref_out, ref_lse, f"NaN tails force={force}", out_tol=out_tol_bound(inp))
 
 
 def test_restart_when_later_page_outgrows_first_max():
@@ -111,7 +112,7 @@ def test_restart_when_later_page_outgrows_first_max():
     assert ref_lse.max() > 100
     for force in (0, 1):
         out, lse = run_gpu(inp, force_splits=force)
-        assert_parity(out, lse, ref_out, ref_lse, f"restart path force={force}")
+        assert_parity(out, lse, ref_out, ref_lse, f"restart path force={force}", out_tol=out_tol_bound(inp))
 
 
 def test_identical_scores_closed_form_on_gpu():
