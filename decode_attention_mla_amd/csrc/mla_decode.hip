@@ -62,6 +62,7 @@ int set_error(int code, const char* fmt, ...) {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
@@ -107,6 +108,7 @@ __device__ __forceinline__ int chunk_xor(int t) {
 }
 
 constexpr int kBlockBytes = kPage * 128;           // one 64-dim column block of a page (8 KiB)
+constexpr int kPBufBytes = 4 * 4 * 64 * 16;        // bf16 P fragments: 4 row tiles x 4 k-steps x 64 lanes x 16 B
 
 __device__ __forceinline__ unsigned short f32_to_bf16(float f) {
   unsigned u = __float_as_uint(f);
@@ -145,23 +147,30 @@ __device__ __forceinline__ unsigned dma_lane_offset(int lane, int par) {
   return (unsigned)((lane >> 3) * kRowBytes + (((lane & 7) ^ cx) << 4));
 }
 
-// Copy one 64x576 bf16 page to LDS: wave w issues slices w, w + NW, ...
+// Copy slice k of this wave's share of a 64x576 bf16 page to LDS: wave w
+// owns slices w, w + NW, ... (72 / NW of them).  ``page`` must be uniform.
+template <int NW>
+__device__ __forceinline__ void issue_slice(const unsigned char* page, unsigned lds_base,
+                                            const unsigned dma_off[2], int wave, int k) {
+  const int i = wave + k * NW;
+  // The opaque copy keeps the compiler from hoisting all 72/NW offsets out
+  // of the page loop (they would stay live in VGPRs for the whole kernel).
+  unsigned lane_off = dma_off[i & 1];
+  asm volatile("" : "+v"(lane_off));
+  const unsigned voff = lane_off + (unsigned)((i & 7) * 8 * kRowBytes + (i >> 3) * 128);
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_base + (unsigned)i * 1024u);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(page),
+               "s"(m0)
+               : "memory");
+}
+
+// Copy one whole page (all of this wave's slices) to LDS.
 template <int NW>
 __device__ __forceinline__ void issue_page(const unsigned char* page_any, unsigned lds_base,
                                            const unsigned dma_off[2], int wave) {
   const unsigned char* page = uniform_ptr(page_any);
 #pragma unroll
-  for (int k = 0; k < kSlices / NW; ++k) {
-    const int i = wave + k * NW;
-    // The opaque copy keeps the compiler from hoisting all 72/NW offsets out
-    // of the page loop (they would stay live in VGPRs for the whole kernel).
-    unsigned lane_off = dma_off[i & 1];
-    asm volatile("" : "+v"(lane_off));
-    const unsigned voff = lane_off + (unsigned)((i & 7) * 8 * kRowBytes + (i >> 3) * 128);
-    const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_base + (unsigned)i * 1024u);
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(page), "s"(m0)
-                 : "memory");
-  }
+  for (int k = 0; k < kSlices / NW; ++k) issue_slice<NW>(page, lds_base, dma_off, wave, k);
 }
 
 // Wave-uniform read of read-only metadata through the constant address
@@ -189,8 +198,10 @@ __device__ __forceinline__ void map_block(const Params& p, int& part, int& rg) {
 
 template <int NW>
 __global__ void __launch_bounds__(NW * 64, 1) mla_splitkv_kernel(Params p) {
+  // Two KV page buffers plus the P exchange buffer: exactly 160 KiB.
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kPageBytes];
-  __shared__ int restart_flag[NW];
+  __shared__ __attribute__((aligned(16))) unsigned char pbuf[kPBufBytes];
+  constexpr int kCtPerWave = kColTiles / NW;   // output column tiles owned by each wave
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -202,15 +213,16 @@ __global__ void __launch_bounds__(NW * 64, 1) mla_splitkv_kernel(Params p) {
   const int begin_req = ld_uniform(sp), end_req = ld_uniform(sp + 1), begin_blk = ld_uniform(sp + 2),
             end_blk = ld_uniform(sp + 3), begin_piece = ld_uniform(sp + 4);
 
-  const int rt = rg * NW + wave;            // this wave's 32-row query tile
+  const int rt0 = rg * NW;                  // first 32-row tile of this workgroup
+  const int rt = rt0 + wave;                // the tile whose S^T / softmax this wave owns
   const int h = lane >> 5;                  // which half of the MFMA k / row slots
-  const int col = lane & 31;                // MFMA column = query row within the tile
-  const int r = rt * 32 + col;              // this lane's query row
-  const bool tile_ok = rt < p.row_tiles;
+  const int col = lane & 31;                // MFMA column = query row within a tile
+  const int r = rt * 32 + col;              // this lane's query row (as row owner)
   const bool row_ok = r < p.R;
 
   const unsigned lds0 = (unsigned)(size_t)(LDS_PTR(unsigned char))smem;
   LDS_PTR(unsigned char) lds = (LDS_PTR(unsigned char))smem;
+  LDS_PTR(unsigned char) pb = (LDS_PTR(unsigned char))pbuf;
   const unsigned dma_off[2] = {dma_lane_offset(lane, 0), dma_lane_offset(lane, 1)};
 
   // QK^T A fragment of k-step ks, token tile tau: token col + 32 tau, logical
@@ -244,9 +256,9 @@ __global__ void __launch_bounds__(NW * 64, 1) mla_splitkv_kernel(Params p) {
     const bool split = (ld_uniform(p.num_splits + req + 1) - slot0) > 1;
     const int32_t* bt = p.block_table + (size_t)req * p.max_blocks;
 
-    f32x16 o[kColTiles];
-    float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
+    f32x16 o[NW][kCtPerWave];              // O^T tiles: all row tiles x this wave's columns
     bf16x8 qf[kKSteps];
+    float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
     for (int restarts = 0;; ++restarts) {
     if (lo < hi) issue_page<NW>(p.kv + (size_t)ld_uniform(bt + (lo)) * kPageBytes, lds0, dma_off, wave);
     // Q^T fragments (B operand): row r, dims 16 ks + 8 h .. + 7.
@@ -264,18 +276,25 @@ __global__ void __launch_bounds__(NW * 64, 1) mla_splitkv_kernel(Params p) {
     // inserts no vmcnt(0) inside the page loop, where that would also wait
     // for the next page's copy.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    if (lo + 1 < hi) issue_page<NW>(p.kv + (size_t)ld_uniform(bt + (lo + 1)) * kPageBytes, lds0 + kPageBytes, dma_off, wave);
 #pragma unroll
-    for (int ct = 0; ct < kColTiles; ++ct) o[ct] = f32x16{};
+    for (int a = 0; a < NW; ++a)
+#pragma unroll
+      for (int c = 0; c < kCtPerWave; ++c) o[a][c] = f32x16{};
     l_run = 0.f;
     bool restart = false;
 
     for (int j = lo; j < hi; ++j) {
       const int bsel = (j - lo) & 1;
       LDS_PTR(unsigned char) buf = lds + bsel * kPageBytes;
-      if (j + 1 < hi) wait_vmcnt<(kSlices / NW < 63 ? kSlices / NW : 63)>();
-      else wait_vmcnt<0>();
+      // Page j was copied while page j - 1 was computed (or in the prologue).
+      wait_vmcnt<0>();
       lds_barrier();
+      // The copy of page j + 1 into the other buffer (free since the end of
+      // page j - 1) is interleaved with this page's QK^T MFMAs below.
+      const bool has_next = j + 1 < hi;
+      const unsigned char* next_page =
+          uniform_ptr(p.kv + (size_t)ld_uniform(bt + (has_next ? j + 1 : j)) * kPageBytes);
+      const unsigned next_lds = lds0 + (bsel ^ 1) * kPageBytes;
       const int valid = min(kPage, L - j * kPage);
       if (valid < kPage) {
         // Tokens past the sequence end: zero their rows in every column block
@@ -289,74 +308,76 @@ __global__ void __launch_bounds__(NW * 64, 1) mla_splitkv_kernel(Params p) {
         lds_barrier();
       }
 
-      // ---- S^T = K Q^T for token tiles 0 (tokens 0..31) and 1 (32..63)
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) {
-        LDS_PTR(unsigned char) a = buf + (ks >> 2) * kBlockBytes + qk_base[ks & 3];
-        const u32x4 k0 = *(LDS_PTR(u32x4))(a);
-        const u32x4 k1 = *(LDS_PTR(u32x4))(a + 32 * 128);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k0), qf[ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k1), qf[ks], s1, 0, 0, 0);
-      }
-
-      // ---- online softmax (base 2).  Lane holds tokens 8(v/4) + 4h + v%4 (+32).
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        s0[v] *= p.scale_log2;
-        s1[v] *= p.scale_log2;
-      }
-      if (valid < kPage) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int tok = 8 * (v >> 2) + 4 * h + (v & 3);
-          if (tok >= valid) s0[v] = -INFINITY;
-          if (tok + 32 >= valid) s1[v] = -INFINITY;
-        }
-      }
-      float mloc = fmaxf(s0[0], s1[0]);
-#pragma unroll
-      for (int v = 1; v < 16; ++v) mloc = fmaxf(mloc, fmaxf(s0[v], s1[v]));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      m_seen = fmaxf(m_seen, mloc);
-      if (j == lo && restarts == 0) m_ref = mloc;
-      const int wave_bad = __any(mloc > m_ref + kRefHeadroom) && restarts < kMaxRestarts;
-      i16x8 pk[4];
+      // ---- S^T = K Q^T for this wave's row tile, one 32-token tile at a time
+      // (tokens 0..31, then 32..63), each followed by its softmax and the
+      // write of its bf16 P fragments; K fragments are read one k-step ahead.
+      // The piece's reference max comes from the first token tile.  Lane
+      // holds tokens 32 tile + 8 (v / 4) + 4 h + v % 4 of row col.
+      const bool tail = valid < kPage;
+      bool wave_bad = false;
       float lsum = 0.f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        // The row sum uses the fp32 probabilities; only the PV operand is
-        // rounded to bf16 (summing the rounded values puts ~1e-3 of noise on lse).
-        const float e0 = __builtin_amdgcn_exp2f(s0[v] - m_ref);
-        const float e1 = __builtin_amdgcn_exp2f(s1[v] - m_ref);
-        const unsigned short b0 = f32_to_bf16(e0);
-        const unsigned short b1 = f32_to_bf16(e1);
-        lsum += e0 + e1;
-        pk[v >> 3][v & 7] = (short)b0;
-        pk[2 + (v >> 3)][v & 7] = (short)b1;
-      }
-      l_run += lsum;
-
-      // ---- O^T += V^T P^T over the 4 sixteen-token k-steps of the page.
+      for (int tile = 0; tile < 2; ++tile) {
+        f32x16 sacc = f32x16{};
+        {
+          auto kfrag = [&](int ks) -> bf16x8 {
+            LDS_PTR(unsigned char) a = buf + (ks >> 2) * kBlockBytes + qk_base[ks & 3] + tile * 32 * 128;
+            return __builtin_bit_cast(bf16x8, *(LDS_PTR(u32x4))(a));
+          };
+          bf16x8 k0 = kfrag(0), k1 = kfrag(1);
+          constexpr int kPerTile = kSlices / NW / 2;            // DMA slices per token tile
+          constexpr int kStride = kKSteps / kPerTile;           // MFMAs between slices
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[kk]);
+          for (int ks = 0; ks < kKSteps; ++ks) {
+            bf16x8 n = k1;
+            if (ks + 2 < kKSteps) n = kfrag(ks + 2);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], sacc, 0, 0, 0);
+            if (has_next && ks % kStride == kStride - 1 && ks / kStride < kPerTile)
+              issue_slice<NW>(next_page, next_lds, dma_off, wave, tile * kPerTile + ks / kStride);
+            k0 = k1;
+            k1 = n;
+          }
+        }
+        // (softmax_scale >= 0, so the max of the raw scores, scaled, is the
+        // max of the scaled scores; masked tokens are left out of the max and
+        // get probability exactly 0.)
+        float mloc = -INFINITY;
 #pragma unroll
-        for (int ct = 0; ct < kColTiles; ++ct) {
-          LDS_PTR(unsigned char) a = buf + (ct >> 1) * kBlockBytes + kk * 16 * 128;
-          const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv_base[ct & 1][0]));
-          const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv_base[ct & 1][1]));
-          const i16x8 av = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb, o[ct], 0, 0, 0);
+        for (int v = 0; v < 16; ++v) {
+          const int tok = 32 * tile + 8 * (v >> 2) + 4 * h + (v & 3);
+          mloc = fmaxf(mloc, (tail && tok >= valid) ? -INFINITY : sacc[v]);
+        }
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * p.scale_log2;
+        m_seen = fmaxf(m_seen, mloc);
+        if (j == lo && restarts == 0 && tile == 0) m_ref = mloc;
+        wave_bad |= __any(mloc > m_ref + kRefHeadroom) && restarts < kMaxRestarts;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int kk = 2 * tile + half;   // 16-token k-step of the PV product
+          bf16x8 pk;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int v = 8 * half + e;
+            const int tok = 32 * tile + 8 * (v >> 2) + 4 * h + (v & 3);
+            float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], p.scale_log2, -m_ref));
+            if (tail && tok >= valid) pe = 0.f;
+            lsum += pe;   // row sum from the fp32 values; only the PV operand is bf16
+            pk[e] = (__bf16)pe;
+          }
+          u32x4 bits = __builtin_bit_cast(u32x4, pk);
+          if (kk == 3 && lane == 0)   // probabilities are >= 0: the sign bit carries the restart flag
+            bits[0] = wave_bad ? (bits[0] | 0x8000u) : (bits[0] & ~0x8000u);
+          *(LDS_PTR(u32x4))(pb + ((wave * 4 + kk) * 64 + lane) * 16) = bits;
         }
       }
+      l_run += lsum;
+      lds_barrier();  // every wave's P is in LDS
 
-      if (lane == 0) restart_flag[wave] = wave_bad;
-      lds_barrier();  // every wave is done with this buffer
       int any_bad = 0;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) any_bad |= restart_flag[w];
-      if (any_bad) {
+      for (int w = 0; w < NW; ++w)
+        any_bad |= *(LDS_PTR(unsigned short))(pb + ((w * 4 + 3) * 64) * 16) >> 15;
+      if (any_bad && restarts < kMaxRestarts) {
         // Slow path: a row outgrew its reference max.  Drain the copy in
         // flight, then redo the piece from its first page with the largest
         // max seen so far as the reference.
@@ -365,48 +386,95 @@ __global__ void __launch_bounds__(NW * 64, 1) mla_splitkv_kernel(Params p) {
         restart = true;
         break;
       }
-      if (j + 2 < hi)
-        issue_page<NW>(p.kv + (size_t)ld_uniform(bt + (j + 2)) * kPageBytes, lds0 + bsel * kPageBytes, dma_off, wave);
+
+      // ---- O^T += V^T P^T: this wave's columns, every row tile of the group.
+      {
+        auto vfrag = [&](int kk, int ct) -> bf16x8 {
+          LDS_PTR(unsigned char) a = buf + (ct >> 1) * kBlockBytes + kk * 16 * 128;
+          const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv_base[ct & 1][0]));
+          const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv_base[ct & 1][1]));
+          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        const int ct0 = wave * kCtPerWave;
+        bf16x8 vcur = vfrag(0, ct0);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          bf16x8 pf[NW];
+#pragma unroll
+          for (int a = 0; a < NW; ++a)
+            pf[a] = __builtin_bit_cast(bf16x8, *(LDS_PTR(u32x4))(pb + ((a * 4 + kk) * 64 + lane) * 16));
+#pragma unroll
+          for (int c = 0; c < kCtPerWave; ++c) {
+            bf16x8 vnext = vcur;
+            if (c + 1 < kCtPerWave) vnext = vfrag(kk, ct0 + c + 1);
+            else if (kk + 1 < 4) vnext = vfrag(kk + 1, ct0);
+#pragma unroll
+            for (int a = 0; a < NW; ++a)
+              o[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur, pf[a], o[a][c], 0, 0, 0);
+            vcur = vnext;
+          }
+        }
+      }
+
+      lds_barrier();  // every wave is done with this page buffer and with P
     }
     if (!restart) break;
     m_ref = m_seen;
     }
 
-    // ---- epilogue: normalise and write out / lse, or the partial slot.
+    // ---- epilogue.  Row owners publish 1 / l for their rows through LDS
+    // (the P buffer is free after the last page's barrier); every wave then
+    // normalises its columns for all row tiles of the group.
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse2 = l_tot > 0.f ? m_ref + __builtin_amdgcn_logf(l_tot) : -INFINITY;
-    if (!tile_ok) continue;
-    if (!split) {
-      if (row_ok) {
-        unsigned short* orow = p.out + ((size_t)req * p.R + r) * kDv;
+    if (h == 0) *(LDS_PTR(float))(pb + (wave * 32 + col) * 4) = inv;
+    lds_barrier();
+    float inv_rows[NW];
 #pragma unroll
-        for (int ct = 0; ct < kColTiles; ++ct) {
+    for (int a = 0; a < NW; ++a) inv_rows[a] = *(LDS_PTR(float))(pb + (a * 32 + col) * 4);
+    lds_barrier();  // the next piece's first P writes come after this
+    if (!split) {
+#pragma unroll
+      for (int a = 0; a < NW; ++a) {
+        const int ra = (rt0 + a) * 32 + col;
+        if (ra >= p.R) continue;
+        unsigned short* orow = p.out + ((size_t)req * p.R + ra) * kDv;
+#pragma unroll
+        for (int c = 0; c < kCtPerWave; ++c) {
+          const int ct = wave * kCtPerWave + c;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            u32x2 w;
-            w[0] = (unsigned)f32_to_bf16(o[ct][4 * g + 0] * inv) | ((unsigned)f32_to_bf16(o[ct][4 * g + 1] * inv) << 16);
-            w[1] = (unsigned)f32_to_bf16(o[ct][4 * g + 2] * inv) | ((unsigned)f32_to_bf16(o[ct][4 * g + 3] * inv) << 16);
-            *(u32x2*)(orow + 32 * ct + 8 * g + 4 * h) = w;
+            bf16x4 w4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w4[e] = (__bf16)(o[a][c][4 * g + e] * inv_rows[a]);
+            *(bf16x4*)(orow + 32 * ct + 8 * g + 4 * h) = w4;
           }
         }
-        if (h == 0) {
-          const int s = r / p.h_q, hh = r - s * p.h_q;
-          p.lse[((size_t)req * p.h_q + hh) * p.s_q + s] = lse2 * kLn2;
-        }
+      }
+      if (h == 0 && row_ok) {
+        const int s = r / p.h_q, hh = r - s * p.h_q;
+        p.lse[((size_t)req * p.h_q + hh) * p.s_q + s] = lse2 * kLn2;
       }
     } else {
       const int slot = slot0 + piece;
-      float* dst = p.oacc + ((((size_t)slot * p.row_tiles + rt) * kColTiles) * 64 + lane) * 16;
 #pragma unroll
-      for (int ct = 0; ct < kColTiles; ++ct) {
+      for (int a = 0; a < NW; ++a) {
+        if (rt0 + a >= p.row_tiles) continue;
+        float* dst = p.oacc + ((((size_t)slot * p.row_tiles + rt0 + a) * kColTiles) * 64 + lane) * 16;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 w = {o[ct][4 * g] * inv, o[ct][4 * g + 1] * inv, o[ct][4 * g + 2] * inv, o[ct][4 * g + 3] * inv};
-          *(f32x4*)(dst + (size_t)ct * 64 * 16 + 4 * g) = w;
+        for (int c = 0; c < kCtPerWave; ++c) {
+          const int ct = wave * kCtPerWave + c;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            f32x4 w4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w4[e] = o[a][c][4 * g + e] * inv_rows[a];
+            *(f32x4*)(dst + (size_t)ct * 64 * 16 + 4 * g) = w4;
+          }
         }
       }
-      if (h == 0) p.lacc[(size_t)slot * p.row_tiles * 32 + r] = lse2;
+      if (h == 0 && rt < p.row_tiles) p.lacc[(size_t)slot * p.row_tiles * 32 + r] = lse2;
     }
   }
 }
@@ -414,51 +482,86 @@ __global__ void __launch_bounds__(NW * 64, 1) mla_splitkv_kernel(Params p) {
 // Merge the partial (O_i, lse_i) of every split request (the log-sum-exp
 // merge of the attention-kernel page and the overview page, section 7):
 // M = max lse_i, w_i = 2^(lse_i - M), out = sum w_i O_i / sum w_i,
-// lse = M + log2(sum w_i) (then converted to natural log).  One wave per
-// (request, 32-row tile, 32-column tile); lane = accumulator lane of the
-// main kernel, so partial reads are contiguous 64-byte rows.
-__global__ void __launch_bounds__(64) mla_combine_kernel(Params p) {
+// lse = M + log2(sum w_i) (then converted to natural log).  One workgroup per
+// (request, 32-row tile, 32-column tile); lane = accumulator lane of the main
+// kernel, so every partial read is a contiguous 64-byte run per lane.  The
+// four waves take every fourth split, two in flight at a time, and are
+// summed through LDS.
+constexpr int kCombineWaves = 4;
+
+__global__ void __launch_bounds__(kCombineWaves * 64) mla_combine_kernel(Params p) {
+  __shared__ float red_max[kCombineWaves][64];
+  __shared__ f32x4 red_acc[kCombineWaves - 1][4][64];
+  __shared__ float red_w[kCombineWaves - 1][64];
   const int per_req = p.row_tiles * kColTiles;
   const int req = blockIdx.x / per_req;
   const int rem = blockIdx.x - req * per_req;
   const int rt = rem / kColTiles, ct = rem - rt * kColTiles;
-  const int slot0 = p.num_splits[req];
-  const int n = p.num_splits[req + 1] - slot0;
+  const int slot0 = ld_uniform(p.num_splits + req);
+  const int n = ld_uniform(p.num_splits + req + 1) - slot0;
   if (n <= 1) return;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int h = lane >> 5;
   const int r = rt * 32 + (lane & 31);
-  if (r >= p.R) return;
   const size_t rows_p = (size_t)p.row_tiles * 32;
+  const float* lrow = p.lacc + (size_t)slot0 * rows_p + r;
+  const size_t ostride = (size_t)p.row_tiles * kColTiles * 64 * 16;   // floats per slot
+  const float* obase = p.oacc + ((((size_t)slot0 * p.row_tiles + rt) * kColTiles + ct) * 64 + lane) * 16;
 
   float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, p.lacc[(size_t)(slot0 + i) * rows_p + r]);
-  float acc[16];
+  for (int i = wave; i < n; i += kCombineWaves) M = fmaxf(M, lrow[(size_t)i * rows_p]);
+  red_max[wave][lane] = M;
+  __syncthreads();
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  for (int w = 0; w < kCombineWaves; ++w) M = fmaxf(M, red_max[w][lane]);
+
+  f32x4 acc[4] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
   float wsum = 0.f;
   if (M != -INFINITY) {
-    for (int i = 0; i < n; ++i) {
-      const float w = __builtin_amdgcn_exp2f(p.lacc[(size_t)(slot0 + i) * rows_p + r] - M);
-      const float* src = p.oacc + ((((size_t)(slot0 + i) * p.row_tiles + rt) * kColTiles + ct) * 64 + lane) * 16;
-      wsum += w;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 v = *(const f32x4*)(src + 4 * g);
-        acc[4 * g] += w * v[0];
-        acc[4 * g + 1] += w * v[1];
-        acc[4 * g + 2] += w * v[2];
-        acc[4 * g + 3] += w * v[3];
-      }
+    int i = wave;
+    for (; i + kCombineWaves < n; i += 2 * kCombineWaves) {
+      const int i2 = i + kCombineWaves;
+      const float l1 = lrow[(size_t)i * rows_p], l2 = lrow[(size_t)i2 * rows_p];
+      const f32x4* s1 = (const f32x4*)(obase + (size_t)i * ostride);
+      const f32x4* s2 = (const f32x4*)(obase + (size_t)i2 * ostride);
+      const f32x4 a0 = s1[0], a1 = s1[1], a2 = s1[2], a3 = s1[3];
+      const f32x4 b0 = s2[0], b1 = s2[1], b2 = s2[2], b3 = s2[3];
+      const float w1 = __builtin_amdgcn_exp2f(l1 - M), w2 = __builtin_amdgcn_exp2f(l2 - M);
+      wsum += w1 + w2;
+      acc[0] += w1 * a0 + w2 * b0;
+      acc[1] += w1 * a1 + w2 * b1;
+      acc[2] += w1 * a2 + w2 * b2;
+      acc[3] += w1 * a3 + w2 * b3;
     }
+    if (i < n) {
+      const float w1 = __builtin_amdgcn_exp2f(lrow[(size_t)i * rows_p] - M);
+      const f32x4* s1 = (const f32x4*)(obase + (size_t)i * ostride);
+      wsum += w1;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) acc[g] += w1 * s1[g];
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) red_acc[wave - 1][g][lane] = acc[g];
+    red_w[wave - 1][lane] = wsum;
+  }
+  __syncthreads();
+  if (wave > 0 || r >= p.R) return;
+#pragma unroll
+  for (int w = 0; w < kCombineWaves - 1; ++w) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc[g] += red_acc[w][g][lane];
+    wsum += red_w[w][lane];
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   unsigned short* orow = p.out + ((size_t)req * p.R + r) * kDv;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     u32x2 w;
-    w[0] = (unsigned)f32_to_bf16(acc[4 * g] * inv) | ((unsigned)f32_to_bf16(acc[4 * g + 1] * inv) << 16);
-    w[1] = (unsigned)f32_to_bf16(acc[4 * g + 2] * inv) | ((unsigned)f32_to_bf16(acc[4 * g + 3] * inv) << 16);
+    w[0] = (unsigned)f32_to_bf16(acc[g][0] * inv) | ((unsigned)f32_to_bf16(acc[g][1] * inv) << 16);
+    w[1] = (unsigned)f32_to_bf16(acc[g][2] * inv) | ((unsigned)f32_to_bf16(acc[g][3] * inv) << 16);
     *(u32x2*)(orow + 32 * ct + 8 * g + 4 * h) = w;
   }
   if (ct == 0 && h == 0) {
@@ -601,8 +704,8 @@ extern "C" int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t
     return set_error(MLA_ERR_INVALID,
                      "mla_decode_fwd: batch=%d s_q=%d h_q=%d num_blocks=%d max_blocks_per_seq=%d num_parts=%d",
                      batch, s_q, h_q, num_blocks, max_blocks_per_seq, num_parts);
-  if (!std::isfinite(softmax_scale))
-    return set_error(MLA_ERR_INVALID, "mla_decode_fwd: softmax_scale is not finite");
+  if (!std::isfinite(softmax_scale) || softmax_scale < 0.f)
+    return set_error(MLA_ERR_INVALID, "mla_decode_fwd: softmax_scale must be finite and >= 0");
   const Geometry g = geometry(h_q, s_q);
   const int slots = num_parts + batch - 1;
   const size_t need = mla_workspace_bytes(slots, h_q, s_q);
@@ -637,13 +740,13 @@ extern "C" int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t
   switch (g.waves) {
     case 1: hipLaunchKernelGGL(mla_splitkv_kernel<1>, dim3(grid), dim3(64), 0, st, prm); break;
     case 2: hipLaunchKernelGGL(mla_splitkv_kernel<2>, dim3(grid), dim3(128), 0, st, prm); break;
-    case 3: hipLaunchKernelGGL(mla_splitkv_kernel<3>, dim3(grid), dim3(192), 0, st, prm); break;
-    default: hipLaunchKernelGGL(mla_splitkv_kernel<4>, dim3(grid), dim3(256), 0, st, prm); break;
+    case 4: hipLaunchKernelGGL(mla_splitkv_kernel<4>, dim3(grid), dim3(256), 0, st, prm); break;
+    default: return set_error(MLA_ERR_INVALID, "mla_decode_fwd: unsupported wave count %d", g.waves);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(MLA_ERR_HIP, "mla_decode_fwd: main kernel launch: %s", hipGetErrorString(e));
   if (ev) hipEventRecord(ev[1], st);
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(batch * g.row_tiles * kColTiles), dim3(64), 0, st, prm);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(batch * g.row_tiles * kColTiles), dim3(kCombineWaves * 64), 0, st, prm);
   e = hipGetLastError();
   if (e != hipSuccess) return set_error(MLA_ERR_HIP, "mla_decode_fwd: combine launch: %s", hipGetErrorString(e));
   if (ev) hipEventRecord(ev[2], st);

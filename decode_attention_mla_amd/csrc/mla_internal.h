@@ -31,7 +31,8 @@ inline Geometry geometry(int h_q, int s_q) {
   Geometry g;
   g.R = h_q * s_q;
   g.row_tiles = (g.R + kRowTile - 1) / kRowTile;
-  g.waves = g.row_tiles < kMaxWaves ? g.row_tiles : kMaxWaves;
+  // 1, 2 or 4 waves: each wave owns 16 / waves of the 512 output columns.
+  g.waves = g.row_tiles >= 3 ? kMaxWaves : g.row_tiles;
   g.row_groups = (g.row_tiles + g.waves - 1) / g.waves;
   return g;
 }

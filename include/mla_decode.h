@@ -122,7 +122,7 @@ size_t mla_workspace_bytes(int total_splits, int h_q, int s_q);
  *                 logical pages >= ceil(L/64) are never read
  *   cache_seqlens device int32 [batch]; must equal the lengths the plan was
  *                 made from, and L <= 64 * max_blocks_per_seq
- *   softmax_scale multiplies the q.k scores
+ *   softmax_scale multiplies the q.k scores; finite and >= 0
  *   sched         device int32 [num_parts, 8] from mla_get_metadata/mla_plan
  *   num_splits    device int32 [batch + 1] from the same plan
  *   workspace     device, >= mla_workspace_bytes(num_parts + batch - 1, h_q, s_q)
