@@ -479,6 +479,219 @@ __global__ void __launch_bounds__(NW * 64, 1) mla_splitkv_kernel(Params p) {
   }
 }
 
+// Small row counts (R = s_q * h_q <= 16), the memory-bound regime: four waves
+// split every page's 64 tokens, 16 each, with 16x16 MFMA tiles, so the page
+// is consumed by all four SIMDs at once and every LDS byte is read once.
+// S^T = K Q^T uses v_mfma_f32_16x16x32_bf16; its accumulator layout (lane =
+// query row, 4 consecutive tokens) is exactly the B operand of the PV product
+// v_mfma_f32_16x16x16_bf16, whose A operand (V^T, 4 consecutive tokens of one
+// column) is one ds_read_b64_tr_b16.  Each wave runs its own online softmax
+// (running max with a lazy rescale: the 128-register accumulator is only
+// rescaled when a row max grows by more than 2^8) and the four states are
+// merged through LDS with the log-sum-exp rule at the end of a piece.
+constexpr float kLazyRescale = 8.0f;   // log2 units
+
+__global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kPageBytes];
+  __shared__ float st_m[4][16], st_l[4][16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int part = blockIdx.x;
+  if (part >= p.num_parts) return;
+  const int32_t* sp = p.sched + part * MLA_SCHED_INTS;
+  const int begin_req = ld_uniform(sp), end_req = ld_uniform(sp + 1), begin_blk = ld_uniform(sp + 2),
+            end_blk = ld_uniform(sp + 3), begin_piece = ld_uniform(sp + 4);
+
+  const int g = lane >> 4;          // 16-lane group: k slots 8 g.. (QK) / tokens 4 g.. (PV)
+  const int c16 = lane & 15;        // MFMA column = query row
+  const bool row_ok = c16 < p.R;
+  const int tok0 = 16 * wave;       // this wave's 16 tokens of every page
+
+  const unsigned lds0 = (unsigned)(size_t)(LDS_PTR(unsigned char))smem;
+  LDS_PTR(unsigned char) lds = (LDS_PTR(unsigned char))smem;
+  const unsigned dma_off[2] = {dma_lane_offset(lane, 0), dma_lane_offset(lane, 1)};
+
+  // QK A fragment (16x16x32) of k-step ks: token tok0 + c16, logical chunk
+  // 4 ks + g = block ks / 2, in-block chunk 4 (ks % 2) + g.
+  const int tq = tok0 + c16;
+  int qk_base[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) qk_base[b] = tq * 128 + (((4 * b + g) ^ chunk_xor(tq)) << 4);
+  // PV A fragment (16x16x16) of column tile ct (16 columns): group g, lane Lq
+  // reads 8 bytes of token tok0 + 4 g + Lq / 4, columns 16 ct + 4 (Lq % 4),
+  // i.e. block ct / 4, in-block chunk 2 (ct % 4) + (Lq % 4) / 2.
+  const int tv = tok0 + 4 * g + (c16 >> 2);
+  int pv_base[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    pv_base[m] = tv * 128 + (((2 * m + ((c16 & 3) >> 1)) ^ chunk_xor(tv)) << 4) + (c16 & 1) * 8;
+
+  for (int req = begin_req; req <= end_req; ++req) {
+    const int L = ld_uniform(p.seqlens + req);
+    const int nblk = (L + kPage - 1) / kPage;
+    const int lo = (req == begin_req) ? begin_blk : 0;
+    const int hi = (req == end_req) ? end_blk : nblk;
+    const int piece = (req == begin_req) ? begin_piece : 0;
+    const int slot0 = ld_uniform(p.num_splits + req);
+    const bool split = (ld_uniform(p.num_splits + req + 1) - slot0) > 1;
+    const int32_t* bt = p.block_table + (size_t)req * p.max_blocks;
+
+    if (lo < hi) issue_page<4>(p.kv + (size_t)ld_uniform(bt + lo) * kPageBytes, lds0, dma_off, wave);
+    // Q^T fragments (B operand of 16x16x32): row c16, dims 32 ks + 8 g .. + 7.
+    bf16x8 qf[kDqk / 32];
+    {
+      const unsigned char* qrow = p.q + ((size_t)req * p.R + (row_ok ? c16 : 0)) * kRowBytes + g * 16;
+      const unsigned keep = row_ok ? ~0u : 0u;
+#pragma unroll
+      for (int ks = 0; ks < kDqk / 32; ++ks) {
+        u32x4 v = *(const u32x4*)(qrow + ks * 64);
+        v &= keep;
+        qf[ks] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+    // Q and the first page (compiler-visible, so nothing is waited on inside
+    // the page loop except the copies it issues itself); the second page's
+    // copy then overlaps the first page's arithmetic.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if (lo + 1 < hi) issue_page<4>(p.kv + (size_t)ld_uniform(bt + lo + 1) * kPageBytes, lds0 + kPageBytes, dma_off, wave);
+
+    f32x4 o[kDv / 16];
+#pragma unroll
+    for (int ct = 0; ct < kDv / 16; ++ct) o[ct] = f32x4{0, 0, 0, 0};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    for (int j = lo; j < hi; ++j) {
+      const int bsel = (j - lo) & 1;
+      LDS_PTR(unsigned char) buf = lds + bsel * kPageBytes;
+      // Page j is this wave's older batch of copies; page j + 1 may be in flight.
+      if (j + 1 < hi)
+        wait_vmcnt<kSlices / 4>();
+      else
+        wait_vmcnt<0>();
+      lds_barrier();
+      const int valid = min(kPage, L - j * kPage);
+      if (valid < kPage) {
+        const int per_blk = (kPage - valid) * 8;
+        for (int u = threadIdx.x; u < per_blk * 9; u += 256) {
+          const int b = u / per_blk, w = u - b * per_blk;
+          *(LDS_PTR(u32x4))(buf + b * kBlockBytes + valid * 128 + w * 16) = u32x4{0, 0, 0, 0};
+        }
+        lds_barrier();
+      }
+
+      // ---- S^T (16 tokens x 16 rows): tokens tok0 + 4 g + v of row c16.
+      f32x4 sa = {0, 0, 0, 0}, sb = {0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < kDqk / 32; ks += 2) {
+        const bf16x8 ka = __builtin_bit_cast(bf16x8, *(LDS_PTR(u32x4))(buf + (ks >> 1) * kBlockBytes + qk_base[0]));
+        const bf16x8 kb = __builtin_bit_cast(bf16x8, *(LDS_PTR(u32x4))(buf + (ks >> 1) * kBlockBytes + qk_base[1]));
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ks], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qf[ks + 1], sb, 0, 0, 0);
+      }
+      f32x4 sv = sa + sb;
+
+      // ---- online softmax for this wave's tokens (base 2, lazy rescale).
+      float x[4];
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tok = tok0 + 4 * g + v;
+        x[v] = tok < valid ? sv[v] * p.scale_log2 : -INFINITY;
+        mloc = fmaxf(mloc, x[v]);
+      }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      const float m_new = fmaxf(m_run, mloc);
+      const bool grow = m_new > m_run + kLazyRescale;
+      if (__any(grow)) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // 0 when m_run = -inf
+        if (grow) m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int ct = 0; ct < kDv / 16; ++ct) o[ct] *= alpha;
+      }
+      i16x4 pb;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float pe = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[v] - m_run);
+        l_run += pe;
+        pb[v] = __builtin_bit_cast(short, (__bf16)pe);
+      }
+
+      // ---- O^T (512 x 16 rows) += V^T (512 x 16 tokens) P^T (16 tokens x 16 rows).
+#pragma unroll
+      for (int ct = 0; ct < kDv / 16; ++ct) {
+        const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_PTR(i16x4))(buf + (ct >> 2) * kBlockBytes + pv_base[ct & 3]));
+        o[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[ct], 0, 0, 0);
+      }
+
+      lds_barrier();  // all waves are done with this buffer
+      if (j + 2 < hi) issue_page<4>(p.kv + (size_t)ld_uniform(bt + j + 2) * kPageBytes, lds0 + bsel * kPageBytes, dma_off, wave);
+    }
+
+    // ---- merge the four waves' states through LDS (page buffers are free).
+    float lw = l_run + __shfl_xor(l_run, 16);
+    lw += __shfl_xor(lw, 32);
+    if (g == 0) {
+      st_m[wave][c16] = m_run;
+      st_l[wave][c16] = lw;
+    }
+    LDS_PTR(f32x4) ob = (LDS_PTR(f32x4))lds;   // [wave][ct][lane] f32x4
+#pragma unroll
+    for (int ct = 0; ct < kDv / 16; ++ct) ob[(wave * (kDv / 16) + ct) * 64 + lane] = o[ct];
+    lds_barrier();
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, st_m[w][c16]);
+    float wgt[4], lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = st_m[w][c16];
+      wgt[w] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      lsum += wgt[w] * st_l[w][c16];
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const float lse2 = lsum > 0.f ? M + __builtin_amdgcn_logf(lsum) : -INFINITY;
+    // This wave finalises column tiles 8 wave .. 8 wave + 7 (128 columns).
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int ct = 8 * wave + k;
+      f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc += wgt[w] * ob[(w * (kDv / 16) + ct) * 64 + lane];
+      acc *= inv;
+      if (!row_ok) continue;
+      const int c = 16 * ct + 4 * g;   // 4 consecutive columns of row c16
+      if (!split) {
+        bf16x4 w4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w4[e] = (__bf16)acc[e];
+        *(bf16x4*)(p.out + ((size_t)req * p.R + c16) * kDv + c) = w4;
+      } else {
+        // Partial slot in the 32-row-tile layout the combine kernel reads:
+        // [slot][row tile 0][c / 32][lane32][16], lane32 = row + 32 ((c % 32) / 4 % 2),
+        // element 4 ((c % 32) / 8) + c % 4.
+        const int cc = c & 31;
+        const int lane32 = c16 + 32 * ((cc >> 2) & 1);
+        float* dst = p.oacc + ((((size_t)(slot0 + piece) * p.row_tiles) * kColTiles + (c >> 5)) * 64 + lane32) * 16 +
+                     4 * (cc >> 3);
+        *(f32x4*)dst = acc;
+      }
+    }
+    if (wave == 0 && g == 0 && row_ok) {
+      if (!split) {
+        const int s = c16 / p.h_q, hh = c16 - s * p.h_q;
+        p.lse[((size_t)req * p.h_q + hh) * p.s_q + s] = lse2 * kLn2;
+      } else {
+        p.lacc[(size_t)(slot0 + piece) * p.row_tiles * 32 + c16] = lse2;
+      }
+    }
+    lds_barrier();  // LDS is reused by the next piece
+  }
+}
+
 // Merge the partial (O_i, lse_i) of every split request (the log-sum-exp
 // merge of the attention-kernel page and the overview page, section 7):
 // M = max lse_i, w_i = 2^(lse_i - M), out = sum w_i O_i / sum w_i,
@@ -737,7 +950,9 @@ extern "C" int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t
   hipEvent_t* ev = profile_slot();
   if (ev) hipEventRecord(ev[0], st);
   const int grid = g.row_groups == 1 ? num_parts : 8 * g.row_groups * ((num_parts + 7) / 8);
-  switch (g.waves) {
+  if (g.R <= 16) {
+    hipLaunchKernelGGL(mla_splitkv_small_kernel, dim3(num_parts), dim3(256), 0, st, prm);
+  } else switch (g.waves) {
     case 1: hipLaunchKernelGGL(mla_splitkv_kernel<1>, dim3(grid), dim3(64), 0, st, prm); break;
     case 2: hipLaunchKernelGGL(mla_splitkv_kernel<2>, dim3(grid), dim3(128), 0, st, prm); break;
     case 4: hipLaunchKernelGGL(mla_splitkv_kernel<4>, dim3(grid), dim3(256), 0, st, prm); break;
