@@ -479,20 +479,51 @@ __global__ void __launch_bounds__(NW * 64, 1) mla_splitkv_kernel(Params p) {
   }
 }
 
-// Small row counts (R = s_q * h_q <= 16), the memory-bound regime: four waves
-// split every page's 64 tokens, 16 each, with 16x16 MFMA tiles, so the page
-// is consumed by all four SIMDs at once and every LDS byte is read once.
-// S^T = K Q^T uses v_mfma_f32_16x16x32_bf16; its accumulator layout (lane =
-// query row, 4 consecutive tokens) is exactly the B operand of the PV product
-// v_mfma_f32_16x16x16_bf16, whose A operand (V^T, 4 consecutive tokens of one
-// column) is one ds_read_b64_tr_b16.  Each wave runs its own online softmax
-// (running max with a lazy rescale: the 128-register accumulator is only
-// rescaled when a row max grows by more than 2^8) and the four states are
-// merged through LDS with the log-sum-exp rule at the end of a piece.
-constexpr float kLazyRescale = 8.0f;   // log2 units
+// Small row counts (R = s_q * h_q <= 16), the memory-bound regime.  Wave w
+// owns tokens 16 w .. 16 w + 15 of every page of the piece and runs its own
+// pipeline: it copies just those 16 token rows (18 KiB) into a private pair
+// of LDS stages, so the page loop has no workgroup barrier at all, and each
+// wave keeps its own softmax state, merged with the other three through LDS
+// when the piece ends (log-sum-exp rule).
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: A = 16 tokens x 32 dims of
+//     K (one ds_read_b128 per lane), B = Q^T held in registers.
+//   * The S^T accumulator (lane = query row, 4 consecutive tokens) is the B
+//     operand of v_mfma_f32_16x16x16_bf16 for O^T = V^T P^T; V^T fragments
+//     (4 consecutive tokens of one column) come from ds_read_b64_tr_b16.
+//   * Probabilities use a fixed per-wave reference: the wave's row max over
+//     its first page.  If a later score exceeds it by more than 2^64 the wave
+//     redoes the piece once with the exact maximum as the reference, so the
+//     accumulator is never rescaled and stays in AGPRs.
+constexpr int kWaveTokens = 16;
+constexpr int kStageBytes = kWaveTokens * kRowBytes;   // 18 KiB: 16 token rows
+constexpr int kStageSlices = kStageBytes / 1024;       // 18 wave-wide 1 KiB copies
+constexpr int kStageBlock = kWaveTokens * 128;         // one 64-dim column block of a stage
+
+// Chunk position of logical chunk c of local token t (0..15) in a stage is
+// c ^ stage_swizzle(t): 16 tokens at one chunk (the QK read) and 8 tokens x a
+// chunk pair (the transposing PV read, 32 lanes) both land on distinct banks.
+__device__ __forceinline__ int stage_swizzle(int t) { return 2 * ((t >> 1) & 3) + ((t >> 3) & 1); }
+
+// Global byte offset of lane `lane`'s 16 bytes within slice parity `par` of a
+// wave's 16-token row group: local token 8 par + lane / 8, chunk position lane % 8.
+__device__ __forceinline__ unsigned stage_dma_offset(int lane, int par) {
+  const int t = 8 * par + (lane >> 3);
+  return (unsigned)(t * kRowBytes + (((lane & 7) ^ stage_swizzle(t)) << 4));
+}
+
+// Copy slice i (block i / 2, tokens 8 (i % 2) .. + 7) of this wave's rows.
+__device__ __forceinline__ void issue_stage_slice(const unsigned char* rows, unsigned stage_lds,
+                                                  const unsigned dma_off[2], int i) {
+  unsigned lane_off = dma_off[i & 1];
+  asm volatile("" : "+v"(lane_off));
+  const unsigned voff = lane_off + (unsigned)((i >> 1) * 128);
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(stage_lds + (unsigned)i * 1024u);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(rows), "s"(m0)
+               : "memory");
+}
 
 __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kPageBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * 2 * kStageBytes];
   __shared__ float st_m[4][16], st_l[4][16];
 
   const int lane = threadIdx.x & 63;
@@ -503,29 +534,28 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
   const int begin_req = ld_uniform(sp), end_req = ld_uniform(sp + 1), begin_blk = ld_uniform(sp + 2),
             end_blk = ld_uniform(sp + 3), begin_piece = ld_uniform(sp + 4);
 
-  const int g = lane >> 4;          // 16-lane group: k slots 8 g.. (QK) / tokens 4 g.. (PV)
-  const int c16 = lane & 15;        // MFMA column = query row
+  const int g = lane >> 4;     // 16-lane group
+  const int c16 = lane & 15;   // MFMA column = query row
   const bool row_ok = c16 < p.R;
-  const int tok0 = 16 * wave;       // this wave's 16 tokens of every page
+  const int tok0 = kWaveTokens * wave;
 
-  const unsigned lds0 = (unsigned)(size_t)(LDS_PTR(unsigned char))smem;
-  LDS_PTR(unsigned char) lds = (LDS_PTR(unsigned char))smem;
-  const unsigned dma_off[2] = {dma_lane_offset(lane, 0), dma_lane_offset(lane, 1)};
+  LDS_PTR(unsigned char) wlds = (LDS_PTR(unsigned char))smem + wave * 2 * kStageBytes;
+  const unsigned wlds0 = (unsigned)(size_t)wlds;
+  const unsigned dma_off[2] = {stage_dma_offset(lane, 0), stage_dma_offset(lane, 1)};
 
-  // QK A fragment (16x16x32) of k-step ks: token tok0 + c16, logical chunk
-  // 4 ks + g = block ks / 2, in-block chunk 4 (ks % 2) + g.
-  const int tq = tok0 + c16;
-  int qk_base[2];
+  // QK A fragment of k-step ks: local token c16, logical chunk 4 ks + g =
+  // block ks / 2, in-block chunk 4 (ks % 2) + g.
+  int qk_off[2];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) qk_base[b] = tq * 128 + (((4 * b + g) ^ chunk_xor(tq)) << 4);
-  // PV A fragment (16x16x16) of column tile ct (16 columns): group g, lane Lq
-  // reads 8 bytes of token tok0 + 4 g + Lq / 4, columns 16 ct + 4 (Lq % 4),
-  // i.e. block ct / 4, in-block chunk 2 (ct % 4) + (Lq % 4) / 2.
-  const int tv = tok0 + 4 * g + (c16 >> 2);
-  int pv_base[4];
+  for (int b = 0; b < 2; ++b) qk_off[b] = c16 * 128 + (((4 * b + g) ^ stage_swizzle(c16)) << 4);
+  // PV A fragment of column tile ct: lane (group g, index c16) reads local
+  // token 4 g + c16 / 4, columns 16 ct + 4 (c16 % 4) .. + 3 = block ct / 4,
+  // in-block chunk 2 (ct % 4) + (c16 % 4) / 2, byte 8 (c16 % 2).
+  const int tv = 4 * g + (c16 >> 2);
+  int pv_off[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
-    pv_base[m] = tv * 128 + (((2 * m + ((c16 & 3) >> 1)) ^ chunk_xor(tv)) << 4) + (c16 & 1) * 8;
+    pv_off[m] = tv * 128 + (((2 * m + ((c16 & 3) >> 1)) ^ stage_swizzle(tv)) << 4) + (c16 & 1) * 8;
 
   for (int req = begin_req; req <= end_req; ++req) {
     const int L = ld_uniform(p.seqlens + req);
@@ -536,131 +566,160 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
     const int slot0 = ld_uniform(p.num_splits + req);
     const bool split = (ld_uniform(p.num_splits + req + 1) - slot0) > 1;
     const int32_t* bt = p.block_table + (size_t)req * p.max_blocks;
-
-    if (lo < hi) issue_page<4>(p.kv + (size_t)ld_uniform(bt + lo) * kPageBytes, lds0, dma_off, wave);
-    // Q^T fragments (B operand of 16x16x32): row c16, dims 32 ks + 8 g .. + 7.
-    bf16x8 qf[kDqk / 32];
-    {
-      const unsigned char* qrow = p.q + ((size_t)req * p.R + (row_ok ? c16 : 0)) * kRowBytes + g * 16;
-      const unsigned keep = row_ok ? ~0u : 0u;
-#pragma unroll
-      for (int ks = 0; ks < kDqk / 32; ++ks) {
-        u32x4 v = *(const u32x4*)(qrow + ks * 64);
-        v &= keep;
-        qf[ks] = __builtin_bit_cast(bf16x8, v);
-      }
-    }
-    // Q and the first page (compiler-visible, so nothing is waited on inside
-    // the page loop except the copies it issues itself); the second page's
-    // copy then overlaps the first page's arithmetic.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    if (lo + 1 < hi) issue_page<4>(p.kv + (size_t)ld_uniform(bt + lo + 1) * kPageBytes, lds0 + kPageBytes, dma_off, wave);
+    auto rows_of = [&](int j) {
+      return uniform_ptr(p.kv + (size_t)ld_uniform(bt + j) * kPageBytes + (size_t)tok0 * kRowBytes);
+    };
 
     f32x4 o[kDv / 16];
+    float m_ref = -INFINITY, l_run = 0.f;
+    bool have_ref = false;
+    for (int attempt = 0;; ++attempt) {
+      if (lo < hi) {
+        const unsigned char* r0 = rows_of(lo);
 #pragma unroll
-    for (int ct = 0; ct < kDv / 16; ++ct) o[ct] = f32x4{0, 0, 0, 0};
-    float m_run = -INFINITY, l_run = 0.f;
-
-    for (int j = lo; j < hi; ++j) {
-      const int bsel = (j - lo) & 1;
-      LDS_PTR(unsigned char) buf = lds + bsel * kPageBytes;
-      // Page j is this wave's older batch of copies; page j + 1 may be in flight.
-      if (j + 1 < hi)
-        wait_vmcnt<kSlices / 4>();
-      else
-        wait_vmcnt<0>();
-      lds_barrier();
-      const int valid = min(kPage, L - j * kPage);
-      if (valid < kPage) {
-        const int per_blk = (kPage - valid) * 8;
-        for (int u = threadIdx.x; u < per_blk * 9; u += 256) {
-          const int b = u / per_blk, w = u - b * per_blk;
-          *(LDS_PTR(u32x4))(buf + b * kBlockBytes + valid * 128 + w * 16) = u32x4{0, 0, 0, 0};
+        for (int i = 0; i < kStageSlices; ++i) issue_stage_slice(r0, wlds0, dma_off, i);
+      }
+      // Q^T fragments (B operand): row c16, dims 32 ks + 8 g .. + 7.
+      bf16x8 qf[kDqk / 32];
+      {
+        const unsigned char* qrow = p.q + ((size_t)req * p.R + (row_ok ? c16 : 0)) * kRowBytes + g * 16;
+        const unsigned keep = row_ok ? ~0u : 0u;
+#pragma unroll
+        for (int ks = 0; ks < kDqk / 32; ++ks) {
+          u32x4 v = *(const u32x4*)(qrow + ks * 64);
+          v &= keep;
+          qf[ks] = __builtin_bit_cast(bf16x8, v);
         }
-        lds_barrier();
+      }
+      // Q and the first page (compiler-visible, so the page loop only ever
+      // waits on the copies it issues itself); the second page's copy then
+      // overlaps the first page's arithmetic.
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      if (lo + 1 < hi) {
+        const unsigned char* r1 = rows_of(lo + 1);
+#pragma unroll
+        for (int i = 0; i < kStageSlices; ++i) issue_stage_slice(r1, wlds0 + kStageBytes, dma_off, i);
       }
 
-      // ---- S^T (16 tokens x 16 rows): tokens tok0 + 4 g + v of row c16.
-      f32x4 sa = {0, 0, 0, 0}, sb = {0, 0, 0, 0};
 #pragma unroll
-      for (int ks = 0; ks < kDqk / 32; ks += 2) {
-        const bf16x8 ka = __builtin_bit_cast(bf16x8, *(LDS_PTR(u32x4))(buf + (ks >> 1) * kBlockBytes + qk_base[0]));
-        const bf16x8 kb = __builtin_bit_cast(bf16x8, *(LDS_PTR(u32x4))(buf + (ks >> 1) * kBlockBytes + qk_base[1]));
-        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ks], sa, 0, 0, 0);
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qf[ks + 1], sb, 0, 0, 0);
-      }
-      f32x4 sv = sa + sb;
+      for (int ct = 0; ct < kDv / 16; ++ct) o[ct] = f32x4{0, 0, 0, 0};
+      float m_seen = -INFINITY;
+      l_run = 0.f;
 
-      // ---- online softmax for this wave's tokens (base 2, lazy rescale).
-      float x[4];
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int tok = tok0 + 4 * g + v;
-        x[v] = tok < valid ? sv[v] * p.scale_log2 : -INFINITY;
-        mloc = fmaxf(mloc, x[v]);
-      }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float m_new = fmaxf(m_run, mloc);
-      const bool grow = m_new > m_run + kLazyRescale;
-      if (__any(grow)) {
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // 0 when m_run = -inf
-        if (grow) m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int ct = 0; ct < kDv / 16; ++ct) o[ct] *= alpha;
-      }
-      i16x4 pb;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float pe = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[v] - m_run);
-        l_run += pe;
-        pb[v] = __builtin_bit_cast(short, (__bf16)pe);
-      }
+      for (int j = lo; j < hi; ++j) {
+        const int stage = (j - lo) & 1;
+        LDS_PTR(unsigned char) buf = wlds + stage * kStageBytes;
+        if (j + 1 < hi)
+          wait_vmcnt<kStageSlices>();
+        else
+          wait_vmcnt<0>();
+        const int valid = min(kPage, L - j * kPage) - tok0;   // valid local tokens (may be <= 0)
+        if (valid < kWaveTokens) {
+          // Zero the V part of this wave's rows past the end of the sequence
+          // (page tails may hold anything, NaN included; P is 0 there).
+          const int t_first = max(valid, 0);
+          const int n = (kWaveTokens - t_first) * 8 * 8;      // 16-byte chunks in blocks 0..7
+          for (int u = lane; u < n; u += 64) {
+            const int t = t_first + (u >> 6), b = (u >> 3) & 7, c = u & 7;
+            *(LDS_PTR(u32x4))(buf + b * kStageBlock + t * 128 + c * 16) = u32x4{0, 0, 0, 0};
+          }
+        }
 
-      // ---- O^T (512 x 16 rows) += V^T (512 x 16 tokens) P^T (16 tokens x 16 rows).
+        // ---- S^T (16 tokens x 16 rows) = K Q^T, three accumulation chains.
+        u32x4 kf[kDqk / 32];
 #pragma unroll
-      for (int ct = 0; ct < kDv / 16; ++ct) {
-        const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_PTR(i16x4))(buf + (ct >> 2) * kBlockBytes + pv_base[ct & 3]));
-        o[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[ct], 0, 0, 0);
-      }
+        for (int ks = 0; ks < kDqk / 32; ++ks)
+          kf[ks] = *(LDS_PTR(u32x4))(buf + (ks >> 1) * kStageBlock + qk_off[ks & 1]);
+        f32x4 sacc[3] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+#pragma unroll
+        for (int ks = 0; ks < kDqk / 32; ++ks)
+          sacc[ks % 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[ks]), qf[ks],
+                                                                  sacc[ks % 3], 0, 0, 0);
+        const f32x4 sv = sacc[0] + sacc[1] + sacc[2];
 
-      lds_barrier();  // all waves are done with this buffer
-      if (j + 2 < hi) issue_page<4>(p.kv + (size_t)ld_uniform(bt + j + 2) * kPageBytes, lds0 + bsel * kPageBytes, dma_off, wave);
+        // ---- probabilities against the fixed reference (base 2).
+        float x[4];
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          x[v] = (4 * g + v) < valid ? sv[v] * p.scale_log2 : -INFINITY;
+          mloc = fmaxf(mloc, x[v]);
+        }
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        if (!have_ref) m_ref = mloc;   // first page of the first attempt
+        have_ref = true;
+        m_seen = fmaxf(m_seen, mloc);
+        i16x4 pb;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float pe = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[v] - m_ref);
+          l_run += pe;
+          pb[v] = __builtin_bit_cast(short, (__bf16)pe);
+        }
+
+        // ---- O^T (512 x 16) += V^T (512 x 16 tokens) P^T, two batches of reads.
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          i16x4 vf[16];
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            const int ct = 16 * h + k;
+            vf[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (LDS_PTR(i16x4))(buf + (ct >> 2) * kStageBlock + pv_off[ct & 3]));
+          }
+          if (h == 1) {
+            // Every read of this stage has been issued; once they complete the
+            // stage takes page j + 2.
+            if (j + 2 < hi) {
+              asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+              const unsigned char* r2 = rows_of(j + 2);
+#pragma unroll
+              for (int i = 0; i < kStageSlices; ++i)
+                issue_stage_slice(r2, wlds0 + stage * kStageBytes, dma_off, i);
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < 16; ++k)
+            o[16 * h + k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[k], pb, o[16 * h + k], 0, 0, 0);
+        }
+      }
+      // One retry with the exact maximum always suffices: every probability is then <= 1.
+      if (attempt > 0 || !__any(m_seen > m_ref + kRefHeadroom)) break;
+      m_ref = m_seen;
     }
 
-    // ---- merge the four waves' states through LDS (page buffers are free).
+    // ---- merge the four waves' states.  Each wave parks its accumulator in
+    // its own stages (its copies are all complete), then every wave
+    // finalises 128 of the 512 columns.
     float lw = l_run + __shfl_xor(l_run, 16);
     lw += __shfl_xor(lw, 32);
     if (g == 0) {
-      st_m[wave][c16] = m_run;
+      st_m[wave][c16] = m_ref;
       st_l[wave][c16] = lw;
     }
-    LDS_PTR(f32x4) ob = (LDS_PTR(f32x4))lds;   // [wave][ct][lane] f32x4
 #pragma unroll
-    for (int ct = 0; ct < kDv / 16; ++ct) ob[(wave * (kDv / 16) + ct) * 64 + lane] = o[ct];
+    for (int ct = 0; ct < kDv / 16; ++ct) *(LDS_PTR(f32x4))(wlds + (ct * 64 + lane) * 16) = o[ct];
     lds_barrier();
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, st_m[w][c16]);
+    for (int w = 0; w < 4; ++w)
+      if (st_l[w][c16] > 0.f) M = fmaxf(M, st_m[w][c16]);
     float wgt[4], lsum = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float mw = st_m[w][c16];
-      wgt[w] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      wgt[w] = st_l[w][c16] > 0.f ? __builtin_amdgcn_exp2f(st_m[w][c16] - M) : 0.f;
       lsum += wgt[w] * st_l[w][c16];
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     const float lse2 = lsum > 0.f ? M + __builtin_amdgcn_logf(lsum) : -INFINITY;
-    // This wave finalises column tiles 8 wave .. 8 wave + 7 (128 columns).
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int ct = 8 * wave + k;
       f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-      for (int w = 0; w < 4; ++w) acc += wgt[w] * ob[(w * (kDv / 16) + ct) * 64 + lane];
+      for (int w = 0; w < 4; ++w)
+        acc += wgt[w] * *(LDS_PTR(f32x4))((LDS_PTR(unsigned char))smem + w * 2 * kStageBytes + (ct * 64 + lane) * 16);
       acc *= inv;
       if (!row_ok) continue;
       const int c = 16 * ct + 4 * g;   // 4 consecutive columns of row c16
@@ -688,7 +747,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
         p.lacc[(size_t)(slot0 + piece) * p.row_tiles * 32 + c16] = lse2;
       }
     }
-    lds_barrier();  // LDS is reused by the next piece
+    lds_barrier();  // every wave is done reading the parked accumulators
   }
 }
 
