@@ -185,7 +185,7 @@ def main():
         roof = dict(bound="mfma", achieved=achieved, peak=MFMA_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=achieved / MFMA_PEAK_TFLOPS, traffic=traffic)
         value, unit = head["tflops"], "TFLOP/s"
-    roof["kernel"] = "mla_splitkv_kernel"
+    roof["kernel"] = "mla_splitkv_small_kernel" if head["h_q"] * head["s_q"] <= 16 else "mla_splitkv_kernel"
     cpu = None
     if not args.no_cpu:
         cpu = (cpu_baseline(inp, head["bytes"], 1e9, "GB/s") if bound_hbm
