@@ -7,11 +7,11 @@
 
 namespace mla {
 
-constexpr int kPage = 64;     // tokens per KV page
-constexpr int kDqk = 576;     // 512 latent + 64 RoPE dims (QK^T)
-constexpr int kDv = 512;      // latent dims (PV)
-constexpr int kRowTile = 32;  // query rows per wave (one 32x32 MFMA column block)
-constexpr int kMaxWaves = 4;  // waves per workgroup, one per SIMD
+constexpr int kPage = 64;       // tokens per KV page
+constexpr int kDqk = 576;       // 512 latent + 64 RoPE dims (QK^T)
+constexpr int kDv = 512;        // latent dims (PV)
+constexpr int kSmallRows = 16;  // up to this many query rows: one workgroup covers them all
+constexpr int kRowGroup = 32;   // query rows per workgroup above that
 
 // Records `code` and a printf-style message as this thread's last error; returns `code`.
 int set_error(int code, const char* fmt, ...);
@@ -22,18 +22,13 @@ int plan(const int32_t* seqlens, int batch, int num_parts, int fixed_overhead, i
 // Launch geometry shared by the planner policy and the kernels.
 struct Geometry {
   int R;           // query rows per request = s_q * h_q
-  int row_tiles;   // ceil(R / 32)
-  int waves;       // waves per workgroup (each owns one 32-row tile)
-  int row_groups;  // workgroups per part = ceil(row_tiles / waves)
+  int row_groups;  // workgroups per part: 1 for R <= 16, else ceil(R / 32)
 };
 
 inline Geometry geometry(int h_q, int s_q) {
   Geometry g;
   g.R = h_q * s_q;
-  g.row_tiles = (g.R + kRowTile - 1) / kRowTile;
-  // 1, 2 or 4 waves: each wave owns 16 / waves of the 512 output columns.
-  g.waves = g.row_tiles >= 3 ? kMaxWaves : g.row_tiles;
-  g.row_groups = (g.row_tiles + g.waves - 1) / g.waves;
+  g.row_groups = g.R <= kSmallRows ? 1 : (g.R + kRowGroup - 1) / kRowGroup;
   return g;
 }
 

@@ -61,23 +61,21 @@ def test_get_metadata_policy_matches_reference_plan(h_q, s_q):
     sl = np.array([100, 257, 4096, 0, 70000, 1], dtype=np.int32)
     sched, ns, total = mla.get_mla_metadata_host(sl, h_q, s_q, num_cus=256)
     R = h_q * s_q
-    row_tiles = -(-R // 32)
-    waves = min(4, row_tiles)
-    groups = -(-row_tiles // waves)
+    groups = 1 if R <= 16 else -(-R // 32)
     parts = max(1, 256 // groups)
-    F = 1 if R <= 32 else 2
+    F = 3 if R <= 16 else 2
     s_ref, n_ref = oracle.plan(sl, num_parts=parts, fixed_overhead=F)
     assert np.array_equal(sched, s_ref) and np.array_equal(ns, n_ref) and total == n_ref[-1]
     assert total <= sched.shape[0] + len(sl) - 1
 
 
 def test_workspace_bytes():
-    # 3 slots x 4 row tiles x 32 rows = 384 partial rows: 384 x 512 fp32 = 786432 B
+    # 3 slots x 128 rows = 384 partial rows: 384 x 512 fp32 = 786432 B
     # (256-aligned) plus 384 fp32 lse = 1536 B (256-aligned).
     assert mla.mla_workspace_bytes(3, 128, 1) == 786432 + 1536
     assert mla.mla_workspace_bytes(0, 128, 1) == 0
-    # 16 rows still occupy one 32-row tile: 32 x 512 x 4 = 65536, 32 x 4 = 128 -> 256.
-    assert mla.mla_workspace_bytes(1, 16, 1) == 65536 + 256
+    # 2 slots x 24 rows = 48 rows: 48 x 2048 = 98304 B, 48 x 4 = 192 -> 256.
+    assert mla.mla_workspace_bytes(2, 12, 2) == 98304 + 256
 
 
 def test_plan_errors():
