@@ -2,12 +2,15 @@
 """Benchmark of dense MLA decode on one MI355X; prints one JSON line.
 
 A step is one dense MLA decode call (split-KV kernel + combine kernel) over
-one batch of the synthetic workload, inputs resident in HBM.  The tile plan
-is made once per decode step and reused by every call of that step (as the
-pages prescribe for all layers of a decode step); its host time is measured
-and reported separately as ``plan_us``.  Several copies of q and the KV pool
-are rotated between steps so that the 256 MB memory-side cache cannot serve
-one step's pages to the next.
+one batch of the synthetic workload, inputs resident in HBM.  Steps are
+replayed from a HIP graph, as serving engines run decode (the
+attention-kernel page's CUDA-graph section); the plain eager rate is
+reported beside it.  The tile plan is made once per decode step and reused
+by every call of that step (as the pages prescribe for all layers of a
+decode step); its host time is measured and reported separately as
+``plan_us``.  Several copies of q and the KV pool are rotated between steps
+so that the 256 MB memory-side cache cannot serve one step's pages to the
+next.
 
 Headline workload: TP-sharded memory-bound decode (batch 16, h_q 16,
 L ~ U[1024, 4096]) -> effective HBM GB/s.  The h_q = 128 workloads
@@ -57,6 +60,16 @@ def measured_traffic(config_name: str):
 
 
 def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6):
+    """Times one workload three ways:
+
+    * graph: ``rot`` decode steps (one per rotating copy of q and the KV
+      pool) captured once in a HIP graph and replayed -- how serving engines
+      run a decode step, and the whole-job throughput reported as ``value``;
+    * kernels: eager calls enqueued behind a GPU sleep so the host runs
+      ahead, with the library's per-kernel HIP events (recorded by the
+      dispatch itself) -> the average main / combine kernel durations;
+    * eager: plain back-to-back calls from Python, wall clock (reference).
+    """
     import torch
     import decode_attention_mla_amd as mla
     from decode_attention_mla_amd import workloads as W
@@ -99,26 +112,57 @@ def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    mla.profile_start(steps)
+
+    # -- graph replay (value)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step(0)                       # warm the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            for i in range(rot):
+                step(i)
     torch.cuda.synchronize()
+    replays = max(1, steps // rot)
+    for _ in range(max(1, warmup // rot)):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
-    for i in range(steps):
-        step(i)
+    for _ in range(replays):
+        graph.replay()
     ev1.record()
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
+    graph_wall_ms = (time.perf_counter() - t0) * 1e3
+    graph_steps = replays * rot
+    ms_per_step = max(graph_wall_ms, ev0.elapsed_time(ev1)) / graph_steps
+    del graph
+
+    # -- per-kernel durations (eager, host ahead of the GPU)
+    torch.cuda._sleep(int(2.0e9 * 0.002 * steps))   # ~2 ms of GPU time per 100 calls at 2 GHz
+    mla.profile_start(steps)
+    for i in range(steps):
+        step(i)
     main_ms, comb_ms, calls = mla.profile_stop()
-    gpu_ms = ev0.elapsed_time(ev1)
+    torch.cuda.synchronize()
     assert calls == steps, (calls, steps)
-    ms_per_step = wall_ms / steps
     main_avg = main_ms / calls
     comb_avg = comb_ms / calls
+
+    # -- plain eager wall clock (reference)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / steps
+
     res = dict(
         workload=inp.name, batch=b, s_q=inp.s_q, h_q=inp.h_q, sum_seqlen=int(inp.cache_seqlens.sum()),
-        parts=int(sched.shape[0]), total_splits=int(total), rotating_copies=rot,
-        flops=flops, bytes=nbytes, ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / steps,
+        parts=int(sched.shape[0]), total_splits=int(total), rotating_copies=rot, graph_steps=graph_steps,
+        flops=flops, bytes=nbytes, ms_per_step=ms_per_step, eager_ms_per_step=eager_ms,
         main_kernel_ms=main_avg, combine_kernel_ms=comb_avg, plan_us=plan_us,
         tflops=flops / (ms_per_step * 1e-3) / 1e12, gbs=nbytes / (ms_per_step * 1e-3) / 1e9,
         main_kernel_tflops=flops / (main_avg * 1e-3) / 1e12, main_kernel_gbs=nbytes / (main_avg * 1e-3) / 1e9,
@@ -201,6 +245,7 @@ def main():
             extra[f"config{idx}"] = dict(
                 workload=r["workload"], tflops=r["tflops"], frac_mfma_peak=r["tflops"] / MFMA_PEAK_TFLOPS,
                 gbs=r["gbs"], frac_hbm_peak=r["gbs"] / HBM_PEAK_GBS, ms_per_step=r["ms_per_step"],
+                eager_ms_per_step=r["eager_ms_per_step"], main_kernel_tflops=r["main_kernel_tflops"],
                 main_kernel_ms=r["main_kernel_ms"], combine_kernel_ms=r["combine_kernel_ms"],
                 parts=r["parts"], total_splits=r["total_splits"], plan_us=r["plan_us"])
 
@@ -212,7 +257,8 @@ def main():
                     d_qk=576, d_v=512, page=64, sum_seqlen=head["sum_seqlen"], parts=head["parts"],
                     total_splits=head["total_splits"], rotating_kv_copies=head["rotating_copies"]),
         roofline=roof, cpu_baseline=cpu,
-        detail=dict(gpu_ms_per_step=head["gpu_ms_per_step"], main_kernel_ms=head["main_kernel_ms"],
+        detail=dict(timing="graph replay", eager_ms_per_step=head["eager_ms_per_step"],
+                    graph_steps=head["graph_steps"], main_kernel_ms=head["main_kernel_ms"],
                     combine_kernel_ms=head["combine_kernel_ms"], plan_us=head["plan_us"],
                     algorithmic_bytes=head["bytes"], algorithmic_flops=head["flops"],
                     kernel_sha256_16=kernel_hash()),

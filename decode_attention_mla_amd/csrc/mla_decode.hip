@@ -942,14 +942,16 @@ extern "C" int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t
     main_fn = (const void*)mla_splitkv_kernel;
     grid = g.row_groups == 1 ? num_parts : 8 * g.row_groups * ((num_parts + 7) / 8);
   }
-  hipError_t e = hipExtLaunchKernel(main_fn, dim3(grid), dim3(256), args, 0, st, ev ? ev[0] : nullptr,
-                                    ev ? ev[1] : nullptr, 0);
+  // Plain launches unless profiling (these are what stream capture records).
+  hipError_t e = ev ? hipExtLaunchKernel(main_fn, dim3(grid), dim3(256), args, 0, st, ev[0], ev[1], 0)
+                    : hipLaunchKernel(main_fn, dim3(grid), dim3(256), args, 0, st);
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) return set_error(MLA_ERR_HIP, "mla_decode_fwd: main kernel launch: %s", hipGetErrorString(e));
   const long long pairs = (long long)batch * g.R;
   const int cgrid = (int)(pairs < kCombineMaxGrid ? pairs : kCombineMaxGrid);
-  e = hipExtLaunchKernel((const void*)mla_combine_kernel, dim3(cgrid), dim3(kCombineWaves * 64), args, 0, st,
-                         ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0);
+  e = ev ? hipExtLaunchKernel((const void*)mla_combine_kernel, dim3(cgrid), dim3(kCombineWaves * 64), args, 0, st,
+                              ev[2], ev[3], 0)
+         : hipLaunchKernel((const void*)mla_combine_kernel, dim3(cgrid), dim3(kCombineWaves * 64), args, 0, st);
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) return set_error(MLA_ERR_HIP, "mla_decode_fwd: combine launch: %s", hipGetErrorString(e));
   return MLA_OK;

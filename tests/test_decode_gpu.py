@@ -177,3 +177,45 @@ def test_python_argument_checks():
     with pytest.raises(ValueError, match="workspace"):
         mla.mla_decode_fwd(d["q"], d["kv"], d["bt"], d["sl"], 0.1, sched, ns,
                            workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+
+
+@pytest.mark.parametrize("case", ["config2", "h64_sq2_forced_splits"])
+def test_graph_replay_matches_eager(case):
+    """One decode call captured in a HIP graph and replayed several times,
+    with eager work (clearing the outputs) and synchronisation between the
+    replays: every replay must reproduce the eager result bit for bit."""
+    import torch
+    import decode_attention_mla_amd as mla
+    if case == "config2":
+        inp, force = W.config_inputs(2), 0
+    else:
+        inp, force = W.make_inputs(6, 2, 64, [70, 129, 1000, 0, 640, 300], pool=None, max_blocks=16, seed=31), 3
+    d = to_device(inp)
+    sched, ns = mla.get_mla_metadata(inp.cache_seqlens, inp.h_q, inp.s_q, force_splits=force)
+    ref_out, ref_lse = mla.mla_decode_fwd(d["q"], d["kv"], d["bt"], d["sl"], inp.softmax_scale, sched, ns)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = ref_out.clone(), ref_lse.clone()
+    out, lse = torch.empty_like(ref_out), torch.empty_like(ref_lse)
+    ws = torch.empty(mla.mla_workspace_bytes(sched.shape[0] + inp.batch - 1, inp.h_q, inp.s_q),
+                     dtype=torch.uint8, device=out.device)
+
+    def call():
+        mla.mla_decode_fwd(d["q"], d["kv"], d["bt"], d["sl"], inp.softmax_scale, sched, ns, out=out, lse=lse,
+                           workspace=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        call()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.synchronize()
+    for _ in range(4):
+        out.zero_()
+        lse.fill_(1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
