@@ -304,6 +304,14 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
   LDS_PTR(unsigned char) wlds = (LDS_PTR(unsigned char))smem + wave * 2 * kStageBytes;
   const unsigned wlds0 = (unsigned)(size_t)wlds;
   const unsigned dma_off[2] = {stage_dma_offset(lane, 0), stage_dma_offset(lane, 1)};
+  // The request's query rows are staged like a page (row r in token slot r);
+  // slots >= R copy row 0 instead (in bounds; their fragments are zeroed).
+  unsigned q_dma_off[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int t = 8 * par + (lane >> 3);
+    q_dma_off[par] = t < p.R ? dma_off[par] : (unsigned)(((lane & 7) ^ stage_swizzle(t)) << 4);
+  }
 
   // QK A fragment of k-step ks: local token c16, logical chunk 4 ks + g =
   // block ks / 2, in-block chunk 4 (ks % 2) + g.
@@ -336,14 +344,30 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
     f32x4 o[kDv / 16];
     float m_ref = -INFINITY, l_run = 0.f;
     bool have_ref = false;
+    // Q^T fragments (B operand): row c16, dims 32 ks + 8 g .. + 7.  Q is
+    // copied into stage 1 ahead of the first page, read into registers as
+    // soon as it lands, and stage 1 then takes the second page, so both
+    // pages are in flight while Q is in use.  (All global reads here are
+    // explicit copies with explicit waits: no compiler-tracked load may be
+    // outstanding while page copies are in flight.)
+    bf16x8 qf[kQkSteps];
+    issue_stage(uniform_ptr(p.q + (size_t)req * p.R * kRowBytes), wlds0 + kStageBytes, q_dma_off);
     for (int attempt = 0;; ++attempt) {
       if (lo < hi) issue_stage(rows_of(lo), wlds0, dma_off);
-      bf16x8 qf[kQkSteps];
-      load_q(qf, p, req, c16, g);
-      // Q and the first page (compiler-visible, so the page loop only ever
-      // waits on the copies it issues itself); the second page's copy then
-      // overlaps the first page's arithmetic.
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      if (attempt == 0) {
+        if (lo < hi)
+          wait_vmcnt<kStageSlices>();   // Q (the first page may still be in flight)
+        else
+          wait_vmcnt<0>();
+        const unsigned keep = row_ok ? ~0u : 0u;
+#pragma unroll
+        for (int ks = 0; ks < kQkSteps; ++ks) {
+          u32x4 v = *(LDS_PTR(u32x4))(wlds + kStageBytes + (ks >> 1) * kStageBlock + qk_off[ks & 1]);
+          v &= keep;
+          qf[ks] = __builtin_bit_cast(bf16x8, v);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage 1 is free again
+      }
       if (lo + 1 < hi) issue_stage(rows_of(lo + 1), wlds0 + kStageBytes, dma_off);
 
 #pragma unroll
