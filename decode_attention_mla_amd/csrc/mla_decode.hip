@@ -153,19 +153,27 @@ __device__ __forceinline__ unsigned stage_dma_offset(int lane, int par) {
 }
 
 // Copy slice i (block i / 2, tokens 8 (i % 2) .. + 7) of this wave's rows.
+// kStream: nontemporal hint, for data that this launch reads exactly once;
+// without it the lines stay in L2 for the other row groups of the part.
+template <bool kStream>
 __device__ __forceinline__ void issue_stage_slice(const unsigned char* rows, unsigned stage_lds,
                                                   const unsigned dma_off[2], int i) {
   unsigned lane_off = dma_off[i & 1];
   asm volatile("" : "+v"(lane_off));
   const unsigned voff = lane_off + (unsigned)((i >> 1) * 128);
   const unsigned m0 = __builtin_amdgcn_readfirstlane(stage_lds + (unsigned)i * 1024u);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(rows), "s"(m0)
-               : "memory");
+  if constexpr (kStream)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(rows), "s"(m0)
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(rows), "s"(m0)
+                 : "memory");
 }
 
+template <bool kStream>
 __device__ __forceinline__ void issue_stage(const unsigned char* rows, unsigned stage_lds, const unsigned dma_off[2]) {
 #pragma unroll
-  for (int i = 0; i < kStageSlices; ++i) issue_stage_slice(rows, stage_lds, dma_off, i);
+  for (int i = 0; i < kStageSlices; ++i) issue_stage_slice<kStream>(rows, stage_lds, dma_off, i);
 }
 
 // Rows past the end of the sequence may hold anything (NaN included): zero
@@ -351,9 +359,9 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
     // explicit copies with explicit waits: no compiler-tracked load may be
     // outstanding while page copies are in flight.)
     bf16x8 qf[kQkSteps];
-    issue_stage(uniform_ptr(p.q + (size_t)req * p.R * kRowBytes), wlds0 + kStageBytes, q_dma_off);
+    issue_stage<false>(uniform_ptr(p.q + (size_t)req * p.R * kRowBytes), wlds0 + kStageBytes, q_dma_off);
     for (int attempt = 0;; ++attempt) {
-      if (lo < hi) issue_stage(rows_of(lo), wlds0, dma_off);
+      if (lo < hi) issue_stage<true>(rows_of(lo), wlds0, dma_off);
       if (attempt == 0) {
         if (lo < hi)
           wait_vmcnt<kStageSlices>();   // Q (the first page may still be in flight)
@@ -368,7 +376,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage 1 is free again
       }
-      if (lo + 1 < hi) issue_stage(rows_of(lo + 1), wlds0 + kStageBytes, dma_off);
+      if (lo + 1 < hi) issue_stage<true>(rows_of(lo + 1), wlds0 + kStageBytes, dma_off);
 
 #pragma unroll
       for (int ct = 0; ct < kDv / 16; ++ct) o[ct] = f32x4{0, 0, 0, 0};
@@ -413,7 +421,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
             // Every read of this stage has been issued; once they complete the
             // stage takes page j + 2.
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            issue_stage(rows_of(j + 2), wlds0 + stage * kStageBytes, dma_off);
+            issue_stage<true>(rows_of(j + 2), wlds0 + stage * kStageBytes, dma_off);
           }
 #pragma unroll
           for (int k = 0; k < 16; ++k)
@@ -437,15 +445,23 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
 #pragma unroll
     for (int ct = 0; ct < kDv / 16; ++ct) *(LDS_PTR(f32x4))(wlds + (ct * 64 + lane) * 16) = o[ct];
     lds_barrier();
+    // All 32 parked fragments this wave merges are read before any is used.
+    f32x4 part[4][8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        part[w][k] = *(LDS_PTR(f32x4))((LDS_PTR(unsigned char))smem + w * 2 * kStageBytes +
+                                       ((8 * wave + k) * 64 + lane) * 16);
     float wgt[4], inv, lse2;
     merge_weights(st_m, st_l, c16, wgt, inv, lse2);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int ct = 8 * wave + k;
       f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
-        acc += wgt[w] * *(LDS_PTR(f32x4))((LDS_PTR(unsigned char))smem + w * 2 * kStageBytes + (ct * 64 + lane) * 16);
+      for (int w = 0; w < 4; ++w) acc += wgt[w] * part[w][k];
       if (row_ok) store_cols4(p, req, c16, split, slot, 16 * ct + 4 * g, acc * inv);   // 4 consecutive columns
     }
     if (wave == 0 && g == 0 && row_ok) store_lse(p, req, c16, split, slot, lse2);
@@ -545,7 +561,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_kernel(Params p) {
     float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
     bool have_ref = false;
     for (int attempt = 0;; ++attempt) {
-      if (lo < hi) issue_stage(rows_of(lo), wlds0, dma_off);
+      if (lo < hi) issue_stage<false>(rows_of(lo), wlds0, dma_off);
       bf16x8 qf[2][kQkSteps];
       load_q(qf[0], p, req, row0 + c16, g);
       load_q(qf[1], p, req, row0 + 16 + c16, g);
@@ -595,7 +611,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_kernel(Params p) {
             for (int t = 0; t < 2; ++t)
               sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % kQkLead], qf[t][ks], sacc[t], 0, 0, 0);
             if (ks + kQkLead < kQkSteps) kf[ks % kQkLead] = kread(ks + kQkLead);
-            issue_stage_slice(nrows, nlds, dma_off, ks);
+            issue_stage_slice<false>(nrows, nlds, dma_off, ks);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -690,6 +706,272 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_kernel(Params p) {
       lds_barrier();   // the parked tiles are read; the stages may be reused
     }
     if (wave == 0 && lane < 32 && row < p.R) store_lse(p, req, row, split, slot, lse2);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wide row groups (R >= 128): one workgroup per (part, group of 128 query
+// rows), so each KV page enters a CU once per 128 rows instead of once per
+// 32 (the per-CU path from L2 is the narrower resource for the 32-row kernel)
+// and two LDS stages cover two full page times of copy latency.
+//   * Each wave still copies its own 16 token rows of a page (the 18 KiB
+//     slice layout above), but both stages are shared: a barrier after the
+//     copies land makes every slice visible to every wave.
+//   * QK^T is split by rows: wave w computes S^T (64 tokens x 32 rows
+//     32 w .. 32 w + 31) with v_mfma_f32_32x32x16_bf16, Q in registers, K
+//     fragments from the four slices.  Each wave owns the softmax state of its
+//     32 rows (so no cross-wave merge is needed at the end).
+//   * Its bf16 probabilities go to LDS straight from the S^T accumulator as
+//     PV B fragments (the token order inside a 16-token step is the
+//     accumulator's; the V^T reads use the same order).
+//   * PV is split by columns: wave w accumulates O^T for columns
+//     128 w .. 128 w + 127 of all 128 rows (4 x 4 tiles of 32x32, 256
+//     registers); every V^T fragment feeds four MFMAs.
+//   * Two barriers per page: after the P fragments are written, and after PV
+//     (P buffer and the page's stage free; the next page's slices landed).
+constexpr int kWideTiles = kWideRows / 32;                 // 32-row tiles per group (= waves)
+constexpr int kPFragBytes = kWideTiles * 4 * 64 * 16;      // P^T: 4 row tiles x 4 token steps x 64 lanes x 16 B
+constexpr int kQkSteps16 = kDqk / 16;                      // 36 k-steps of the 32x32x16 MFMA
+constexpr int kWideQkLead = 6;                             // K fragment reads in flight
+constexpr float kRestartFlag = -0.0f;                      // sign bit carried by a P element
+
+template <bool kStream>
+__global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
+  // Two page stages (4 slices of 18 KiB each) and the P^T exchange buffer: 160 KiB.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kPageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char pbuf[kPFragBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int part, rg;
+  map_block(p, part, rg);
+  if (part >= p.num_parts) return;
+  const PieceRange pr = load_part(p, part);
+
+  const int h = lane >> 5;     // which half of the 32x32 MFMA k slots
+  const int n = lane & 31;     // 32x32 MFMA column = query row within a tile
+  const int row0 = rg * kWideRows;
+  const int r = row0 + 32 * wave + n;   // the row this lane owns in QK^T / softmax
+  const bool row_ok = r < p.R;
+  const int tok0 = kWaveTokens * wave;
+
+  LDS_PTR(unsigned char) lds = (LDS_PTR(unsigned char))smem;
+  LDS_PTR(unsigned char) pb = (LDS_PTR(unsigned char))pbuf;
+  const unsigned lds0 = (unsigned)(size_t)lds;
+  const unsigned dma_off[2] = {stage_dma_offset(lane, 0), stage_dma_offset(lane, 1)};
+
+  // QK A fragment (32x32x16) of token tile tt, k-step ks: token m = 32 tt + n
+  // = slice 2 tt + n / 16, local row n % 16; dims 16 ks + 8 h .. + 7 =
+  // block ks / 4, in-block chunk 2 (ks % 4) + h.
+  int kq[2][4];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t = n & 15;
+      kq[tt][q] = (2 * tt + (n >> 4)) * kStageBytes + t * 128 + (((2 * q + h) ^ stage_swizzle(t)) << 4);
+    }
+  // PV A fragment (V^T, 32 columns x 16 tokens of slice kk) in the token order
+  // of the S^T accumulator: lane (group G, index Lq) reads token
+  // 4 (G / 2) + Lq / 4 (read 0) or that + 8 (read 1) at columns
+  // 32 ct + 16 (G % 2) + 4 (Lq % 4) .. + 3.
+  const int G = lane >> 4, Lq = lane & 15;
+  int pv[2][2];
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int t = 4 * (G >> 1) + (Lq >> 2) + 8 * rd;
+      pv[rd][par] = t * 128 + (((4 * par + 2 * (G & 1) + ((Lq & 3) >> 1)) ^ stage_swizzle(t)) << 4) + 8 * (Lq & 1);
+    }
+
+  for (int req = pr.begin_req; req <= pr.end_req; ++req) {
+    const int L = ld_uniform(p.seqlens + req);
+    const int nblk = (L + kPage - 1) / kPage;
+    const int lo = (req == pr.begin_req) ? pr.begin_blk : 0;
+    const int hi = (req == pr.end_req) ? pr.end_blk : nblk;
+    const int slot0 = ld_uniform(p.num_splits + req);
+    const int slot = slot0 + ((req == pr.begin_req) ? pr.begin_piece : 0);
+    const bool split = (ld_uniform(p.num_splits + req + 1) - slot0) > 1;
+    const int32_t* bt = p.block_table + (size_t)req * p.max_blocks;
+    auto rows_of = [&](int j) {
+      return uniform_ptr(p.kv + (size_t)ld_uniform(bt + j) * kPageBytes + (size_t)tok0 * kRowBytes);
+    };
+
+    f32x16 o[kWideTiles][4];   // O^T tiles: row tile x this wave's 4 column tiles
+    float m_ref = -INFINITY, l_run = 0.f;
+    bool have_ref = false;
+    for (int attempt = 0;; ++attempt) {
+      if (lo < hi) issue_stage<kStream>(rows_of(lo), lds0 + wave * kStageBytes, dma_off);
+      // Q^T fragments (B operand): row r, dims 16 ks + 8 h .. + 7.
+      bf16x8 qf[kQkSteps16];
+      {
+        const unsigned char* qrow = p.q + ((size_t)req * p.R + (row_ok ? r : 0)) * kRowBytes + h * 16;
+        const unsigned keep = row_ok ? ~0u : 0u;
+#pragma unroll
+        for (int ks = 0; ks < kQkSteps16; ++ks) {
+          u32x4 v = *(const u32x4*)(qrow + ks * 32);
+          v &= keep;
+          qf[ks] = __builtin_bit_cast(bf16x8, v);
+        }
+      }
+      // Q and the first page (a wait the compiler sees, so it inserts none
+      // inside the page loop, whose waits cover only the copies it issues).
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+#pragma unroll
+      for (int a = 0; a < kWideTiles; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o[a][c] = f32x16{};
+      float m_seen = -INFINITY;
+      l_run = 0.f;
+      bool restart = false;
+      int next_blk = ld_uniform(bt + (lo + 1 < hi ? lo + 1 : lo));
+
+      for (int j = lo; j < hi; ++j) {
+        const int stage = (j - lo) & 1;
+        LDS_PTR(unsigned char) buf = lds + stage * kPageBytes;
+        // Page j: this wave's slice has landed; zero its rows past the end of
+        // the sequence, then the barrier makes all four slices visible (and
+        // every wave is past the previous page's PV: P buffer and the other
+        // stage are free).
+        wait_vmcnt<0>();
+        const int valid = min(kPage, L - j * kPage);
+        if (valid < kPage) zero_stage_tail(buf + wave * kStageBytes, valid - tok0, lane);
+        lds_barrier();
+        // The next page's 18 slices go to the other stage during QK^T (on the
+        // last page, the current page is copied again: harmless, keeps the
+        // loop free of branches).
+        const unsigned char* nrows =
+            uniform_ptr(p.kv + (size_t)next_blk * kPageBytes + (size_t)tok0 * kRowBytes);
+        next_blk = ld_uniform(bt + (j + 2 < hi ? j + 2 : j));
+        const unsigned nlds = lds0 + (stage ^ 1) * kPageBytes + wave * kStageBytes;
+
+        // ---- S^T (64 tokens x this wave's 32 rows), token tile by token tile;
+        // each tile's probabilities become two PV B fragments in LDS.
+        bool bad = false;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          f32x16 sacc = f32x16{};
+          {
+            auto kread = [&](int ks) {
+              return __builtin_bit_cast(bf16x8,
+                                        *(LDS_PTR(u32x4))(buf + (ks >> 2) * kStageBlock + kq[tt][ks & 3]));
+            };
+            bf16x8 kf[kWideQkLead];
+#pragma unroll
+            for (int i = 0; i < kWideQkLead; ++i) kf[i] = kread(i);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < kQkSteps16; ++ks) {
+              sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks % kWideQkLead], qf[ks], sacc, 0, 0, 0);
+              if (ks + kWideQkLead < kQkSteps16) kf[ks % kWideQkLead] = kread(ks + kWideQkLead);
+              if (ks % 4 == 0) issue_stage_slice<kStream>(nrows, nlds, dma_off, 9 * tt + ks / 4);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          // Lane holds row n, tokens 32 tt + 8 i + 4 h + e in element 4 i + e.
+          float mloc = -INFINITY;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int tok = 32 * tt + 8 * (v >> 2) + 4 * h + (v & 3);
+            mloc = fmaxf(mloc, tok < valid ? sacc[v] : -INFINITY);
+          }
+          mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * p.scale_log2;
+          if (!have_ref) m_ref = mloc;   // first token tile of the first page of the first attempt
+          have_ref = true;
+          m_seen = fmaxf(m_seen, mloc);
+          bad |= mloc > m_ref + kRefHeadroom;
+          const bool flag = tt == 1 && attempt == 0 && __any(bad);   // wave-wide vote, outside any branch
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            bf16x8 pk;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int v = 8 * half + e;
+              const int tok = 32 * tt + 8 * (v >> 2) + 4 * h + (v & 3);
+              float pe = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], p.scale_log2, -m_ref));
+              if (tok >= valid) pe = 0.f;
+              l_run += pe;
+              pk[e] = (__bf16)pe;
+            }
+        const int kk = 2 * tt + half;
+            if (kk == 3 && lane == 0 && flag) pk[0] = (__bf16)kRestartFlag;
+            *(LDS_PTR(bf16x8))(pb + ((wave * 4 + kk) * 64 + lane) * 16) = pk;
+          }
+        }
+        lds_barrier();   // every wave's P fragments are in LDS
+
+        // A wave whose row max outgrew its reference by more than 2^64 set the
+        // sign of one probability: every wave then redoes the piece with the
+        // largest maxima seen as references (once; exact maxima bound every
+        // probability by 1).  The attempt runs to its end first (its results
+        // are discarded), which keeps a single exit from the page loop.
+#pragma unroll
+        for (int w = 0; w < kWideTiles; ++w)
+          restart |= (*(LDS_PTR(unsigned short))(pb + (w * 4 + 3) * 64 * 16) >> 15) != 0;
+
+        // ---- O^T (this wave's 128 columns x 128 rows) += V^T P^T.
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          bf16x8 pf[kWideTiles];
+#pragma unroll
+          for (int a = 0; a < kWideTiles; ++a)
+            pf[a] = *(LDS_PTR(bf16x8))(pb + ((a * 4 + kk) * 64 + lane) * 16);
+          LDS_PTR(unsigned char) vs = buf + kk * kStageBytes;
+          auto vread = [&](int c) {
+            const int ct = 4 * wave + c;
+            LDS_PTR(unsigned char) a = vs + (ct >> 1) * kStageBlock;
+            const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv[0][ct & 1]));
+            const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv[1][ct & 1]));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+          };
+          bf16x8 vf[2];
+          vf[0] = vread(0);
+          vf[1] = vread(1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+#pragma unroll
+            for (int a = 0; a < kWideTiles; ++a)
+              o[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[c & 1], pf[a], o[a][c], 0, 0, 0);
+            if (c + 2 < 4) vf[c & 1] = vread(c + 2);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      wait_vmcnt<0>();   // the last page's (repeated) copy
+      if (!restart) break;
+      lds_barrier();     // every wave is past the last page before the stages are refilled
+      m_ref = m_seen;
+    }
+
+    // ---- epilogue: each wave owns rows 32 w + n for l and lse; publish 1 / l
+    // so that every wave can normalise its columns of all 128 rows.
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse2 = l_tot > 0.f ? m_ref + __builtin_amdgcn_logf(l_tot) : -INFINITY;
+    lds_barrier();   // every wave is done with the P buffer
+    if (h == 0) *(LDS_PTR(float))(pb + (wave * 32 + n) * 4) = inv;
+    lds_barrier();
+    float inv_rows[kWideTiles];
+#pragma unroll
+    for (int a = 0; a < kWideTiles; ++a) inv_rows[a] = *(LDS_PTR(float))(pb + (a * 32 + n) * 4);
+#pragma unroll
+    for (int a = 0; a < kWideTiles; ++a) {
+      const int ra = row0 + 32 * a + n;
+      if (ra >= p.R) continue;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int ct = 4 * wave + c;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          store_cols4(p, req, ra, split, slot, 32 * ct + 8 * i + 4 * h,
+                      f32x4{o[a][c][4 * i], o[a][c][4 * i + 1], o[a][c][4 * i + 2], o[a][c][4 * i + 3]} *
+                          inv_rows[a]);
+      }
+    }
+    if (h == 0 && row_ok) store_lse(p, req, r, split, slot, lse2);
+    lds_barrier();   // the 1 / l table is read; the next piece may reuse the buffers
   }
 }
 
@@ -962,6 +1244,11 @@ extern "C" int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t
   if (g.R <= kSmallRows) {
     main_fn = (const void*)mla_splitkv_small_kernel;
     grid = num_parts;
+  } else if (g.R >= kWideRows) {
+    // Row groups of one part share pages through L2 (cached copies); a single
+    // group streams every page once (nontemporal copies).
+    main_fn = g.row_groups == 1 ? (const void*)mla_splitkv_wide_kernel<true> : (const void*)mla_splitkv_wide_kernel<false>;
+    grid = g.row_groups == 1 ? num_parts : 8 * g.row_groups * ((num_parts + 7) / 8);
   } else {
     main_fn = (const void*)mla_splitkv_kernel;
     grid = g.row_groups == 1 ? num_parts : 8 * g.row_groups * ((num_parts + 7) / 8);

@@ -12,6 +12,7 @@ constexpr int kDqk = 576;       // 512 latent + 64 RoPE dims (QK^T)
 constexpr int kDv = 512;        // latent dims (PV)
 constexpr int kSmallRows = 16;  // up to this many query rows: one workgroup covers them all
 constexpr int kRowGroup = 32;   // query rows per workgroup above that
+constexpr int kWideRows = 128;  // from this many rows on: workgroups of 128 rows
 
 // Records `code` and a printf-style message as this thread's last error; returns `code`.
 int set_error(int code, const char* fmt, ...);
@@ -22,13 +23,15 @@ int plan(const int32_t* seqlens, int batch, int num_parts, int fixed_overhead, i
 // Launch geometry shared by the planner policy and the kernels.
 struct Geometry {
   int R;           // query rows per request = s_q * h_q
-  int row_groups;  // workgroups per part: 1 for R <= 16, else ceil(R / 32)
+  int row_groups;  // workgroups per part: 1 for R <= 16, ceil(R / 128) for R >= 128, else ceil(R / 32)
 };
 
 inline Geometry geometry(int h_q, int s_q) {
   Geometry g;
   g.R = h_q * s_q;
-  g.row_groups = g.R <= kSmallRows ? 1 : (g.R + kRowGroup - 1) / kRowGroup;
+  g.row_groups = g.R <= kSmallRows ? 1
+                 : g.R >= kWideRows ? (g.R + kWideRows - 1) / kWideRows
+                                    : (g.R + kRowGroup - 1) / kRowGroup;
   return g;
 }
 

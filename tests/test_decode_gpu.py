@@ -92,16 +92,23 @@ def test_nan_in_page_tails_and_unused_pages():
         assert_parity(out, lse, ref_out, ref_lse, f"NaN tails force={force}", out_tol=out_tol_bound(inp))
 
 
-def test_restart_when_later_page_outgrows_first_max():
+@pytest.mark.parametrize("h_q", [16, 32, 128, 160])
+def test_restart_when_later_page_outgrows_first_max(h_q):
     # First page scores ~0, a later page ~ +150 (far beyond the 2^64 headroom):
-    # the kernel must take its restart path and still match.
+    # the kernel must take its restart path and still match.  At 128 and more
+    # heads only rows 32 .. 63 outgrow their maxima (one wave of a 128-row
+    # group votes for the restart of all four).
     rng = np.random.default_rng(3)
     L = 64 * 5 + 7
     keys = (0.01 * rng.standard_normal((L, W.D_QK))).astype(np.float32)
     keys[64 * 3 + 5, :] = 0.5          # one token with a huge score
     keys[64 * 4 + 1, :] = -0.5
-    q = np.abs(rng.standard_normal((1, 1, 32, W.D_QK))).astype(np.float32)
-    inp = W.make_inputs(1, 1, 32, [L], pool=8, max_blocks=6, seed=5)
+    q = np.abs(rng.standard_normal((1, 1, h_q, W.D_QK))).astype(np.float32)
+    if h_q >= 128:
+        keep = np.zeros(h_q, dtype=bool)
+        keep[32:64] = True
+        q[0, 0, ~keep] *= 1e-3
+    inp = W.make_inputs(1, 1, h_q, [L], pool=8, max_blocks=6, seed=5)
     kv = inp.kv_cache.copy()
     for t in range(L):
         kv[inp.block_table[0, t // 64], t % 64, 0] = W.f32_to_bf16_bits(keys[t])

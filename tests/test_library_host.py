@@ -61,7 +61,7 @@ def test_get_metadata_policy_matches_reference_plan(h_q, s_q):
     sl = np.array([100, 257, 4096, 0, 70000, 1], dtype=np.int32)
     sched, ns, total = mla.get_mla_metadata_host(sl, h_q, s_q, num_cus=256)
     R = h_q * s_q
-    groups = 1 if R <= 16 else -(-R // 32)
+    groups = 1 if R <= 16 else -(-R // 128) if R >= 128 else -(-R // 32)
     parts = max(1, 256 // groups)
     F = 3 if R <= 16 else 2
     s_ref, n_ref = oracle.plan(sl, num_parts=parts, fixed_overhead=F)
