@@ -73,6 +73,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 #define LDS_PTR(T) __attribute__((address_space(3))) T*
 
 constexpr int kRowBytes = kDqk * 2;                // 1152
@@ -732,8 +733,46 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_kernel(Params p) {
 constexpr int kWideTiles = kWideRows / 32;                 // 32-row tiles per group (= waves)
 constexpr int kPFragBytes = kWideTiles * 4 * 64 * 16;      // P^T: 4 row tiles x 4 token steps x 64 lanes x 16 B
 constexpr int kQkSteps16 = kDqk / 16;                      // 36 k-steps of the 32x32x16 MFMA
-constexpr int kWideQkLead = 6;                             // K fragment reads in flight
+constexpr int kWideQkLead = 4;                             // K fragment reads in flight
 constexpr float kRestartFlag = -0.0f;                      // sign bit carried by a P element
+constexpr int kWideSoftmaxPieces = 12;                     // pieces of one tile's softmax
+
+// Softmax state of one 32-token S^T tile.  Lane l holds row l % 32 and, in
+// element 4 i + e, token 8 i + 4 (l / 32) + e of the tile.  The pieces:
+//   0      max of this lane's 16 scores
+//   1      row max over both lane halves, scaled; the first tile sets the
+//          reference; running max and the restart test
+//   2 .. 5, 7 .. 10   two probabilities exp2(scale s - reference) each: row
+//          sum, bf16 pairs
+//   6, 11  the two 8-token halves go to LDS as PV B fragments
+struct WideSoftmax {
+  float mloc;
+  u32x4 pk[2];
+};
+
+// O^T += V^T P^T on the matrix cores with the accumulator pinned to AGPRs:
+// O (256 registers per lane) stays in the accumulation registers for the
+// whole piece, which leaves the architectural VGPRs to Q, the S^T tiles and
+// the softmax.  The compiler does not see inside the statement, so the code
+// around it keeps the hazard distances itself: operands come from LDS reads
+// (waited for by the compiler's counters) and reads of the accumulator are
+// preceded by wide_acc_settle().
+__device__ __forceinline__ void pv_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// S^T tiles in architectural VGPRs (so they never compete with O for the
+// accumulation registers); the first step of a tile starts from zero.
+__device__ __forceinline__ void qk_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b, bool first) {
+  if (first)
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+  else
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+// Wait states between the last matrix op writing the accumulators and any
+// other access to them (a 16-pass MFMA result needs 18).
+__device__ __forceinline__ void wide_acc_settle() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
 
 template <bool kStream>
 __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
@@ -763,14 +802,12 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
   // QK A fragment (32x32x16) of token tile tt, k-step ks: token m = 32 tt + n
   // = slice 2 tt + n / 16, local row n % 16; dims 16 ks + 8 h .. + 7 =
   // block ks / 4, in-block chunk 2 (ks % 4) + h.
-  int kq[2][4];
+  int kq[4];   // tile 0; tile 1 is 2 slices further
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int t = n & 15;
-      kq[tt][q] = (2 * tt + (n >> 4)) * kStageBytes + t * 128 + (((2 * q + h) ^ stage_swizzle(t)) << 4);
-    }
+  for (int q = 0; q < 4; ++q) {
+    const int t = n & 15;
+    kq[q] = (n >> 4) * kStageBytes + t * 128 + (((2 * q + h) ^ stage_swizzle(t)) << 4);
+  }
   // PV A fragment (V^T, 32 columns x 16 tokens of slice kk) in the token order
   // of the S^T accumulator: lane (group G, index Lq) reads token
   // 4 (G / 2) + Lq / 4 (read 0) or that + 8 (read 1) at columns
@@ -846,100 +883,144 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
         next_blk = ld_uniform(bt + (j + 2 < hi ? j + 2 : j));
         const unsigned nlds = lds0 + (stage ^ 1) * kPageBytes + wave * kStageBytes;
 
-        // ---- S^T (64 tokens x this wave's 32 rows), token tile by token tile;
-        // each tile's probabilities become two PV B fragments in LDS.
-        bool bad = false;
+        // ---- S^T (64 tokens x this wave's 32 rows) in two 32-token tiles.
+        // The softmax of each tile rides along the next MFMA stream (tile 0
+        // with QK^T of tile 1, tile 1 with PV of tokens 0 .. 31), so its VALU
+        // work and exp2 latency hide under the matrix cores.
+        bool bad = false, flag = false;
+        WideSoftmax sm[2];
+        const int lim = valid - 4 * h;   // element v of a tile is a real token iff its offset is below this
+        // One piece of tile tt's softmax (see WideSoftmax); k is a constant
+        // after unrolling.  The scores are read from the accumulator as they
+        // are needed; tokens past the end of the sequence (last page only)
+        // are masked in both passes.
+        auto softmax_piece = [&](int tt, int k, const f32x16& sacc) {
+          WideSoftmax& t = sm[tt];
+          const bool ragged = valid < 32 * tt + 32;   // uniform
+          auto ok = [&](int v) { return 32 * tt + 8 * (v >> 2) + (v & 3) < lim; };
+          if (k == 0) {
+            auto max16 = [](const float* x) {
+              const float m0 = fmaxf(fmaxf(x[0], x[1]), x[2]), m1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
+              const float m2 = fmaxf(fmaxf(x[6], x[7]), x[8]), m3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
+              const float m4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
+              return fmaxf(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)), fmaxf(m4, x[15]));
+            };
+            float x[16];
+            if (ragged) {
+#pragma unroll
+              for (int v = 0; v < 16; ++v) x[v] = ok(v) ? sacc[v] : -INFINITY;
+              t.mloc = max16(x);
+            } else {
+#pragma unroll
+              for (int v = 0; v < 16; ++v) x[v] = sacc[v];
+              t.mloc = max16(x);
+            }
+          } else if (k == 1) {
+            // The other half of the row's tokens sits in lane l ^ 32
+            // (softmax_scale >= 0: the max commutes with the scaling).
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t.mloc), __float_as_uint(t.mloc), false, false);
+            const float mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2;
+            if (!have_ref) m_ref = mloc;   // first tile of the first page of the first attempt
+            have_ref = true;
+            m_seen = fmaxf(m_seen, mloc);
+            bad |= mloc > m_ref + kRefHeadroom;
+            if (tt == 1) flag = attempt == 0 && __any(bad);   // wave-wide vote, outside any branch
+          } else if (k == 6 || k == 11) {
+            const int half = k == 6 ? 0 : 1;
+            u32x4 w = t.pk[half];
+            if (tt == 1 && half == 1 && lane == 0 && flag) w[0] |= 0x8000u;   // kRestartFlag in element 0
+            *(LDS_PTR(u32x4))(pb + ((wave * 4 + 2 * tt + half) * 64 + lane) * 16) = w;
+          } else {
+            const int half = k < 6 ? 0 : 1, e = k < 6 ? k - 2 : k - 7;   // elements 8 half + 2 e, + 1
+            const int v = 8 * half + 2 * e;
+            float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], p.scale_log2, -m_ref));
+            float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v + 1], p.scale_log2, -m_ref));
+            if (ragged) {
+              p0 = ok(v) ? p0 : 0.f;
+              p1 = ok(v + 1) ? p1 : 0.f;
+            }
+            l_run += p0 + p1;
+            t.pk[half][e] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)p0, (__bf16)p1});
+          }
+        };
+
+        f32x16 sacc[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          f32x16 sacc = f32x16{};
-          {
-            auto kread = [&](int ks) {
-              return __builtin_bit_cast(bf16x8,
-                                        *(LDS_PTR(u32x4))(buf + (ks >> 2) * kStageBlock + kq[tt][ks & 3]));
-            };
-            bf16x8 kf[kWideQkLead];
+          auto kread = [&](int ks) {
+            return __builtin_bit_cast(bf16x8,
+                                      *(LDS_PTR(u32x4))(buf + 2 * tt * kStageBytes + (ks >> 2) * kStageBlock + kq[ks & 3]));
+          };
+          bf16x8 kf[kWideQkLead];
 #pragma unroll
-            for (int i = 0; i < kWideQkLead; ++i) kf[i] = kread(i);
+          for (int i = 0; i < kWideQkLead; ++i) kf[i] = kread(i);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ks = 0; ks < kQkSteps16; ++ks) {
+            qk_mfma(sacc[tt], kf[ks % kWideQkLead], qf[ks], ks == 0);
+            if (ks + kWideQkLead < kQkSteps16) kf[ks % kWideQkLead] = kread(ks + kWideQkLead);
+            if (ks % 4 == 0) issue_stage_slice<kStream>(nrows, nlds, dma_off, 9 * tt + ks / 4);
+            // Tile 0's softmax: one piece every other step from step 1.
+            if (tt == 1 && ks == 1) wide_acc_settle();
+            if (tt == 1 && ks % 2 == 1 && ks / 2 < kWideSoftmaxPieces) softmax_piece(0, ks / 2, sacc[0]);
             __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        lds_barrier();   // every wave's tile-0 probabilities are in LDS
+        wide_acc_settle();   // tile 1's scores are read next
+
+        // ---- O^T (this wave's 128 columns x 128 rows) += V^T P^T, one
+        // 16-token step kk at a time; tile 1's softmax runs along kk = 0, 1.
+        // Two 16-token steps kk0, kk0 + 1 (8 groups of four MFMAs, one per
+        // row tile a, sharing a V^T fragment); the V^T fragments are read two
+        // groups ahead, each P^T fragment of the second step as soon as the
+        // last MFMA of the first step that uses its register is issued, and
+        // the softmax pieces (if any) sit between single MFMAs.
+        auto pv_block = [&](int kk0, bool with_softmax) {
+          auto vread = [&](int s) {
+            const int ct = 4 * wave + (s & 3);
+            LDS_PTR(unsigned char) a = buf + (kk0 + (s >> 2)) * kStageBytes + (ct >> 1) * kStageBlock;
+            const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv[0][ct & 1]));
+            const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv[1][ct & 1]));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+          };
+          bf16x8 pf[kWideTiles], vf[2];
+          auto pread = [&](int i, int a) { pf[a] = *(LDS_PTR(bf16x8))(pb + ((a * 4 + kk0 + i) * 64 + lane) * 16); };
 #pragma unroll
-            for (int ks = 0; ks < kQkSteps16; ++ks) {
-              sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks % kWideQkLead], qf[ks], sacc, 0, 0, 0);
-              if (ks + kWideQkLead < kQkSteps16) kf[ks % kWideQkLead] = kread(ks + kWideQkLead);
-              if (ks % 4 == 0) issue_stage_slice<kStream>(nrows, nlds, dma_off, 9 * tt + ks / 4);
+          for (int a = 0; a < kWideTiles; ++a) pread(0, a);
+          vf[0] = vread(0);
+          vf[1] = vread(1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+#pragma unroll
+            for (int a = 0; a < kWideTiles; ++a) {
+              const int m = 4 * s + a;
+              pv_mfma(o[a][s & 3], vf[s & 1], pf[a]);
+              if (s == 3) pread(1, a);
+              if (a == kWideTiles - 1 && s + 2 < 8) vf[s & 1] = vread(s + 2);
+              if (with_softmax && (m & 1) && (m >> 1) < kWideSoftmaxPieces) softmax_piece(1, m >> 1, sacc[1]);
               __builtin_amdgcn_sched_barrier(0);
             }
           }
-          // Lane holds row n, tokens 32 tt + 8 i + 4 h + e in element 4 i + e.
-          float mloc = -INFINITY;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int tok = 32 * tt + 8 * (v >> 2) + 4 * h + (v & 3);
-            mloc = fmaxf(mloc, tok < valid ? sacc[v] : -INFINITY);
-          }
-          mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * p.scale_log2;
-          if (!have_ref) m_ref = mloc;   // first token tile of the first page of the first attempt
-          have_ref = true;
-          m_seen = fmaxf(m_seen, mloc);
-          bad |= mloc > m_ref + kRefHeadroom;
-          const bool flag = tt == 1 && attempt == 0 && __any(bad);   // wave-wide vote, outside any branch
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            bf16x8 pk;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int v = 8 * half + e;
-              const int tok = 32 * tt + 8 * (v >> 2) + 4 * h + (v & 3);
-              float pe = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], p.scale_log2, -m_ref));
-              if (tok >= valid) pe = 0.f;
-              l_run += pe;
-              pk[e] = (__bf16)pe;
-            }
-        const int kk = 2 * tt + half;
-            if (kk == 3 && lane == 0 && flag) pk[0] = (__bf16)kRestartFlag;
-            *(LDS_PTR(bf16x8))(pb + ((wave * 4 + kk) * 64 + lane) * 16) = pk;
-          }
-        }
-        lds_barrier();   // every wave's P fragments are in LDS
+        };
+        pv_block(0, true);
+        lds_barrier();   // every wave's tile-1 probabilities (and restart vote) are in LDS
 
         // A wave whose row max outgrew its reference by more than 2^64 set the
         // sign of one probability: every wave then redoes the piece with the
         // largest maxima seen as references (once; exact maxima bound every
         // probability by 1).  The attempt runs to its end first (its results
-        // are discarded), which keeps a single exit from the page loop.
+        // are discarded), which keeps a single exit from the page loop.  Only
+        // the first attempt may ask for a restart (whatever the data, even
+        // NaN, the piece is processed at most twice).
 #pragma unroll
         for (int w = 0; w < kWideTiles; ++w)
-          restart |= (*(LDS_PTR(unsigned short))(pb + (w * 4 + 3) * 64 * 16) >> 15) != 0;
-
-        // ---- O^T (this wave's 128 columns x 128 rows) += V^T P^T.
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          bf16x8 pf[kWideTiles];
-#pragma unroll
-          for (int a = 0; a < kWideTiles; ++a)
-            pf[a] = *(LDS_PTR(bf16x8))(pb + ((a * 4 + kk) * 64 + lane) * 16);
-          LDS_PTR(unsigned char) vs = buf + kk * kStageBytes;
-          auto vread = [&](int c) {
-            const int ct = 4 * wave + c;
-            LDS_PTR(unsigned char) a = vs + (ct >> 1) * kStageBlock;
-            const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv[0][ct & 1]));
-            const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv[1][ct & 1]));
-            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-          };
-          bf16x8 vf[2];
-          vf[0] = vread(0);
-          vf[1] = vread(1);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-#pragma unroll
-            for (int a = 0; a < kWideTiles; ++a)
-              o[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[c & 1], pf[a], o[a][c], 0, 0, 0);
-            if (c + 2 < 4) vf[c & 1] = vread(c + 2);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
+          restart |= attempt == 0 && (*(LDS_PTR(unsigned short))(pb + (w * 4 + 3) * 64 * 16) >> 15) != 0;
+        pv_block(2, false);
       }
       wait_vmcnt<0>();   // the last page's (repeated) copy
+      wide_acc_settle();
       if (!restart) break;
       lds_barrier();     // every wave is past the last page before the stages are refilled
       m_ref = m_seen;
