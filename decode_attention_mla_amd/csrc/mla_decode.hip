@@ -1060,59 +1060,105 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
 // Merge the partial (O_i, lse_i) of every split request (the log-sum-exp
 // merge of the attention-kernel page and the overview page, section 7):
 // M = max lse_i, w_i = 2^(lse_i - M), out = sum w_i O_i / sum w_i,
-// lse = M + log2(sum w_i) (then converted to natural log).  Workgroups stride
-// over (request, row) pairs; rows of requests that are not split are skipped
-// (the main kernel wrote them).  The four waves take every fourth split, each
-// lane 8 consecutive columns (two 16-byte loads per split, all of a wave's
-// loads in flight together), merge online in registers and are combined
-// through LDS.
+// lse = M + log2(sum w_i) (then converted to natural log).  Rows of requests
+// that are not split are skipped (the main kernel wrote them).
+//   Each lane owns 8 consecutive columns and issues the loads of
+// kCombineChunk splits at once (two 16-byte loads each), so a wave pays one
+// memory round trip per chunk.  If no request has more than kCombineChunk
+// pieces (the schedule table says), each wave merges one (request, row) pair
+// on its own (many short merges: no LDS, no barrier); otherwise a workgroup
+// merges one pair, wave w taking splits w, w + 4, ..., and the four states
+// meet in LDS (few long merges).
 constexpr int kCombineWaves = 4;
-constexpr int kCombineUnroll = 4;   // splits per wave whose loads are issued together
+constexpr int kCombineChunk = 8;
 
-__device__ __forceinline__ void lse_merge(float& M, float& l, f32x4& a0, f32x4& a1, float li, f32x4 b0, f32x4 b1,
-                                          float wl) {
-  // Adds a state (li = log2 weight, b = its normalised output, wl = its mass)
-  // to the running (M, l, a): everything is kept relative to the running max.
-  if (!(wl > 0.f)) return;
-  const float Mn = fmaxf(M, li);
-  const float sa = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-  const float sb = __builtin_amdgcn_exp2f(li - Mn) * wl;
-  a0 = a0 * sa + b0 * sb;
-  a1 = a1 * sa + b1 * sb;
-  l = l * sa + sb;
-  M = Mn;
+// Online merge of splits first, first + step, ... (count of them) of one
+// pair into (M, l, a0, a1).
+__device__ __forceinline__ void combine_splits(const float* lrow, const float* orow, size_t lstride, size_t ostride,
+                                               int first, int step, int count, float& M, float& l, f32x4& a0,
+                                               f32x4& a1) {
+  for (int k0 = 0; k0 < count; k0 += kCombineChunk) {
+    float li[kCombineChunk];
+    f32x4 b0[kCombineChunk], b1[kCombineChunk];
+#pragma unroll
+    for (int u = 0; u < kCombineChunk; ++u) {
+      const int i = first + step * min(k0 + u, count - 1);   // clamped: duplicates get weight 0 below
+      li[u] = ld_uniform(lrow + (size_t)i * lstride);
+      b0[u] = *(const f32x4*)(orow + (size_t)i * ostride);
+      b1[u] = *(const f32x4*)(orow + (size_t)i * ostride + 4);
+    }
+    float Mc = M;
+#pragma unroll
+    for (int u = 0; u < kCombineChunk; ++u)
+      if (k0 + u < count) Mc = fmaxf(Mc, li[u]);
+    if (Mc == -INFINITY) continue;   // nothing with mass so far (uniform)
+    const float sa = __builtin_amdgcn_exp2f(M - Mc);   // M = -inf gives 0
+    a0 *= sa;
+    a1 *= sa;
+    l *= sa;
+#pragma unroll
+    for (int u = 0; u < kCombineChunk; ++u) {
+      const float w = (k0 + u < count) ? __builtin_amdgcn_exp2f(li[u] - Mc) : 0.f;   // lse = -inf gives 0
+      a0 += w * b0[u];
+      a1 += w * b1[u];
+      l += w;
+    }
+    M = Mc;
+  }
+}
+
+__device__ __forceinline__ void combine_store(const Params& p, int req, int row, int lane, float M, float l, f32x4 a0,
+                                              f32x4 a1) {
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  unsigned short* o = p.out + ((size_t)req * p.R + row) * kDv + lane * 8;
+  u32x4 w;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    w[e] = (unsigned)f32_to_bf16(a0[2 * e] * inv) | ((unsigned)f32_to_bf16(a0[2 * e + 1] * inv) << 16);
+    w[2 + e] = (unsigned)f32_to_bf16(a1[2 * e] * inv) | ((unsigned)f32_to_bf16(a1[2 * e + 1] * inv) << 16);
+  }
+  *(u32x4*)o = w;
+  if (lane == 0) {
+    const int sq = row / p.h_q, hh = row - sq * p.h_q;
+    p.lse[((size_t)req * p.h_q + hh) * p.s_q + sq] = l > 0.f ? (M + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+  }
 }
 
 __global__ void __launch_bounds__(kCombineWaves * 64) mla_combine_kernel(Params p) {
   __shared__ f32x4 red_o[kCombineWaves][2][64];
   __shared__ float red_m[kCombineWaves], red_l[kCombineWaves];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int pairs = p.batch * p.R;
+  const size_t ostride = (size_t)p.R * kDv;
+  const int max_pieces = ld_uniform(p.sched + 5);   // the schedule table's largest piece count
+  if (max_pieces <= 1) return;
+  if (max_pieces <= kCombineChunk) {
+    // Many short merges: one pair per wave.
+    for (int pair = blockIdx.x * kCombineWaves + wave; pair < pairs; pair += gridDim.x * kCombineWaves) {
+      const int req = pair / p.R, row = pair - req * p.R;
+      const int slot0 = ld_uniform(p.num_splits + req);
+      const int n = ld_uniform(p.num_splits + req + 1) - slot0;
+      if (n <= 1) continue;   // uniform over the wave
+      float M = -INFINITY, l = 0.f;
+      f32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
+      combine_splits(p.lacc + (size_t)slot0 * p.R + row, p.oacc + ((size_t)slot0 * p.R + row) * kDv + lane * 8, p.R,
+                     ostride, 0, 1, n, M, l, a0, a1);
+      combine_store(p, req, row, lane, M, l, a0, a1);
+    }
+    return;
+  }
+  // Few long merges: one pair per workgroup, wave w taking splits w, w + 4, ...
   for (int pair = blockIdx.x; pair < pairs; pair += gridDim.x) {
     const int req = pair / p.R, row = pair - req * p.R;
     const int slot0 = ld_uniform(p.num_splits + req);
     const int n = ld_uniform(p.num_splits + req + 1) - slot0;
     if (n <= 1) continue;   // uniform over the workgroup
-    const float* lrow = p.lacc + (size_t)slot0 * p.R + row;
-    const float* orow = p.oacc + ((size_t)slot0 * p.R + row) * kDv + lane * 8;
-    const size_t ostride = (size_t)p.R * kDv;
+    const int nw = (n - wave + kCombineWaves - 1) / kCombineWaves;   // this wave's splits
     float M = -INFINITY, l = 0.f;
     f32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
-    for (int i0 = wave; i0 < n; i0 += kCombineWaves * kCombineUnroll) {
-      float li[kCombineUnroll];
-      f32x4 b0[kCombineUnroll], b1[kCombineUnroll];
-#pragma unroll
-      for (int u = 0; u < kCombineUnroll; ++u) {
-        const int i = min(i0 + u * kCombineWaves, n - 1);   // clamped: duplicates get weight 0 below
-        li[u] = lrow[(size_t)i * p.R];
-        b0[u] = *(const f32x4*)(orow + (size_t)i * ostride);
-        b1[u] = *(const f32x4*)(orow + (size_t)i * ostride + 4);
-      }
-#pragma unroll
-      for (int u = 0; u < kCombineUnroll; ++u)
-        lse_merge(M, l, a0, a1, li[u], b0[u], b1[u], (i0 + u * kCombineWaves < n && li[u] != -INFINITY) ? 1.f : 0.f);
-    }
+    combine_splits(p.lacc + (size_t)slot0 * p.R + row, p.oacc + ((size_t)slot0 * p.R + row) * kDv + lane * 8, p.R,
+                   ostride, wave, kCombineWaves, nw, M, l, a0, a1);
     red_o[wave][0][lane] = a0;
     red_o[wave][1][lane] = a1;
     if (lane == 0) {
@@ -1121,25 +1167,21 @@ __global__ void __launch_bounds__(kCombineWaves * 64) mla_combine_kernel(Params 
     }
     __syncthreads();
     if (wave == 0) {
-      float Mt = -INFINITY, lt = 0.f;
+      float Mt = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kCombineWaves; ++w) Mt = fmaxf(Mt, red_m[w]);
+      float lt = 0.f;
       f32x4 t0 = {0, 0, 0, 0}, t1 = {0, 0, 0, 0};
+      if (Mt != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kCombineWaves; ++w)
-        lse_merge(Mt, lt, t0, t1, red_m[w], red_o[w][0][lane] / fmaxf(red_l[w], 1e-30f),
-                  red_o[w][1][lane] / fmaxf(red_l[w], 1e-30f), red_l[w]);
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      unsigned short* o = p.out + ((size_t)req * p.R + row) * kDv + lane * 8;
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        w[e] = (unsigned)f32_to_bf16(t0[2 * e] * inv) | ((unsigned)f32_to_bf16(t0[2 * e + 1] * inv) << 16);
-        w[2 + e] = (unsigned)f32_to_bf16(t1[2 * e] * inv) | ((unsigned)f32_to_bf16(t1[2 * e + 1] * inv) << 16);
+        for (int w = 0; w < kCombineWaves; ++w) {
+          const float sw = __builtin_amdgcn_exp2f(red_m[w] - Mt);   // an empty wave (-inf) gives 0
+          t0 += sw * red_o[w][0][lane];
+          t1 += sw * red_o[w][1][lane];
+          lt += sw * red_l[w];
+        }
       }
-      *(u32x4*)o = w;
-      if (lane == 0) {
-        const int s = row / p.h_q, hh = row - s * p.h_q;
-        p.lse[((size_t)req * p.h_q + hh) * p.s_q + s] = lt > 0.f ? (Mt + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
-      }
+      combine_store(p, req, row, lane, Mt, lt, t0, t1);
     }
     __syncthreads();   // red_* are reused by the next pair
   }
@@ -1275,7 +1317,7 @@ static hipEvent_t* profile_slot() {
   return &g_prof.ev[(size_t)(g_prof.used++) * 4];
 }
 
-constexpr int kCombineMaxGrid = 1024;
+constexpr int kCombineMaxGrid = 2048;   // about one round of resident workgroups
 
 extern "C" int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* block_table,
                               const int32_t* cache_seqlens, int batch, int s_q, int h_q, int num_blocks,

@@ -84,7 +84,12 @@ int plan(const int32_t* seqlens, int batch, int num_parts, int fixed_overhead, i
     }
   }
   num_splits[0] = 0;
-  for (int b = 0; b < batch; ++b) num_splits[b + 1] = num_splits[b] + pieces[b];
+  int max_pieces = 0;
+  for (int b = 0; b < batch; ++b) {
+    num_splits[b + 1] = num_splits[b] + pieces[b];
+    max_pieces = std::max(max_pieces, pieces[b]);
+  }
+  for (int p = 0; p < np; ++p) sched[(size_t)p * MLA_SCHED_INTS + 5] = max_pieces;
   *parts_out = np;
   return MLA_OK;
 }

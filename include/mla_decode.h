@@ -47,9 +47,10 @@ enum {
 
 /* Rows of the per-part schedule table: 8 int32 per part,
  *   [begin_req, end_req (inclusive), begin_block (within begin_req),
- *    end_block (exclusive, within end_req), begin_piece, 0, 0, 0]
+ *    end_block (exclusive, within end_req), begin_piece, max_pieces, 0, 0]
  * begin_piece is the index, among begin_req's pieces, of the piece this part
- * holds.  num_splits is an exclusive prefix sum of pieces per request,
+ * holds; max_pieces (equal in every row) is the largest number of pieces of
+ * any request, which the merge kernel uses to pick its work layout.  num_splits is an exclusive prefix sum of pieces per request,
  * length batch + 1: request b owns partial slots [num_splits[b], num_splits[b+1]). */
 #define MLA_SCHED_INTS 8
 

@@ -43,7 +43,11 @@ def blocks_of(seqlens) -> list[int]:
 
 
 def plan(seqlens, num_parts: int, fixed_overhead: int = 0, force_splits: int = 0):
-    """Return (sched int32 [parts, 8], num_splits int32 [b + 1])."""
+    """Return (sched int32 [parts, 8], num_splits int32 [b + 1]).
+
+    A row is [begin_req, end_req, begin_block, end_block, begin_piece,
+    max_pieces, 0, 0]; max_pieces (the same in every row) is the largest
+    number of pieces any request was cut into."""
     n = blocks_of(seqlens)
     b = len(n)
     if b == 0 or num_parts <= 0:
@@ -82,7 +86,14 @@ def plan(seqlens, num_parts: int, fixed_overhead: int = 0, force_splits: int = 0
         parts.append([begin[0], end_req, begin[1], end_blk, begin[2], 0, 0, 0])
     num_splits = np.zeros(b + 1, dtype=np.int32)
     num_splits[1:] = np.cumsum(pieces)
-    return np.array(parts, dtype=np.int32).reshape(-1, SCHED_INTS), num_splits
+    return _with_max_pieces(np.array(parts, dtype=np.int32).reshape(-1, SCHED_INTS), pieces), num_splits
+
+
+def _with_max_pieces(sched: np.ndarray, pieces) -> np.ndarray:
+    """Column 5 of every row: the largest number of pieces of any request
+    (table layout only: it tells the merge how many partials a row can have)."""
+    sched[:, 5] = max(pieces) if len(pieces) else 0
+    return sched
 
 
 def _plan_forced(n, k):
@@ -99,7 +110,7 @@ def _plan_forced(n, k):
         pieces.append(cnt)
     num_splits = np.zeros(len(n) + 1, dtype=np.int32)
     num_splits[1:] = np.cumsum(pieces)
-    return np.array(parts, dtype=np.int32).reshape(-1, SCHED_INTS), num_splits
+    return _with_max_pieces(np.array(parts, dtype=np.int32).reshape(-1, SCHED_INTS), pieces), num_splits
 
 
 def pieces_of(sched: np.ndarray, seqlens):

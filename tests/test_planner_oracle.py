@@ -43,7 +43,7 @@ def test_hand_worked_two_parts():
     # L = {100, 257} -> 2 and 5 blocks; 2 parts, F = 0: payload = ceil(7/2) = 4.
     # Part 0 takes request 0 whole (2) and 2 blocks of request 1; part 1 takes the rest.
     sched, ns = oracle.plan([100, 257], num_parts=2, fixed_overhead=0)
-    assert sched.tolist() == [[0, 1, 0, 2, 0, 0, 0, 0], [1, 1, 2, 5, 1, 0, 0, 0]]
+    assert sched.tolist() == [[0, 1, 0, 2, 0, 2, 0, 0], [1, 1, 2, 5, 1, 2, 0, 0]]   # column 5: most pieces (2)
     assert ns.tolist() == [0, 1, 3]
 
 
@@ -53,15 +53,15 @@ def test_hand_worked_fixed_overhead():
     # 1 - F = 0 blocks can be taken -> part ends.  Part 1: request 1 costs 6 > 4,
     # take 4 - 1 = 3 blocks.  Part 2 (last): the remaining 2 blocks.
     sched, ns = oracle.plan([100, 257], num_parts=3, fixed_overhead=1)
-    assert sched.tolist() == [[0, 0, 0, 2, 0, 0, 0, 0], [1, 1, 0, 3, 0, 0, 0, 0],
-                              [1, 1, 3, 5, 1, 0, 0, 0]]
+    assert sched.tolist() == [[0, 0, 0, 2, 0, 2, 0, 0], [1, 1, 0, 3, 0, 2, 0, 0],
+                              [1, 1, 3, 5, 1, 2, 0, 0]]
     assert ns.tolist() == [0, 1, 3]
 
 
 def test_forced_two_splits_tiny_config():
     sched, ns = oracle.plan([100, 257], num_parts=1, force_splits=2)
-    assert sched.tolist() == [[0, 0, 0, 1, 0, 0, 0, 0], [0, 0, 1, 2, 1, 0, 0, 0],
-                              [1, 1, 0, 3, 0, 0, 0, 0], [1, 1, 3, 5, 1, 0, 0, 0]]
+    assert sched.tolist() == [[0, 0, 0, 1, 0, 2, 0, 0], [0, 0, 1, 2, 1, 2, 0, 0],
+                              [1, 1, 0, 3, 0, 2, 0, 0], [1, 1, 3, 5, 1, 2, 0, 0]]
     assert ns.tolist() == [0, 2, 4]
 
 
@@ -70,7 +70,7 @@ def test_empty_requests_are_placed():
     check_plan_valid([0, 130, 0, 0], sched, ns, 2, 0)
     # n = {0, 3, 0, 0}, payload = ceil(3/2) = 2: request 1 is cut 2 + 1 blocks.
     assert ns.tolist() == [0, 1, 3, 4, 5]
-    assert sched.tolist() == [[0, 1, 0, 2, 0, 0, 0, 0], [1, 3, 2, 0, 1, 0, 0, 0]]
+    assert sched.tolist() == [[0, 1, 0, 2, 0, 2, 0, 0], [1, 3, 2, 0, 1, 2, 0, 0]]
 
 
 @pytest.mark.parametrize("seed", range(40))
