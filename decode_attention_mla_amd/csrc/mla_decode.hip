@@ -291,13 +291,48 @@ __device__ __forceinline__ PieceRange load_part(const Params& p, int part) {
 
 // ---------------------------------------------------------------------------
 // Small row counts (R = s_q * h_q <= 16), the memory-bound regime: one
-// workgroup per part covers every query row.  S^T (16 tokens x 16 rows) uses
-// v_mfma_f32_16x16x32_bf16; its accumulator (lane = query row, 4 consecutive
-// tokens) is directly the B operand of v_mfma_f32_16x16x16_bf16 for
-// O^T (512 x 16) = V^T P^T.
+// workgroup per part covers every query row.
+//   * Each wave copies its 16 token rows of a page into a shared stage (the
+//     18 KiB slice layout above); after a barrier every wave sees all four
+//     slices of the page.
+//   * QK^T is split by tokens: wave w computes S^T (its 16 tokens x 16 rows)
+//     with v_mfma_f32_16x16x32_bf16, Q^T in registers, K from its own slice.
+//   * Its bf16 probabilities go to LDS as B fragments of the same MFMA shape
+//     (32 tokens x 16 rows each, two per page).
+//   * PV is split by columns: wave w accumulates O^T for columns
+//     128 w .. 128 w + 127 over all 64 tokens of the page (8 tiles of 16x16,
+//     32 registers), V^T from transposing reads of all four slices.  Nothing
+//     is merged across waves at the end: each wave stores its own columns.
+//   * The per-row softmax reference is common to the four waves (the max over
+//     the whole first page, exchanged through LDS); row sums are kept per
+//     wave and added at the end.
+//   * Two barriers per page: the page's slices landed (and every wave is past
+//     the previous page: its stage and the P buffer are free), and the P
+//     fragments are written.
+constexpr int kSmallPBytes = 2 * 64 * 16;   // two 32-token P^T fragments
+constexpr int kSmallPvLead = 6;             // V^T fragments in flight
+
+// Max / sum over the four 16-lane rows of a wave (lanes c16, c16 + 16,
+// c16 + 32, c16 + 48: the four token groups of one query row), with two
+// cross-row swaps instead of LDS permutes.
+__device__ __forceinline__ float row_max4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row_sum4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * 2 * kStageBytes];
-  __shared__ float st_m[4][kRowGroup], st_l[4][kRowGroup];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kPageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char pbuf[kSmallPBytes];
+  __shared__ float red[4][kSmallRows];   // per-wave row maxima, then row sums
+  __shared__ int vote[4];                // per-wave restart votes
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -310,11 +345,13 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
   const bool row_ok = c16 < p.R;
   const int tok0 = kWaveTokens * wave;
 
-  LDS_PTR(unsigned char) wlds = (LDS_PTR(unsigned char))smem + wave * 2 * kStageBytes;
-  const unsigned wlds0 = (unsigned)(size_t)wlds;
+  LDS_PTR(unsigned char) lds = (LDS_PTR(unsigned char))smem;
+  LDS_PTR(unsigned char) pb = (LDS_PTR(unsigned char))pbuf;
+  const unsigned wslice = (unsigned)(size_t)lds + wave * kStageBytes;   // this wave's slice of stage 0
   const unsigned dma_off[2] = {stage_dma_offset(lane, 0), stage_dma_offset(lane, 1)};
-  // The request's query rows are staged like a page (row r in token slot r);
-  // slots >= R copy row 0 instead (in bounds; their fragments are zeroed).
+  // The request's query rows are staged like a page slice (row r in token
+  // slot r) in this wave's slice of stage 1; slots >= R copy row 0 instead
+  // (in bounds; their fragments are zeroed).
   unsigned q_dma_off[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
@@ -327,15 +364,27 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
   int qk_off[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) qk_off[b] = c16 * 128 + (((4 * b + g) ^ stage_swizzle(c16)) << 4);
-  // PV A fragment of column tile ct: lane (group g, index c16) reads local
-  // token 4 g + c16 / 4, columns 16 ct + 4 (c16 % 4) .. + 3 = block ct / 4,
-  // in-block chunk 2 (ct % 4) + (c16 % 4) / 2, byte 8 (c16 % 2); it receives
-  // column 16 ct + c16 of tokens 4 g .. 4 g + 3.
-  const int tv = 4 * g + (c16 >> 2);
-  int pv_off[4];
+  // PV A fragment (V^T: 16 columns x 32 tokens of a 32-token step): lane
+  // (g, c16) needs column c16 of the tile and step tokens 8 g .. 8 g + 7,
+  // from two transposing reads r = 0, 1: the group's 16 lanes read tokens
+  // 8 g + 4 r .. + 3 (lane c16: token 8 g + 4 r + c16 / 4, columns
+  // 4 (c16 % 4) .. + 3 of the tile) and lane c16 receives column c16.  Step
+  // token 8 g + 4 r + c16 / 4 is local token 8 (g % 2) + 4 r + c16 / 4 of
+  // slice g / 2 of the step; tile ct of this wave's columns is column block
+  // 2 w + ct / 4, in-block chunk 2 (ct % 4) + (c16 % 4) / 2, byte 8 (c16 % 2).
+  int pv_off[2][4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-    pv_off[m] = tv * 128 + (((2 * m + ((c16 & 3) >> 1)) ^ stage_swizzle(tv)) << 4) + (c16 & 1) * 8;
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int tl = 8 * (g & 1) + 4 * r + (c16 >> 2);
+      pv_off[r][q] = (g >> 1) * kStageBytes + tl * 128 +
+                     (((2 * q + ((c16 & 3) >> 1)) ^ stage_swizzle(tl)) << 4) + 8 * (c16 & 1);
+    }
+  // This lane's 4 probabilities (local tokens 4 g .. + 3 of row c16) are
+  // step wave / 2, step tokens 16 (wave % 2) + 4 g .. + 3: B lane
+  // (2 (wave % 2) + g / 2, c16), bytes 8 (g % 2) .. + 7.
+  const int pw_off = ((wave >> 1) * 64 + (2 * (wave & 1) + (g >> 1)) * 16 + c16) * 16 + 8 * (g & 1);
 
   for (int req = pr.begin_req; req <= pr.end_req; ++req) {
     const int L = ld_uniform(p.seqlens + req);
@@ -350,123 +399,156 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
       return uniform_ptr(p.kv + (size_t)ld_uniform(bt + j) * kPageBytes + (size_t)tok0 * kRowBytes);
     };
 
-    f32x4 o[kDv / 16];
+    f32x4 o[8];
     float m_ref = -INFINITY, l_run = 0.f;
     bool have_ref = false;
     // Q^T fragments (B operand): row c16, dims 32 ks + 8 g .. + 7.  Q is
-    // copied into stage 1 ahead of the first page, read into registers as
-    // soon as it lands, and stage 1 then takes the second page, so both
-    // pages are in flight while Q is in use.  (All global reads here are
-    // explicit copies with explicit waits: no compiler-tracked load may be
-    // outstanding while page copies are in flight.)
+    // copied into this wave's slice of stage 1 ahead of the first page, read
+    // into registers as soon as it lands, and that slice then takes the
+    // second page, so both pages are in flight while Q is in use.  (All
+    // global reads here are explicit copies with explicit waits: no
+    // compiler-tracked load may be outstanding while page copies are in
+    // flight.)
     bf16x8 qf[kQkSteps];
-    issue_stage<false>(uniform_ptr(p.q + (size_t)req * p.R * kRowBytes), wlds0 + kStageBytes, q_dma_off);
+    issue_stage<false>(uniform_ptr(p.q + (size_t)req * p.R * kRowBytes), wslice + kPageBytes, q_dma_off);
     for (int attempt = 0;; ++attempt) {
-      if (lo < hi) issue_stage<true>(rows_of(lo), wlds0, dma_off);
+      if (lo < hi) issue_stage<true>(rows_of(lo), wslice, dma_off);
       if (attempt == 0) {
         if (lo < hi)
           wait_vmcnt<kStageSlices>();   // Q (the first page may still be in flight)
         else
           wait_vmcnt<0>();
         const unsigned keep = row_ok ? ~0u : 0u;
+        LDS_PTR(unsigned char) qs = lds + kPageBytes + wave * kStageBytes;
 #pragma unroll
         for (int ks = 0; ks < kQkSteps; ++ks) {
-          u32x4 v = *(LDS_PTR(u32x4))(wlds + kStageBytes + (ks >> 1) * kStageBlock + qk_off[ks & 1]);
+          u32x4 v = *(LDS_PTR(u32x4))(qs + (ks >> 1) * kStageBlock + qk_off[ks & 1]);
           v &= keep;
           qf[ks] = __builtin_bit_cast(bf16x8, v);
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage 1 is free again
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the Q slot is free again
       }
-      if (lo + 1 < hi) issue_stage<true>(rows_of(lo + 1), wlds0 + kStageBytes, dma_off);
+      if (lo + 1 < hi) issue_stage<true>(rows_of(lo + 1), wslice + kPageBytes, dma_off);
 
 #pragma unroll
-      for (int ct = 0; ct < kDv / 16; ++ct) o[ct] = f32x4{0, 0, 0, 0};
+      for (int ct = 0; ct < 8; ++ct) o[ct] = f32x4{0, 0, 0, 0};
       float m_seen = -INFINITY;
       l_run = 0.f;
+      bool restart = false;
 
       for (int j = lo; j < hi; ++j) {
         const int stage = (j - lo) & 1;
-        LDS_PTR(unsigned char) buf = wlds + stage * kStageBytes;
-        if (j + 1 < hi)
+        LDS_PTR(unsigned char) buf = lds + stage * kPageBytes;
+        // This wave's slice of page j (the next page's copy, if any, is issued
+        // below, after the barrier).
+        if (j == lo && lo + 1 < hi)
           wait_vmcnt<kStageSlices>();
         else
           wait_vmcnt<0>();
-        const int valid = min(kPage, L - j * kPage) - tok0;   // valid local tokens (may be <= 0)
-        if (valid < kWaveTokens) zero_stage_tail(buf, valid, lane);
+        const int valid = min(kPage, L - j * kPage);
+        if (valid - tok0 < kWaveTokens) zero_stage_tail(buf + wave * kStageBytes, valid - tok0, lane);
+        lds_barrier();   // page j is visible; every wave is past page j - 1
+        // Page j + 1 goes to the stage page j - 1 held (pages lo, lo + 1 were
+        // issued ahead of the loop).  (A third page in flight from the start,
+        // held in registers, was measured slower: every page then lands late.)
+        if (j > lo && j + 1 < hi) issue_stage<true>(rows_of(j + 1), wslice + ((j + 1 - lo) & 1) * kPageBytes, dma_off);
 
-        // ---- S^T (16 tokens x 16 rows) = K Q^T, three accumulation chains.
+        // ---- S^T (this wave's 16 tokens x 16 rows) = K Q^T, three chains.
+        LDS_PTR(unsigned char) own = buf + wave * kStageBytes;
         u32x4 kf[kQkSteps];
 #pragma unroll
         for (int ks = 0; ks < kQkSteps; ++ks)
-          kf[ks] = *(LDS_PTR(u32x4))(buf + (ks >> 1) * kStageBlock + qk_off[ks & 1]);
+          kf[ks] = *(LDS_PTR(u32x4))(own + (ks >> 1) * kStageBlock + qk_off[ks & 1]);
         f32x4 sacc[3] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
 #pragma unroll
         for (int ks = 0; ks < kQkSteps; ++ks)
           sacc[ks % 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[ks]), qf[ks],
                                                                   sacc[ks % 3], 0, 0, 0);
-        const i16x4 pb = probabilities(sacc[0] + sacc[1] + sacc[2], g, valid, p.scale_log2, have_ref, m_ref,
-                                       m_seen, l_run);
-        have_ref = true;   // the first page of the first attempt set the reference
+        const f32x4 sv = sacc[0] + sacc[1] + sacc[2];
 
-        // ---- O^T (512 x 16) += V^T (512 x 16 tokens) P^T, two batches of reads.
+        // ---- softmax against the common reference (base 2).
+        float x[4], mloc = -INFINITY;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          i16x4 vf[16];
+        for (int v = 0; v < 4; ++v) {
+          // (softmax_scale >= 0, so masking before or after scaling is the same.)
+          x[v] = tok0 + 4 * g + v < valid ? sv[v] * p.scale_log2 : -INFINITY;
+          mloc = fmaxf(mloc, x[v]);
+        }
+        mloc = row_max4(mloc);   // this wave's tokens of row c16
+        if (!have_ref) {   // first page of the first attempt: the whole page's row max
+          if (g == 0) red[wave][c16] = mloc;
+          lds_barrier();
+          m_ref = fmaxf(fmaxf(red[0][c16], red[1][c16]), fmaxf(red[2][c16], red[3][c16]));
+          have_ref = true;
+        }
+        m_seen = fmaxf(m_seen, mloc);
+        i16x4 pk;
 #pragma unroll
-          for (int k = 0; k < 16; ++k) {
-            const int ct = 16 * h + k;
-            vf[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (LDS_PTR(i16x4))(buf + (ct >> 2) * kStageBlock + pv_off[ct & 3]));
+        for (int v = 0; v < 4; ++v) {
+          const float pe = __builtin_amdgcn_exp2f(x[v] - m_ref);   // masked tokens: exp2(-inf) = 0
+          l_run += pe;   // row sum from the fp32 values; only the PV operand is bf16
+          pk[v] = __builtin_bit_cast(short, (__bf16)pe);
+        }
+        *(LDS_PTR(i16x4))(pb + pw_off) = pk;
+        // A row max more than 2^64 above the reference: every wave redoes the
+        // piece with the exact maxima (first attempt only, so at most twice).
+        if (attempt == 0) {
+          const bool any_bad = __any(mloc > m_ref + kRefHeadroom);
+          if (lane == 0) vote[wave] = any_bad;
+        }
+        lds_barrier();   // every wave's probabilities (and vote) are in LDS
+        if (attempt == 0) restart |= (vote[0] | vote[1] | vote[2] | vote[3]) != 0;
+
+        // ---- O^T (this wave's 128 columns x 16 rows) += V^T P^T, two steps of
+        // 32 tokens, 8 column tiles each.
+        // Software pipelined: V^T fragment i + kSmallPvLead is read right after
+        // the MFMA of fragment i (i = 8 step + ct).
+        {
+          auto vread = [&](int i) {
+            LDS_PTR(unsigned char) a = buf + (i >> 3) * 2 * kStageBytes + (2 * wave + ((i & 7) >> 2)) * kStageBlock;
+            const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv_off[0][i & 3]));
+            const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv_off[1][i & 3]));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+          };
+          const bf16x8 pB0 = *(LDS_PTR(bf16x8))(pb + lane * 16);
+          const bf16x8 pB1 = *(LDS_PTR(bf16x8))(pb + (64 + lane) * 16);
+          bf16x8 vf[kSmallPvLead];
+#pragma unroll
+          for (int i = 0; i < kSmallPvLead; ++i) vf[i] = vread(i);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            o[i & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[i % kSmallPvLead], i < 8 ? pB0 : pB1, o[i & 7], 0, 0, 0);
+            if (i + kSmallPvLead < 16) vf[i % kSmallPvLead] = vread(i + kSmallPvLead);
+            __builtin_amdgcn_sched_barrier(0);
           }
-          if (h == 1 && j + 2 < hi) {
-            // Every read of this stage has been issued; once they complete the
-            // stage takes page j + 2.
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            issue_stage<true>(rows_of(j + 2), wlds0 + stage * kStageBytes, dma_off);
-          }
-#pragma unroll
-          for (int k = 0; k < 16; ++k)
-            o[16 * h + k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[k], pb, o[16 * h + k], 0, 0, 0);
         }
       }
-      // One retry with the exact maximum always suffices: every probability is then <= 1.
-      if (attempt > 0 || !__any(m_seen > m_ref + kRefHeadroom)) break;
-      m_ref = m_seen;
+      wait_vmcnt<0>();
+      if (!restart) break;
+      // Restart: the exact row maxima over all four waves become the reference.
+      lds_barrier();   // every wave is past the last page
+      if (g == 0) red[wave][c16] = m_seen;
+      lds_barrier();
+      m_ref = fmaxf(fmaxf(red[0][c16], red[1][c16]), fmaxf(red[2][c16], red[3][c16]));
+      lds_barrier();   // red is read before it is written again
     }
 
-    // ---- merge the four waves' states.  Each wave parks its accumulator in
-    // its own stages (its copies are all complete), then every wave
-    // finalises 128 of the 512 columns.
-    float lw = l_run + __shfl_xor(l_run, 16);
-    lw += __shfl_xor(lw, 32);
-    if (g == 0) {
-      st_m[wave][c16] = m_ref;
-      st_l[wave][c16] = lw;
-    }
-#pragma unroll
-    for (int ct = 0; ct < kDv / 16; ++ct) *(LDS_PTR(f32x4))(wlds + (ct * 64 + lane) * 16) = o[ct];
+    // ---- epilogue: row sums over the four waves; each wave stores its columns.
+    const float lw = row_sum4(l_run);
+    lds_barrier();   // every wave is done with red, the P buffer and the stages
+    if (g == 0) red[wave][c16] = lw;
     lds_barrier();
-    // All 32 parked fragments this wave merges are read before any is used.
-    f32x4 part[4][8];
+    const float l_tot = (red[0][c16] + red[1][c16]) + (red[2][c16] + red[3][c16]);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse2 = l_tot > 0.f ? m_ref + __builtin_amdgcn_logf(l_tot) : -INFINITY;
+    // In the O^T accumulator lane (g, c16) holds row c16, columns 4 g .. + 3 of the tile.
+    if (row_ok) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        part[w][k] = *(LDS_PTR(f32x4))((LDS_PTR(unsigned char))smem + w * 2 * kStageBytes +
-                                       ((8 * wave + k) * 64 + lane) * 16);
-    float wgt[4], inv, lse2;
-    merge_weights(st_m, st_l, c16, wgt, inv, lse2);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int ct = 8 * wave + k;
-      f32x4 acc = {0, 0, 0, 0};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) acc += wgt[w] * part[w][k];
-      if (row_ok) store_cols4(p, req, c16, split, slot, 16 * ct + 4 * g, acc * inv);   // 4 consecutive columns
+      for (int ct = 0; ct < 8; ++ct) store_cols4(p, req, c16, split, slot, 128 * wave + 16 * ct + 4 * g, o[ct] * inv);
     }
     if (wave == 0 && g == 0 && row_ok) store_lse(p, req, c16, split, slot, lse2);
-    lds_barrier();  // every wave is done reading the parked accumulators
+    lds_barrier();   // red is read; the next piece may reuse LDS
   }
 }
 
@@ -1221,7 +1303,8 @@ static int policy(const int32_t* seqlens, int batch, int h_q, int s_q, int* num_
   const Geometry g = geometry(h_q, s_q);
   *parts = *num_cus / g.row_groups;
   if (*parts < 1) *parts = 1;
-  *F = g.R <= kSmallRows ? 3 : 2;
+  // Per-piece overhead in pages (prologue, epilogue, partial write + merge), measured per kernel.
+  *F = g.R <= kSmallRows ? 3 : g.R >= kWideRows ? 4 : 2;
   return MLA_OK;
 }
 

@@ -63,7 +63,7 @@ def test_get_metadata_policy_matches_reference_plan(h_q, s_q):
     R = h_q * s_q
     groups = 1 if R <= 16 else -(-R // 128) if R >= 128 else -(-R // 32)
     parts = max(1, 256 // groups)
-    F = 3 if R <= 16 else 2
+    F = 3 if R <= 16 else 4 if R >= 128 else 2
     s_ref, n_ref = oracle.plan(sl, num_parts=parts, fixed_overhead=F)
     assert np.array_equal(sched, s_ref) and np.array_equal(ns, n_ref) and total == n_ref[-1]
     assert total <= sched.shape[0] + len(sl) - 1
