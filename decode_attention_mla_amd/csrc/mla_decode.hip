@@ -817,18 +817,20 @@ constexpr int kPFragBytes = kWideTiles * 4 * 64 * 16;      // P^T: 4 row tiles x
 constexpr int kQkSteps16 = kDqk / 16;                      // 36 k-steps of the 32x32x16 MFMA
 constexpr int kWideQkLead = 4;                             // K fragment reads in flight
 constexpr float kRestartFlag = -0.0f;                      // sign bit carried by a P element
-constexpr int kWideSoftmaxPieces = 12;                     // pieces of one tile's softmax
+constexpr int kWideSoftmaxPieces = 14;                     // pieces of one tile's softmax
 
 // Softmax state of one 32-token S^T tile.  Lane l holds row l % 32 and, in
-// element 4 i + e, token 8 i + 4 (l / 32) + e of the tile.  The pieces:
-//   0      max of this lane's 16 scores
-//   1      row max over both lane halves, scaled; the first tile sets the
-//          reference; running max and the restart test
-//   2 .. 5, 7 .. 10   two probabilities exp2(scale s - reference) each: row
-//          sum, bf16 pairs
-//   6, 11  the two 8-token halves go to LDS as PV B fragments
+// element 4 i + e, token 8 i + 4 (l / 32) + e of the tile.  The pieces (each
+// rides between MFMAs; no piece depends on a result of the same piece):
+//   0, 1   max of this lane's 16 scores (partial maxima, then their max)
+//   2      row max over both lane halves, scaled
+//   3      the first tile sets the reference; running max, restart test
+//   4 .. 13   element pairs through a three-stage pipeline: exponent
+//          argument, exp2, row sum + bf16 pack; each completed 8-token half
+//          goes to LDS as a PV B fragment
 struct WideSoftmax {
-  float mloc;
+  float mp[6], mloc;
+  float ex[16];
   u32x4 pk[2];
 };
 
@@ -943,6 +945,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
         for (int c = 0; c < 4; ++c) o[a][c] = f32x16{};
       float m_seen = -INFINITY;
       l_run = 0.f;
+      float l_part[4] = {0.f, 0.f, 0.f, 0.f};
       bool restart = false;
       int next_blk = ld_uniform(bt + (lo + 1 < hi ? lo + 1 : lo));
 
@@ -979,50 +982,75 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
         auto softmax_piece = [&](int tt, int k, const f32x16& sacc) {
           WideSoftmax& t = sm[tt];
           const bool ragged = valid < 32 * tt + 32;   // uniform
-          auto ok = [&](int v) { return 32 * tt + 8 * (v >> 2) + (v & 3) < lim; };
+          // Element v of the tile is a real token.  Only evaluated inside the
+          // ragged branches: `lim_in` is re-materialised there so that the
+          // compares cannot be hoisted onto the full-tile path.
+          auto ok = [&](int v, int lim_in) { return 32 * tt + 8 * (v >> 2) + (v & 3) < lim_in; };
+          auto branch_lim = [&]() {
+            int l2;
+            asm volatile("v_mov_b32 %0, %1 ; ragged tile" : "=v"(l2) : "v"(lim));
+            return l2;
+          };
           if (k == 0) {
-            auto max16 = [](const float* x) {
-              const float m0 = fmaxf(fmaxf(x[0], x[1]), x[2]), m1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
-              const float m2 = fmaxf(fmaxf(x[6], x[7]), x[8]), m3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
-              const float m4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
-              return fmaxf(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)), fmaxf(m4, x[15]));
-            };
-            float x[16];
+            // Partial maxima (five independent max3s).
             if (ragged) {
+              // A real branch (the statement cannot be speculated): full
+              // tiles must not pay for the masking selects.
+              const int l2 = branch_lim();
+              float x[16];
 #pragma unroll
-              for (int v = 0; v < 16; ++v) x[v] = ok(v) ? sacc[v] : -INFINITY;
-              t.mloc = max16(x);
+              for (int v = 0; v < 16; ++v) x[v] = ok(v, l2) ? sacc[v] : -INFINITY;
+#pragma unroll
+              for (int i = 0; i < 5; ++i) t.mp[i] = fmaxf(fmaxf(x[3 * i], x[3 * i + 1]), x[3 * i + 2]);
+              t.mp[5] = x[15];
             } else {
 #pragma unroll
-              for (int v = 0; v < 16; ++v) x[v] = sacc[v];
-              t.mloc = max16(x);
+              for (int i = 0; i < 5; ++i) t.mp[i] = fmaxf(fmaxf(sacc[3 * i], sacc[3 * i + 1]), sacc[3 * i + 2]);
+              t.mp[5] = sacc[15];
             }
           } else if (k == 1) {
+            t.mloc = fmaxf(fmaxf(fmaxf(t.mp[0], t.mp[1]), t.mp[2]), fmaxf(fmaxf(t.mp[3], t.mp[4]), t.mp[5]));
+          } else if (k == 2) {
             // The other half of the row's tokens sits in lane l ^ 32
             // (softmax_scale >= 0: the max commutes with the scaling).
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t.mloc), __float_as_uint(t.mloc), false, false);
-            const float mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2;
-            if (!have_ref) m_ref = mloc;   // first tile of the first page of the first attempt
+            t.mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2;
+          } else if (k == 3) {
+            if (!have_ref) m_ref = t.mloc;   // first tile of the first page of the first attempt
             have_ref = true;
-            m_seen = fmaxf(m_seen, mloc);
-            bad |= mloc > m_ref + kRefHeadroom;
+            m_seen = fmaxf(m_seen, t.mloc);
+            bad |= t.mloc > m_ref + kRefHeadroom;
             if (tt == 1) flag = attempt == 0 && __any(bad);   // wave-wide vote, outside any branch
-          } else if (k == 6 || k == 11) {
-            const int half = k == 6 ? 0 : 1;
-            u32x4 w = t.pk[half];
-            if (tt == 1 && half == 1 && lane == 0 && flag) w[0] |= 0x8000u;   // kRestartFlag in element 0
-            *(LDS_PTR(u32x4))(pb + ((wave * 4 + 2 * tt + half) * 64 + lane) * 16) = w;
           } else {
-            const int half = k < 6 ? 0 : 1, e = k < 6 ? k - 2 : k - 7;   // elements 8 half + 2 e, + 1
-            const int v = 8 * half + 2 * e;
-            float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], p.scale_log2, -m_ref));
-            float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v + 1], p.scale_log2, -m_ref));
-            if (ragged) {
-              p0 = ok(v) ? p0 : 0.f;
-              p1 = ok(v + 1) ? p1 : 0.f;
+            // Three-stage pipeline over the 8 element pairs, so that no step
+            // waits on a result of the same step: exponent arguments of pair
+            // k - 4, exp2 of pair k - 5, row sum and bf16 pack of pair k - 6.
+            const int pa = k - 4, pe = k - 5, pc = k - 6;
+            if (pc >= 0 && pc < 8) {
+              float p0 = t.ex[2 * pc], p1 = t.ex[2 * pc + 1];
+              if (ragged) {
+                const int l2 = branch_lim();   // a real branch, as above
+                p0 = ok(2 * pc, l2) ? p0 : 0.f;
+                p1 = ok(2 * pc + 1, l2) ? p1 : 0.f;
+              }
+              l_part[pc & 3] += p0 + p1;   // four independent partial row sums
+              asm volatile("" : "+v"(l_part[pc & 3]));   // keeps the add here (not sunk to the loop end)
+              t.pk[pc >> 2][pc & 3] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)p0, (__bf16)p1});
             }
-            l_run += p0 + p1;
-            t.pk[half][e] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)p0, (__bf16)p1});
+            if (pe >= 0 && pe < 8) {
+              t.ex[2 * pe] = __builtin_amdgcn_exp2f(t.ex[2 * pe]);
+              t.ex[2 * pe + 1] = __builtin_amdgcn_exp2f(t.ex[2 * pe + 1]);
+            }
+            if (pa >= 0 && pa < 8) {
+              t.ex[2 * pa] = __builtin_fmaf(sacc[2 * pa], p.scale_log2, -m_ref);
+              t.ex[2 * pa + 1] = __builtin_fmaf(sacc[2 * pa + 1], p.scale_log2, -m_ref);
+            }
+            if (pc == 3 || pc == 7) {   // an 8-token half is complete: to LDS as a PV B fragment
+              const int half = pc >> 2;
+              u32x4 w = t.pk[half];
+              if (tt == 1 && half == 1 && lane == 0 && flag) w[0] |= 0x8000u;   // kRestartFlag in element 0
+              *(LDS_PTR(u32x4))(pb + ((wave * 4 + 2 * tt + half) * 64 + lane) * 16) = w;
+            }
           }
         };
 
@@ -1096,13 +1124,16 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
         // are discarded), which keeps a single exit from the page loop.  Only
         // the first attempt may ask for a restart (whatever the data, even
         // NaN, the piece is processed at most twice).
+        unsigned short flags[kWideTiles];
 #pragma unroll
-        for (int w = 0; w < kWideTiles; ++w)
-          restart |= attempt == 0 && (*(LDS_PTR(unsigned short))(pb + (w * 4 + 3) * 64 * 16) >> 15) != 0;
+        for (int w = 0; w < kWideTiles; ++w) flags[w] = *(LDS_PTR(unsigned short))(pb + (w * 4 + 3) * 64 * 16);
         pv_block(2, false);
+#pragma unroll
+        for (int w = 0; w < kWideTiles; ++w) restart |= attempt == 0 && (flags[w] >> 15) != 0;
       }
       wait_vmcnt<0>();   // the last page's (repeated) copy
       wide_acc_settle();
+      l_run = (l_part[0] + l_part[1]) + (l_part[2] + l_part[3]);
       if (!restart) break;
       lds_barrier();     // every wave is past the last page before the stages are refilled
       m_ref = m_seen;
