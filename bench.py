@@ -43,6 +43,15 @@ def kernel_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
+def main_kernel_name(rows: int) -> str:
+    """The split-KV kernel the library launches for h_q * s_q = rows."""
+    if rows <= 16:
+        return "mla_splitkv_small_kernel"
+    if rows >= 128:
+        return "mla_splitkv_wide_kernel<true>" if rows <= 128 else "mla_splitkv_wide_kernel<false>"
+    return "mla_splitkv_kernel"
+
+
 def measured_traffic(config_name: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
@@ -229,7 +238,7 @@ def main():
         roof = dict(bound="mfma", achieved=achieved, peak=MFMA_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=achieved / MFMA_PEAK_TFLOPS, traffic=traffic)
         value, unit = head["tflops"], "TFLOP/s"
-    roof["kernel"] = "mla_splitkv_small_kernel" if head["h_q"] * head["s_q"] <= 16 else "mla_splitkv_kernel"
+    roof["kernel"] = main_kernel_name(head["h_q"] * head["s_q"])
     cpu = None
     if not args.no_cpu:
         cpu = (cpu_baseline(inp, head["bytes"], 1e9, "GB/s") if bound_hbm

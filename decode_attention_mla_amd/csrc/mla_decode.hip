@@ -290,6 +290,22 @@ __device__ __forceinline__ PieceRange load_part(const Params& p, int part) {
 }
 
 // ---------------------------------------------------------------------------
+// Maps a workgroup id to (part, row group).  Workgroups are dealt to the 8
+// XCDs round robin (id % 8), and each XCD takes a contiguous run of
+// ceil(parts / 8) parts, all row groups of a part next to each other in its
+// dispatch order: the parts of one request (consecutive in the plan) then
+// share its query rows, and the row groups of a part its KV pages, through
+// that XCD's L2.  The grid is 8 * row_groups * ceil(parts / 8); ids past the
+// last part exit.
+__device__ __forceinline__ void map_block(const Params& p, int& part, int& rg) {
+  const int id = blockIdx.x;
+  const int xcd = id & 7, slot = id >> 3;
+  const int per = (p.num_parts + 7) / 8;
+  rg = slot % p.row_groups;
+  part = xcd * per + slot / p.row_groups;
+}
+
+// ---------------------------------------------------------------------------
 // Small row counts (R = s_q * h_q <= 16), the memory-bound regime: one
 // workgroup per part covers every query row.
 //   * Each wave copies its 16 token rows of a page into a shared stage (the
@@ -336,7 +352,8 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int part = blockIdx.x;
+  int part, rg;
+  map_block(p, part, rg);   // rg = 0: one row group
   if (part >= p.num_parts) return;
   const PieceRange pr = load_part(p, part);
 
@@ -567,21 +584,6 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
 //   * The 32-row x 512 fp32 accumulator is 256 registers per wave; each wave
 //     has its own (its tokens' share), merged through LDS in two rounds of
 //     256 columns at the end of a piece.
-
-// Maps a workgroup id to (part, row group).  Workgroups are dealt to the 8
-// XCDs round robin; the row groups of one part share an XCD and are adjacent
-// in its dispatch order.
-__device__ __forceinline__ void map_block(const Params& p, int& part, int& rg) {
-  const int id = blockIdx.x;
-  if (p.row_groups == 1) {
-    part = id;
-    rg = 0;
-    return;
-  }
-  const int xcd = id & 7, slot = id >> 3;
-  rg = slot % p.row_groups;
-  part = (slot / p.row_groups) * 8 + xcd;
-}
 
 constexpr int kParkCols = 8;   // 32-column tiles parked per merge round (32 KiB per wave)
 constexpr int kQkLead = 6;     // K fragment reads in flight ahead of the QK MFMAs
@@ -1478,17 +1480,16 @@ extern "C" int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t
   void* args[] = {&prm};
   const void* main_fn;
   int grid;
+  // The XCD-aware block mapping (map_block) needs 8 * row_groups * ceil(parts / 8) workgroups.
+  grid = 8 * g.row_groups * ((num_parts + 7) / 8);
   if (g.R <= kSmallRows) {
     main_fn = (const void*)mla_splitkv_small_kernel;
-    grid = num_parts;
   } else if (g.R >= kWideRows) {
     // Row groups of one part share pages through L2 (cached copies); a single
     // group streams every page once (nontemporal copies).
     main_fn = g.row_groups == 1 ? (const void*)mla_splitkv_wide_kernel<true> : (const void*)mla_splitkv_wide_kernel<false>;
-    grid = g.row_groups == 1 ? num_parts : 8 * g.row_groups * ((num_parts + 7) / 8);
   } else {
     main_fn = (const void*)mla_splitkv_kernel;
-    grid = g.row_groups == 1 ? num_parts : 8 * g.row_groups * ((num_parts + 7) / 8);
   }
   // Plain launches unless profiling (these are what stream capture records).
   hipError_t e = ev ? hipExtLaunchKernel(main_fn, dim3(grid), dim3(256), args, 0, st, ev[0], ev[1], 0)
