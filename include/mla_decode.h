@@ -104,11 +104,12 @@ int mla_max_parts(const int32_t* cache_seqlens, int batch, int h_q, int s_q, int
 
 /*
  * mla_workspace_bytes — device scratch needed by mla_decode_fwd for a plan
- * with total_splits partial slots: fp32 partial outputs
- * [total_splits, ceil(R/32)*32, 512] and fp32 partial lse
- * [total_splits, ceil(R/32)*32], each region 256-byte aligned (the split-KV
- * workspace of the split-KV blog, 0539edu.com, section 3.1).  Any plan has
- * total_splits <= num_parts + batch - 1.
+ * with total_splits partial slots, R = s_q * h_q: fp32 partial outputs
+ * [total_splits, R, 512] (row-major: one query row's 512 values contiguous)
+ * and fp32 base-2 partial lse [total_splits, R], each region 256-byte aligned
+ * (the split-KV workspace of the split-KV blog, 0539edu.com, section 3.1).
+ * Any plan has total_splits <= num_parts + batch - 1.  The caller allocates
+ * it; its contents need no initialisation and are scratch after the call.
  */
 size_t mla_workspace_bytes(int total_splits, int h_q, int s_q);
 
@@ -132,8 +133,9 @@ size_t mla_workspace_bytes(int total_splits, int h_q, int s_q);
  *   lse           device fp32 [batch, h_q, s_q] (written; -inf when L = 0)
  *   stream        hipStream_t to enqueue on (NULL = the null stream)
  *
- * Enqueues the split-KV kernel, then the combine kernel (whose workgroups
- * return at once for requests that are not split); returns without
+ * Enqueues the split-KV kernel (one of three, by R: <= 16, < 128, >= 128),
+ * then the combine kernel (which returns at once when no request is split,
+ * and skips the rows of requests that are not); returns without
  * synchronising and allocates nothing.  Block-table
  * entries must lie in [0, num_blocks) and the device lengths must match the
  * plan: neither is checked on the device (undefined behaviour otherwise).
