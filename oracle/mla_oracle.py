@@ -27,7 +27,13 @@ justification in the design notes):
   * softmax_scale multiplies the scores (the overview's reference code);
   * lse is the natural log of sum(exp(scaled scores));
   * an empty request (L = 0) gives out = 0 and lse = -inf;
-  * queries are not causally masked: every query token sees all L keys.
+  * by default queries are not causally masked: every query token sees all
+    L keys.  With ``causal=True`` (the API's is_causal flag, for multi-token
+    prediction, s_q > 1) the s_q query tokens are the last s_q positions of
+    the sequence, so query token s (0-based) sees keys 0 .. L - s_q + s, i.e.
+    the first max(0, L - (s_q - 1 - s)) keys; a token that sees no key gets
+    out = 0 and lse = -inf (the split-KV blog's note on splits whose keys are
+    all masked).
 
 Pins (tests/test_oracle.py): closed forms for L = 1, identical scores and
 softmax_scale = 0, a position-encoded cache under uniform weights, the
@@ -89,14 +95,20 @@ def attend(qrows: np.ndarray, keys: np.ndarray, softmax_scale: float):
     return out, lse
 
 
-def mla_decode(q, kv_cache, block_table, cache_seqlens, softmax_scale, requests=None):
+def visible_keys(L: int, s_q: int, s: int, causal: bool) -> int:
+    """Number of keys query token s of s_q sees (see the causal reading above)."""
+    return int(L) if not causal else max(0, int(L) - (s_q - 1 - s))
+
+
+def mla_decode(q, kv_cache, block_table, cache_seqlens, softmax_scale, requests=None, causal=False):
     """Dense MLA decode for every (request, query token, head).
 
     q uint16 [b, s_q, h_q, 576] (bf16 bits); kv_cache uint16 [nb, 64, 1, 576];
     block_table int32 [b, max_blocks]; cache_seqlens int32 [b].
     Returns out float64 [b, s_q, h_q, 512] and lse float64 [b, h_q, s_q].
     ``requests`` restricts the work to a subset of request indices (the
-    other entries are left as NaN).
+    other entries are left as NaN).  ``causal`` masks each query token to the
+    keys before and at its own position.
     """
     b, s_q, h_q, d = q.shape
     assert d == D_QK
@@ -105,24 +117,27 @@ def mla_decode(q, kv_cache, block_table, cache_seqlens, softmax_scale, requests=
     todo = range(b) if requests is None else requests
     for i in todo:
         keys = request_keys(kv_cache, block_table[i], int(cache_seqlens[i]))
-        qrows = bf16_to_f64(q[i].reshape(s_q * h_q, D_QK))   # row r = s * h_q + h
-        o, ls = attend(qrows, keys, softmax_scale)
-        out[i] = o.reshape(s_q, h_q, D_V)
-        lse[i] = ls.reshape(s_q, h_q).T
+        for s in range(s_q):
+            qrows = bf16_to_f64(q[i, s])                       # [h_q, 576]
+            o, ls = attend(qrows, keys[:visible_keys(cache_seqlens[i], s_q, s, causal)], softmax_scale)
+            out[i, s] = o
+            lse[i, :, s] = ls
     return out, lse
 
 
-def mla_decode_rows(q, kv_cache, block_table, cache_seqlens, softmax_scale, picks):
+def mla_decode_rows(q, kv_cache, block_table, cache_seqlens, softmax_scale, picks, causal=False):
     """Outputs for a sample of (request, query token, head) triples.
 
     Returns out float64 [n, 512] and lse float64 [n] in the order of ``picks``.
     """
     outs, lses = [], []
     cache = {}
+    s_q = q.shape[1]
     for (i, s, h) in picks:
         if i not in cache:
             cache[i] = request_keys(kv_cache, block_table[i], int(cache_seqlens[i]))
-        o, ls = attend(bf16_to_f64(q[i, s, h])[None, :], cache[i], softmax_scale)
+        keys = cache[i][:visible_keys(cache_seqlens[i], s_q, s, causal)]
+        o, ls = attend(bf16_to_f64(q[i, s, h])[None, :], keys, softmax_scale)
         outs.append(o[0])
         lses.append(ls[0])
     return np.array(outs), np.array(lses)

@@ -302,3 +302,75 @@ def test_workload_recipe_properties():
     inp = W.config_inputs(1)
     assert list(inp.cache_seqlens) == [100, 257]
     assert inp.num_blocks == 16
+
+
+# ---------------------------------------------------------------------------
+# Causal masking for multi-token prediction (the API's is_causal flag): the
+# s_q query tokens are the last s_q positions, token s sees keys
+# 0 .. L - s_q + s.
+
+@pytest.mark.parametrize("L", [1, 2, 3, 64, 65, 66, 130])
+def test_causal_position_encoded_cache(L):
+    """Uniform weights (scale 0) over position-encoded keys: token s of 3
+    averages positions 0 .. L - 3 + s, so out = (L - 3 + s) / 2 and
+    lse = ln(L - 2 + s); a token that sees no key gives 0 and -inf."""
+    s_q = 3
+    keys = np.zeros((L, D_QK), np.float32)
+    keys[:, 0] = np.arange(L)
+    q, kv, bt, sl = _single_request(keys, np.ones((s_q, D_QK), np.float32), 0.0, seed=L)
+    q = q.reshape(1, s_q, 1, D_QK)
+    out, lse = oracle.mla_decode(q, kv, bt, sl, 0.0, causal=True)
+    for s in range(s_q):
+        n = L - 2 + s            # keys 0 .. L - 3 + s
+        if n <= 0:
+            assert np.all(out[0, s, 0] == 0) and lse[0, 0, s] == -np.inf
+        else:
+            assert abs(out[0, s, 0, 0] - (n - 1) / 2) < 1e-12
+            assert abs(lse[0, 0, s] - math.log(n)) < 1e-12
+
+
+def test_causal_single_query_token_is_the_dense_result():
+    inp = W.config_inputs(1)
+    a = oracle.mla_decode(inp.q, inp.kv_cache, inp.block_table, inp.cache_seqlens, inp.softmax_scale)
+    b = oracle.mla_decode(inp.q, inp.kv_cache, inp.block_table, inp.cache_seqlens, inp.softmax_scale, causal=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_causal_brute_force_exact_rational_tiny():
+    """Exact rational scores; token s of s_q = 2 keeps only keys t <= L - 2 + s."""
+    inp = W.make_inputs(2, 2, 2, [2, 66], pool=6, max_blocks=2, seed=9)
+    out, lse = oracle.mla_decode(inp.q, inp.kv_cache, inp.block_table, inp.cache_seqlens,
+                                 inp.softmax_scale, causal=True)
+    scale = Fraction(inp.softmax_scale)
+    for b in range(2):
+        L = int(inp.cache_seqlens[b])
+        toks = []
+        for t in range(L):
+            row = inp.kv_cache[inp.block_table[b, t // PAGE], t % PAGE, 0]
+            toks.append([Fraction(float(x)) for x in W.bf16_bits_to_f32(row)])
+        for s in range(2):
+            seen = [k for t, k in enumerate(toks) if t <= L - 2 + s]
+            for h in range(2):
+                qq = [Fraction(float(x)) for x in W.bf16_bits_to_f32(inp.q[b, s, h])]
+                sc = [float(scale * sum(a * c for a, c in zip(qq, k))) for k in seen]
+                m = max(sc)
+                w = [math.exp(x - m) for x in sc]
+                z = math.fsum(w)
+                assert abs(lse[b, h, s] - (m + math.log(z))) < 1e-12
+                for c in (0, 3, 300, 511):
+                    ref = math.fsum(wi * float(k[c]) for wi, k in zip(w, seen)) / z
+                    assert abs(out[b, s, h, c] - ref) < 1e-12
+
+
+def test_causal_rows_sampler_matches_full():
+    inp = W.make_inputs(3, 2, 4, [70, 1, 129], pool=8, max_blocks=3, seed=10)
+    out, lse = oracle.mla_decode(inp.q, inp.kv_cache, inp.block_table, inp.cache_seqlens,
+                                 inp.softmax_scale, causal=True)
+    picks = [(0, 0, 1), (0, 1, 3), (1, 0, 0), (1, 1, 2), (2, 0, 3)]
+    o, l = oracle.mla_decode_rows(inp.q, inp.kv_cache, inp.block_table, inp.cache_seqlens,
+                                  inp.softmax_scale, picks, causal=True)
+    for k, (i, s, h) in enumerate(picks):
+        if np.isneginf(lse[i, h, s]):
+            assert np.isneginf(l[k]) and np.all(o[k] == 0)
+        else:
+            assert np.allclose(o[k], out[i, s, h], rtol=0, atol=1e-13) and abs(l[k] - lse[i, h, s]) < 1e-13
