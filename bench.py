@@ -68,7 +68,7 @@ def measured_traffic(config_name: str):
     return e.get("bytes_per_launch")
 
 
-def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6):
+def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6, causal: bool = False):
     """Times one workload three ways:
 
     * graph: ``rot`` decode steps (one per rotating copy of q and the KV
@@ -86,7 +86,7 @@ def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6
     t = time.perf_counter()
     inp = W.config_inputs(idx)
     log(f"[bench] config {idx} {inp.name}: inputs drawn in {time.perf_counter() - t:.1f}s")
-    flops, nbytes = W.algorithmic_work(inp.cache_seqlens, inp.s_q, inp.h_q)
+    flops, nbytes = W.algorithmic_work(inp.cache_seqlens, inp.s_q, inp.h_q, causal=causal)
     dev = torch.device("cuda", 0)
 
     def bf16(a):
@@ -116,7 +116,7 @@ def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6
 
     def step(i):
         mla.mla_decode_fwd(qs[i % rot], kvs[i % rot], bt, sl, inp.softmax_scale, sched, ns, out=out, lse=lse,
-                           workspace=ws)
+                           workspace=ws, causal=causal)
 
     for i in range(warmup):
         step(i)
@@ -169,14 +169,16 @@ def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6
     eager_ms = (time.perf_counter() - t0) * 1e3 / steps
 
     res = dict(
-        workload=inp.name, batch=b, s_q=inp.s_q, h_q=inp.h_q, sum_seqlen=int(inp.cache_seqlens.sum()),
+        workload=inp.name + ("_causal" if causal else ""), batch=b, s_q=inp.s_q, h_q=inp.h_q,
+        sum_seqlen=int(inp.cache_seqlens.sum()),
         parts=int(sched.shape[0]), total_splits=int(total), rotating_copies=rot, graph_steps=graph_steps,
         flops=flops, bytes=nbytes, ms_per_step=ms_per_step, eager_ms_per_step=eager_ms,
         main_kernel_ms=main_avg, combine_kernel_ms=comb_avg, plan_us=plan_us,
         tflops=flops / (ms_per_step * 1e-3) / 1e12, gbs=nbytes / (ms_per_step * 1e-3) / 1e9,
         main_kernel_tflops=flops / (main_avg * 1e-3) / 1e12, main_kernel_gbs=nbytes / (main_avg * 1e-3) / 1e9,
     )
-    log(f"[bench] config {idx}: {json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()})}")
+    log(f"[bench] config {idx}{' causal' if causal else ''}: "
+        f"{json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()})}")
     del kvs, qs
     torch.cuda.empty_cache()
     return inp, res
@@ -247,11 +249,11 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        for idx in (3, 4, 5):
-            if idx == args.config:
+        for idx, causal in ((3, False), (4, False), (4, True), (5, False)):
+            if idx == args.config and not causal:
                 continue
-            _, r = run_workload(idx, args.extra_steps, max(2, args.extra_steps // 5))
-            extra[f"config{idx}"] = dict(
+            _, r = run_workload(idx, args.extra_steps, max(2, args.extra_steps // 5), causal=causal)
+            extra[f"config{idx}" + ("_causal" if causal else "")] = dict(
                 workload=r["workload"], tflops=r["tflops"], frac_mfma_peak=r["tflops"] / MFMA_PEAK_TFLOPS,
                 gbs=r["gbs"], frac_hbm_peak=r["gbs"] / HBM_PEAK_GBS, ms_per_step=r["ms_per_step"],
                 eager_ms_per_step=r["eager_ms_per_step"], main_kernel_tflops=r["main_kernel_tflops"],

@@ -53,8 +53,8 @@ def lib() -> ctypes.CDLL:
     L.mla_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     L.mla_workspace_bytes.restype = ctypes.c_size_t
     L.mla_decode_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                 ctypes.c_int, ctypes.c_float, vp, ctypes.c_int, vp, vp, ctypes.c_size_t,
-                                 vp, vp, vp]
+                                 ctypes.c_int, ctypes.c_float, ctypes.c_int, vp, ctypes.c_int, vp, vp,
+                                 ctypes.c_size_t, vp, vp, vp]
     L.mla_decode_fwd.restype = ctypes.c_int
     L.mla_profile_start.argtypes = [ctypes.c_int]
     L.mla_profile_start.restype = ctypes.c_int
@@ -144,12 +144,14 @@ def _need(cond: bool, msg: str) -> None:
 
 
 def mla_decode_fwd(q, kv_cache, block_table, cache_seqlens, softmax_scale: float, sched, num_splits,
-                   out=None, lse=None, workspace=None):
+                   out=None, lse=None, workspace=None, causal: bool = False):
     """Dense MLA decode.  Returns (out bf16 [b, s_q, h_q, 512], lse fp32 [b, h_q, s_q]).
 
     q bf16 [b, s_q, h_q, 576]; kv_cache bf16 [num_blocks, 64, 1, 576];
     block_table int32 [b, max_blocks]; cache_seqlens int32 [b];
     sched / num_splits from get_mla_metadata for the same cache_seqlens.
+    causal: query token s of s_q sees keys 0 .. L - s_q + s (multi-token
+    prediction) instead of all L.
     All tensors on the same GPU, contiguous.  Enqueued on the current stream.
     """
     import torch
@@ -183,7 +185,8 @@ def mla_decode_fwd(q, kv_cache, block_table, cache_seqlens, softmax_scale: float
     stream = torch.cuda.current_stream(q.device).cuda_stream
     rc = lib().mla_decode_fwd(q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(), cache_seqlens.data_ptr(),
                               b, s_q, h_q, int(kv_cache.shape[0]), int(block_table.shape[1]),
-                              float(softmax_scale), sched.data_ptr(), num_parts, num_splits.data_ptr(),
+                              float(softmax_scale), 1 if causal else 0, sched.data_ptr(), num_parts,
+                              num_splits.data_ptr(),
                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                               out.data_ptr(), lse.data_ptr(), stream)
     _check(rc, "mla_decode_fwd")

@@ -95,8 +95,17 @@ struct Params {
   float* oacc;                 // [slots, R, 512] normalised partial O
   float* lacc;                 // [slots, R] partial lse, base 2
   int batch, R, h_q, s_q, max_blocks, num_parts, row_groups;
+  int causal;                  // 1: query token s of s_q sees keys 0 .. L - s_q + s
   float scale_log2;            // softmax_scale * log2(e)
 };
+
+// Keys query row `row` (= s * h_q + h) sees in a request of length L: all L,
+// or with the causal mask of multi-token prediction the first
+// L - (s_q - 1 - s) (the s_q query tokens are the sequence's last positions;
+// the pages' is_causal flag).  May be <= 0.
+__device__ __forceinline__ int row_keys(const Params& p, int L, int row) {
+  return p.causal ? L - (p.s_q - 1 - row / p.h_q) : L;
+}
 
 constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0), expcnt and lgkmcnt not waited
 
@@ -205,8 +214,8 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[kQkSteps], const Params& p, 
 // Softmax of one 16-row S^T tile against the wave's fixed reference (base 2).
 // sv: this lane's 4 scores (tokens 4 g .. + 3 of its row); returns the bf16
 // probabilities and adds them (fp32) to l.
-__device__ __forceinline__ i16x4 probabilities(f32x4 sv, int g, int valid, float scale_log2, bool& have_ref,
-                                               float& m_ref, float& m_seen, float& l) {
+__device__ __forceinline__ i16x4 probabilities(f32x4 sv, int g, int valid, float scale_log2, float& m_ref,
+                                               float& m_seen, float& l) {
   float x[4];
   float mloc = -INFINITY;
 #pragma unroll
@@ -217,7 +226,7 @@ __device__ __forceinline__ i16x4 probabilities(f32x4 sv, int g, int valid, float
   }
   mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
   mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-  if (!have_ref) m_ref = mloc;
+  if (m_ref == -INFINITY) m_ref = mloc;   // the first tile with a visible key sets the reference
   m_seen = fmaxf(m_seen, mloc);
   i16x4 pb;
 #pragma unroll
@@ -418,7 +427,6 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
 
     f32x4 o[8];
     float m_ref = -INFINITY, l_run = 0.f;
-    bool have_ref = false;
     // Q^T fragments (B operand): row c16, dims 32 ks + 8 g .. + 7.  Q is
     // copied into this wave's slice of stage 1 ahead of the first page, read
     // into registers as soon as it lands, and that slice then takes the
@@ -484,25 +492,29 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
         const f32x4 sv = sacc[0] + sacc[1] + sacc[2];
 
         // ---- softmax against the common reference (base 2).
+        const int vis = row_keys(p, L, c16) - j * kPage;   // keys of this page row c16 sees (may be <= 0 or > 64)
         float x[4], mloc = -INFINITY;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           // (softmax_scale >= 0, so masking before or after scaling is the same.)
-          x[v] = tok0 + 4 * g + v < valid ? sv[v] * p.scale_log2 : -INFINITY;
+          x[v] = tok0 + 4 * g + v < vis ? sv[v] * p.scale_log2 : -INFINITY;
           mloc = fmaxf(mloc, x[v]);
         }
         mloc = row_max4(mloc);   // this wave's tokens of row c16
-        if (!have_ref) {   // first page of the first attempt: the whole page's row max
+        // A row's reference is the whole page's row max of the first page in
+        // which it sees a key, the same in every wave (exchanged through LDS).
+        // m_ref is equal across waves, so the vote is uniform.
+        if (__any(m_ref == -INFINITY)) {
           if (g == 0) red[wave][c16] = mloc;
           lds_barrier();
-          m_ref = fmaxf(fmaxf(red[0][c16], red[1][c16]), fmaxf(red[2][c16], red[3][c16]));
-          have_ref = true;
+          if (m_ref == -INFINITY) m_ref = fmaxf(fmaxf(red[0][c16], red[1][c16]), fmaxf(red[2][c16], red[3][c16]));
         }
         m_seen = fmaxf(m_seen, mloc);
+        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;   // no key seen yet: every x is -inf
         i16x4 pk;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float pe = __builtin_amdgcn_exp2f(x[v] - m_ref);   // masked tokens: exp2(-inf) = 0
+          const float pe = __builtin_amdgcn_exp2f(x[v] - m_use);   // masked tokens: exp2(-inf) = 0
           l_run += pe;   // row sum from the fp32 values; only the PV operand is bf16
           pk[v] = __builtin_bit_cast(short, (__bf16)pe);
         }
@@ -644,7 +656,6 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_kernel(Params p) {
 
     f32x16 o[kDv / 32];
     float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-    bool have_ref = false;
     for (int attempt = 0;; ++attempt) {
       if (lo < hi) issue_stage<false>(rows_of(lo), wlds0, dma_off);
       bf16x8 qf[2][kQkSteps];
@@ -713,8 +724,8 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_kernel(Params p) {
         i16x4 pb[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-          pb[t] = probabilities(sacc[t], g, valid, p.scale_log2, have_ref, m_ref[t], m_seen[t], l_run[t]);
-        have_ref = true;   // the first page of the first attempt set the references
+          pb[t] = probabilities(sacc[t], g, row_keys(p, L, row0 + 16 * t + c16) - j * kPage - tok0, p.scale_log2,
+                                m_ref[t], m_seen[t], l_run[t]);
 
         // ---- P^T as the 32x32x16 B operand: lane 32 h + n needs tokens
         // 8 h .. 8 h + 7 of row n.  Half t = n / 16 holds them in lanes
@@ -923,7 +934,6 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
 
     f32x16 o[kWideTiles][4];   // O^T tiles: row tile x this wave's 4 column tiles
     float m_ref = -INFINITY, l_run = 0.f;
-    bool have_ref = false;
     for (int attempt = 0;; ++attempt) {
       if (lo < hi) issue_stage<kStream>(rows_of(lo), lds0 + wave * kStageBytes, dma_off);
       // Q^T fragments (B operand): row r, dims 16 ks + 8 h .. + 7.
@@ -976,14 +986,18 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
         // work and exp2 latency hide under the matrix cores.
         bool bad = false, flag = false;
         WideSoftmax sm[2];
-        const int lim = valid - 4 * h;   // element v of a tile is a real token iff its offset is below this
+        // Element v of a tile is a key this lane's row sees iff its offset is
+        // below lim; a tile is ragged (masking needed) for this workgroup if
+        // it is for the row that sees the fewest keys.
+        const int lim = row_keys(p, L, r) - j * kPage - 4 * h;
+        const int vis_min = (p.causal ? L - (p.s_q - 1) : L) - j * kPage;
         // One piece of tile tt's softmax (see WideSoftmax); k is a constant
         // after unrolling.  The scores are read from the accumulator as they
         // are needed; tokens past the end of the sequence (last page only)
         // are masked in both passes.
         auto softmax_piece = [&](int tt, int k, const f32x16& sacc) {
           WideSoftmax& t = sm[tt];
-          const bool ragged = valid < 32 * tt + 32;   // uniform
+          const bool ragged = vis_min < 32 * tt + 32;   // uniform
           // Element v of the tile is a real token.  Only evaluated inside the
           // ragged branches: `lim_in` is re-materialised there so that the
           // compares cannot be hoisted onto the full-tile path.
@@ -1018,8 +1032,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t.mloc), __float_as_uint(t.mloc), false, false);
             t.mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2;
           } else if (k == 3) {
-            if (!have_ref) m_ref = t.mloc;   // first tile of the first page of the first attempt
-            have_ref = true;
+            if (m_ref == -INFINITY) m_ref = t.mloc;   // the first tile in which the row sees a key
             m_seen = fmaxf(m_seen, t.mloc);
             bad |= t.mloc > m_ref + kRefHeadroom;
             if (tt == 1) flag = attempt == 0 && __any(bad);   // wave-wide vote, outside any branch
@@ -1437,7 +1450,7 @@ constexpr int kCombineMaxGrid = 2048;   // about one round of resident workgroup
 
 extern "C" int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* block_table,
                               const int32_t* cache_seqlens, int batch, int s_q, int h_q, int num_blocks,
-                              int max_blocks_per_seq, float softmax_scale, const int32_t* sched,
+                              int max_blocks_per_seq, float softmax_scale, int causal, const int32_t* sched,
                               int num_parts, const int32_t* num_splits, void* workspace,
                               size_t workspace_bytes, void* out, float* lse, void* stream) {
   if (!q || !kv_cache || !block_table || !cache_seqlens || !sched || !num_splits || !out || !lse)
@@ -1448,6 +1461,7 @@ extern "C" int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t
                      batch, s_q, h_q, num_blocks, max_blocks_per_seq, num_parts);
   if (!std::isfinite(softmax_scale) || softmax_scale < 0.f)
     return set_error(MLA_ERR_INVALID, "mla_decode_fwd: softmax_scale must be finite and >= 0");
+  if (causal != 0 && causal != 1) return set_error(MLA_ERR_INVALID, "mla_decode_fwd: causal must be 0 or 1");
   const Geometry g = geometry(h_q, s_q);
   const int slots = num_parts + batch - 1;
   const size_t need = mla_workspace_bytes(slots, h_q, s_q);
@@ -1473,6 +1487,7 @@ extern "C" int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t
   prm.max_blocks = max_blocks_per_seq;
   prm.num_parts = num_parts;
   prm.row_groups = g.row_groups;
+  prm.causal = causal;
   prm.scale_log2 = softmax_scale * kLog2e;
 
   hipStream_t st = (hipStream_t)stream;

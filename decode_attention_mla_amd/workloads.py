@@ -164,19 +164,22 @@ def config_inputs(index: int) -> MlaInputs:
                        c["max_blocks"], seed=index, name=c["name"])
 
 
-def algorithmic_work(seqlens, s_q: int, h_q: int) -> tuple[float, float]:
+def algorithmic_work(seqlens, s_q: int, h_q: int, causal: bool = False) -> tuple[float, float]:
     """(FLOPs, bytes) the method must do for one decode call.
 
-    FLOPs = 2 * s_q * h_q * sum(L) * (576 + 512): the QK^T and PV products.
-    Bytes = bf16 KV read once per request, q read, out written (bf16), lse
-    written (fp32).  Masked tail tokens, split partials and the block table
-    are overhead and are not counted.
+    FLOPs = 2 * h_q * sum over (request, query token) of the keys it sees *
+    (576 + 512): the QK^T and PV products (all L keys, or with the causal
+    mask L - (s_q - 1 - s) for query token s).  Bytes = bf16 KV read once per
+    request, q read, out written (bf16), lse written (fp32).  Masked tail
+    tokens, split partials and the block table are overhead and are not
+    counted.
     """
     sl = np.asarray(seqlens, dtype=np.int64)
     R = s_q * h_q
     total = int(sl.sum())
     b = int(sl.shape[0])
-    flops = 2.0 * R * total * (D_QK + D_V)
+    seen = s_q * total if not causal else int(sum(np.maximum(sl - (s_q - 1 - s), 0).sum() for s in range(s_q)))
+    flops = 2.0 * h_q * seen * (D_QK + D_V)
     nbytes = 2.0 * (total * D_QK + b * R * D_QK + b * R * D_V) + 4.0 * b * R
     return flops, nbytes
 

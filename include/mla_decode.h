@@ -125,6 +125,12 @@ size_t mla_workspace_bytes(int total_splits, int h_q, int s_q);
  *   cache_seqlens device int32 [batch]; must equal the lengths the plan was
  *                 made from, and L <= 64 * max_blocks_per_seq
  *   softmax_scale multiplies the q.k scores; finite and >= 0
+ *   causal        0: every query token sees all L keys (the dense path);
+ *                 1: the s_q query tokens are the last s_q positions of the
+ *                 sequence (multi-token prediction), so token s sees keys
+ *                 0 .. L - s_q + s (the pages' is_causal flag, "FlashMLA
+ *                 new-kernel deep dive", API section); a token that sees no
+ *                 key gets out = 0, lse = -inf
  *   sched         device int32 [num_parts, 8] from mla_get_metadata/mla_plan
  *   num_splits    device int32 [batch + 1] from the same plan
  *   workspace     device, >= mla_workspace_bytes(num_parts + batch - 1, h_q, s_q)
@@ -143,7 +149,7 @@ size_t mla_workspace_bytes(int total_splits, int h_q, int s_q);
  */
 int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* block_table,
                    const int32_t* cache_seqlens, int batch, int s_q, int h_q, int num_blocks,
-                   int max_blocks_per_seq, float softmax_scale, const int32_t* sched,
+                   int max_blocks_per_seq, float softmax_scale, int causal, const int32_t* sched,
                    int num_parts, const int32_t* num_splits, void* workspace,
                    size_t workspace_bytes, void* out, float* lse, void* stream);
 

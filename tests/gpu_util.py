@@ -19,7 +19,7 @@ def to_device(inp, kv_override=None):
                 sl=torch.from_numpy(inp.cache_seqlens).to(dev))
 
 
-def run_gpu(inp, force_splits=0, num_cus=0, dev_inputs=None, repeat=1):
+def run_gpu(inp, force_splits=0, num_cus=0, dev_inputs=None, repeat=1, causal=False):
     import torch
     import decode_attention_mla_amd as mla
     d = dev_inputs or to_device(inp)
@@ -27,7 +27,8 @@ def run_gpu(inp, force_splits=0, num_cus=0, dev_inputs=None, repeat=1):
                                      force_splits=force_splits)
     out = lse = None
     for _ in range(repeat):
-        out, lse = mla.mla_decode_fwd(d["q"], d["kv"], d["bt"], d["sl"], inp.softmax_scale, sched, ns)
+        out, lse = mla.mla_decode_fwd(d["q"], d["kv"], d["bt"], d["sl"], inp.softmax_scale, sched, ns,
+                                      causal=causal)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 

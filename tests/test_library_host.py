@@ -95,15 +95,18 @@ def test_plan_errors():
 
 def test_decode_argument_errors_return_codes_without_launching():
     L = mla.lib()
-    rc = L.mla_decode_fwd(None, None, None, None, 1, 1, 16, 1, 1, 0.1, None, 1, None, None, 0, None, None, None)
+    rc = L.mla_decode_fwd(None, None, None, None, 1, 1, 16, 1, 1, 0.1, 0, None, 1, None, None, 0, None, None, None)
     assert rc == -1 and b"null" in L.mla_last_error()
     dummy = ctypes.c_void_p(16)   # never dereferenced: every check fails before any launch
-    rc = L.mla_decode_fwd(dummy, dummy, dummy, dummy, 0, 1, 16, 1, 1, 0.1, dummy, 1, dummy, dummy, 0,
+    rc = L.mla_decode_fwd(dummy, dummy, dummy, dummy, 0, 1, 16, 1, 1, 0.1, 0, dummy, 1, dummy, dummy, 0,
                           dummy, dummy, None)
     assert rc == -1 and b"batch=0" in L.mla_last_error()
-    rc = L.mla_decode_fwd(dummy, dummy, dummy, dummy, 2, 1, 16, 8, 4, float("nan"), dummy, 3, dummy, dummy, 0,
+    rc = L.mla_decode_fwd(dummy, dummy, dummy, dummy, 2, 1, 16, 8, 4, float("nan"), 0, dummy, 3, dummy, dummy, 0,
                           dummy, dummy, None)
     assert rc == -1 and b"softmax_scale" in L.mla_last_error()
-    rc = L.mla_decode_fwd(dummy, dummy, dummy, dummy, 2, 1, 16, 8, 4, 0.1, dummy, 3, dummy, dummy, 100,
+    rc = L.mla_decode_fwd(dummy, dummy, dummy, dummy, 2, 1, 16, 8, 4, 0.1, 2, dummy, 3, dummy, dummy, 0,
+                          dummy, dummy, None)
+    assert rc == -1 and b"causal" in L.mla_last_error()
+    rc = L.mla_decode_fwd(dummy, dummy, dummy, dummy, 2, 1, 16, 8, 4, 0.1, 0, dummy, 3, dummy, dummy, 100,
                           dummy, dummy, None)
     assert rc == -3 and b"workspace" in L.mla_last_error()
