@@ -995,7 +995,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
         // after unrolling.  The scores are read from the accumulator as they
         // are needed; tokens past the end of the sequence (last page only)
         // are masked in both passes.
-        auto softmax_piece = [&](int tt, int k, const f32x16& sacc) {
+        auto softmax_piece = [&](int tt, int k, f32x16& sacc) {
           WideSoftmax& t = sm[tt];
           const bool ragged = vis_min < 32 * tt + 32;   // uniform
           // Element v of the tile is a real token.  Only evaluated inside the
@@ -1011,14 +1011,17 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
             // Partial maxima (five independent max3s).
             if (ragged) {
               // A real branch (the statement cannot be speculated): full
-              // tiles must not pay for the masking selects.
+              // tiles must not pay for the masking selects.  Masked scores
+              // become -inf in place; the exponent arguments below are
+              // clamped with max(., -inf), which turns the NaN of
+              // -inf * 0 (softmax_scale = 0) or -inf + inf (a row with no
+              // key seen yet) into -inf, so exp2 gives 0 there.
               const int l2 = branch_lim();
-              float x[16];
 #pragma unroll
-              for (int v = 0; v < 16; ++v) x[v] = ok(v, l2) ? sacc[v] : -INFINITY;
+              for (int v = 0; v < 16; ++v) sacc[v] = ok(v, l2) ? sacc[v] : -INFINITY;
 #pragma unroll
-              for (int i = 0; i < 5; ++i) t.mp[i] = fmaxf(fmaxf(x[3 * i], x[3 * i + 1]), x[3 * i + 2]);
-              t.mp[5] = x[15];
+              for (int i = 0; i < 5; ++i) t.mp[i] = fmaxf(fmaxf(sacc[3 * i], sacc[3 * i + 1]), sacc[3 * i + 2]);
+              t.mp[5] = sacc[15];
             } else {
 #pragma unroll
               for (int i = 0; i < 5; ++i) t.mp[i] = fmaxf(fmaxf(sacc[3 * i], sacc[3 * i + 1]), sacc[3 * i + 2]);
@@ -1042,12 +1045,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
             // k - 4, exp2 of pair k - 5, row sum and bf16 pack of pair k - 6.
             const int pa = k - 4, pe = k - 5, pc = k - 6;
             if (pc >= 0 && pc < 8) {
-              float p0 = t.ex[2 * pc], p1 = t.ex[2 * pc + 1];
-              if (ragged) {
-                const int l2 = branch_lim();   // a real branch, as above
-                p0 = ok(2 * pc, l2) ? p0 : 0.f;
-                p1 = ok(2 * pc + 1, l2) ? p1 : 0.f;
-              }
+              const float p0 = t.ex[2 * pc], p1 = t.ex[2 * pc + 1];
               l_part[pc & 3] += p0 + p1;   // four independent partial row sums
               asm volatile("" : "+v"(l_part[pc & 3]));   // keeps the add here (not sunk to the loop end)
               t.pk[pc >> 2][pc & 3] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)p0, (__bf16)p1});
@@ -1057,8 +1055,8 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
               t.ex[2 * pe + 1] = __builtin_amdgcn_exp2f(t.ex[2 * pe + 1]);
             }
             if (pa >= 0 && pa < 8) {
-              t.ex[2 * pa] = __builtin_fmaf(sacc[2 * pa], p.scale_log2, -m_ref);
-              t.ex[2 * pa + 1] = __builtin_fmaf(sacc[2 * pa + 1], p.scale_log2, -m_ref);
+              t.ex[2 * pa] = fmaxf(__builtin_fmaf(sacc[2 * pa], p.scale_log2, -m_ref), -INFINITY);
+              t.ex[2 * pa + 1] = fmaxf(__builtin_fmaf(sacc[2 * pa + 1], p.scale_log2, -m_ref), -INFINITY);
             }
             if (pc == 3 || pc == 7) {   // an 8-token half is complete: to LDS as a PV B fragment
               const int half = pc >> 2;
