@@ -108,6 +108,16 @@ def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6
     plan_us = (time.perf_counter() - t) / reps * 1e6
     sched = torch.from_numpy(sched_np).to(dev)
     ns = torch.from_numpy(ns_np).to(dev)
+    # The same plan on the GPU (device lengths; capturable with the decode).
+    for _ in range(3):
+        mla.get_mla_metadata_device(sl, inp.h_q, inp.s_q)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        mla.get_mla_metadata_device(sl, inp.h_q, inp.s_q)
+    e1.record()
+    torch.cuda.synchronize()
+    plan_device_us = e0.elapsed_time(e1) / reps * 1e3
     b = inp.batch
     out = torch.empty((b, inp.s_q, inp.h_q, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((b, inp.h_q, inp.s_q), dtype=torch.float32, device=dev)
@@ -173,7 +183,7 @@ def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6
         sum_seqlen=int(inp.cache_seqlens.sum()),
         parts=int(sched.shape[0]), total_splits=int(total), rotating_copies=rot, graph_steps=graph_steps,
         flops=flops, bytes=nbytes, ms_per_step=ms_per_step, eager_ms_per_step=eager_ms,
-        main_kernel_ms=main_avg, combine_kernel_ms=comb_avg, plan_us=plan_us,
+        main_kernel_ms=main_avg, combine_kernel_ms=comb_avg, plan_us=plan_us, plan_device_us=plan_device_us,
         tflops=flops / (ms_per_step * 1e-3) / 1e12, gbs=nbytes / (ms_per_step * 1e-3) / 1e9,
         main_kernel_tflops=flops / (main_avg * 1e-3) / 1e12, main_kernel_gbs=nbytes / (main_avg * 1e-3) / 1e9,
     )
@@ -258,7 +268,8 @@ def main():
                 gbs=r["gbs"], frac_hbm_peak=r["gbs"] / HBM_PEAK_GBS, ms_per_step=r["ms_per_step"],
                 eager_ms_per_step=r["eager_ms_per_step"], main_kernel_tflops=r["main_kernel_tflops"],
                 main_kernel_ms=r["main_kernel_ms"], combine_kernel_ms=r["combine_kernel_ms"],
-                parts=r["parts"], total_splits=r["total_splits"], plan_us=r["plan_us"])
+                parts=r["parts"], total_splits=r["total_splits"], plan_us=r["plan_us"],
+                plan_device_us=r["plan_device_us"])
 
     line = dict(
         metric=METRIC, value=value, unit=unit, n_gpus=1, steps=args.steps, warmup=args.warmup,
@@ -271,6 +282,7 @@ def main():
         detail=dict(timing="graph replay", eager_ms_per_step=head["eager_ms_per_step"],
                     graph_steps=head["graph_steps"], main_kernel_ms=head["main_kernel_ms"],
                     combine_kernel_ms=head["combine_kernel_ms"], plan_us=head["plan_us"],
+                    plan_device_us=head["plan_device_us"],
                     algorithmic_bytes=head["bytes"], algorithmic_flops=head["flops"],
                     kernel_sha256_16=kernel_hash()),
         extra=extra,

@@ -20,7 +20,7 @@ D_QK = 576
 D_V = 512
 
 # Every symbol include/mla_decode.h declares.
-EXPORTED = ("mla_plan", "mla_get_metadata", "mla_max_parts", "mla_workspace_bytes",
+EXPORTED = ("mla_plan", "mla_get_metadata", "mla_get_metadata_device", "mla_max_parts", "mla_workspace_bytes",
             "mla_decode_fwd", "mla_profile_start", "mla_profile_stop", "mla_last_error")
 
 _lib = None
@@ -52,6 +52,9 @@ def lib() -> ctypes.CDLL:
     L.mla_max_parts.restype = ctypes.c_int
     L.mla_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     L.mla_workspace_bytes.restype = ctypes.c_size_t
+    L.mla_get_metadata_device.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
+                                          ctypes.c_int, vp, ip, vp]
+    L.mla_get_metadata_device.restype = ctypes.c_int
     L.mla_decode_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int, ctypes.c_float, ctypes.c_int, vp, ctypes.c_int, vp, vp,
                                  ctypes.c_size_t, vp, vp, vp]
@@ -129,6 +132,29 @@ def get_mla_metadata(cache_seqlens, h_q: int, s_q: int, num_cus: int = 0, force_
     dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
     return (torch.from_numpy(sched).to(dev, non_blocking=False),
             torch.from_numpy(ns).to(dev, non_blocking=False))
+
+
+def get_mla_metadata_device(cache_seqlens, h_q: int, s_q: int, num_cus: int = 0):
+    """The split plan computed on the GPU from device lengths (int32 [b]),
+    enqueued on the current stream: returns (sched int32 [P, 8],
+    num_splits int32 [b + 1]) device tensors, P = the policy's part count
+    (rows past the walk's last part are empty).  Capturable in a graph."""
+    import torch
+    _need(cache_seqlens.dim() == 1 and cache_seqlens.dtype == torch.int32 and cache_seqlens.is_cuda
+          and cache_seqlens.is_contiguous(), "cache_seqlens must be a contiguous int32 [b] GPU tensor")
+    b = int(cache_seqlens.shape[0])
+    dummy = np.zeros(b, dtype=np.int32)   # the part count depends on sizes only
+    cap = lib().mla_max_parts(_ptr(dummy), b, int(h_q), int(s_q), int(num_cus), 0)
+    _check(cap if cap < 0 else 0, "mla_max_parts")
+    dev = cache_seqlens.device
+    sched = torch.empty((cap, SCHED_INTS), dtype=torch.int32, device=dev)
+    ns = torch.empty(b + 1, dtype=torch.int32, device=dev)
+    parts = ctypes.c_int(0)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(lib().mla_get_metadata_device(cache_seqlens.data_ptr(), b, int(h_q), int(s_q), int(num_cus),
+                                         sched.data_ptr(), cap, ns.data_ptr(), ctypes.byref(parts), stream),
+           "mla_get_metadata_device")
+    return sched[:parts.value], ns
 
 
 def mla_workspace_bytes(total_splits: int, h_q: int, s_q: int) -> int:

@@ -1314,6 +1314,91 @@ __global__ void __launch_bounds__(kCombineWaves * 64) mla_combine_kernel(Params 
   }
 }
 
+// ---------------------------------------------------------------------------
+// The split planner on the GPU ("FlashMLA new-kernel deep dive", Tile
+// Scheduler: the pages run their planner as a one-warp kernel), so that a
+// captured decode step can replan from lengths that change on the device.
+// It takes the same greedy walk as the host planner (planner.cpp), with the
+// same payload rule, and writes the same table: rows for the parts the walk
+// fills, then empty rows (begin_req = 1 > end_req = 0, which every split-KV
+// kernel skips) up to num_parts, column 5 = the largest piece count in every
+// row, and the per-request prefix of pieces.
+//   One wave: block counts are loaded 64 requests at a time into a register
+// (lane i holds request 64 c + i) and read with v_readlane by the walk,
+// whose state is wave-uniform (scalar arithmetic); lane 0 stores.
+constexpr int kPlanMaxBatch = 1 << 16;
+
+__global__ void __launch_bounds__(64) mla_plan_kernel(const int32_t* seqlens, int batch, int num_parts, int F,
+                                                    int32_t* sched, int32_t* num_splits) {
+  const int lane = threadIdx.x;
+  auto blocks_of = [](int L) { return L > 0 ? (L + kPage - 1) / kPage : 0; };   // negative lengths count as 0
+  // total = sum (n_b + F); payload = ceil(total / parts) + F
+  long long part_sum = 0;
+  for (int b = lane; b < batch; b += 64) part_sum += blocks_of(seqlens[b]) + F;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) part_sum += __shfl_xor(part_sum, off);
+  const long long total = __builtin_amdgcn_readfirstlane((int)(part_sum & 0xffffffff)) |
+                          ((long long)__builtin_amdgcn_readfirstlane((int)(part_sum >> 32)) << 32);
+  const long long payload = (total + num_parts - 1) / num_parts + F;
+
+  int chunk = -1, nv = 0;   // block counts of requests 64 chunk .. + 63 (lane i: request 64 chunk + i)
+  auto n_of = [&](int req) {
+    const int c = req >> 6;
+    if (c != chunk) {
+      chunk = c;
+      const int b = 64 * c + lane;
+      nv = b < batch ? blocks_of(seqlens[b]) : 0;
+    }
+    return __builtin_amdgcn_readlane(nv, req & 63);
+  };
+
+  int req = 0, blk = 0, cur = 0, acc = 0, max_pieces = 0, np = 0;
+  if (lane == 0) num_splits[0] = 0;
+  for (int p = 0; p < num_parts && req < batch; ++p) {
+    const bool last_part = p == num_parts - 1;
+    long long cap = payload;
+    const int br = req, bb = blk, bp = cur;
+    int er = -1, eb = -1;
+    while (req < batch) {
+      const int n = n_of(req);
+      const long long rem = n - blk;
+      if (last_part || rem + F <= cap) {   // the rest of this request fits
+        cap -= rem + F;
+        ++cur;
+        er = req;
+        eb = n;
+        acc += cur;
+        max_pieces = max(max_pieces, cur);
+        if (lane == 0) num_splits[req + 1] = acc;
+        ++req;
+        blk = 0;
+        cur = 0;
+        continue;
+      }
+      const long long take = cap - F;
+      if (take > 0) {                     // cut the request at a block boundary
+        blk += (int)take;
+        ++cur;
+        er = req;
+        eb = blk;
+      }
+      break;
+    }
+    if (er < 0) continue;
+    if (lane == 0) {
+      int32_t* row = sched + (size_t)np * MLA_SCHED_INTS;
+      row[0] = br; row[1] = er; row[2] = bb; row[3] = eb; row[4] = bp;
+      row[6] = row[7] = 0;
+    }
+    ++np;
+  }
+  for (int r = np + lane; r < num_parts; r += 64) {   // empty rows: no request
+    int32_t* row = sched + (size_t)r * MLA_SCHED_INTS;
+    row[0] = 1; row[1] = 0; row[2] = row[3] = row[4] = row[6] = row[7] = 0;
+  }
+  for (int r = lane; r < num_parts; r += 64) sched[(size_t)r * MLA_SCHED_INTS + 5] = max_pieces;
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
@@ -1377,6 +1462,26 @@ extern "C" int mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q
   rc = plan(cache_seqlens, batch, parts, F, force_splits, sched_out, max_parts, num_splits_out, num_parts_out);
   if (rc) return rc;
   *total_splits_out = num_splits_out[batch];
+  return MLA_OK;
+}
+
+extern "C" int mla_get_metadata_device(const int32_t* cache_seqlens_dev, int batch, int h_q, int s_q, int num_cus,
+                                       int32_t* sched_dev, int max_parts, int32_t* num_splits_dev,
+                                       int* num_parts_out, void* stream) {
+  if (!sched_dev || !num_splits_dev || !num_parts_out)
+    return set_error(MLA_ERR_INVALID, "mla_get_metadata_device: null pointer argument");
+  if (batch > kPlanMaxBatch)
+    return set_error(MLA_ERR_INVALID, "mla_get_metadata_device: batch=%d > %d", batch, kPlanMaxBatch);
+  int parts, F;
+  int rc = policy(cache_seqlens_dev, batch, h_q, s_q, &num_cus, &parts, &F);
+  if (rc) return rc;
+  if (max_parts < parts)
+    return set_error(MLA_ERR_CAPACITY, "mla_get_metadata_device: max_parts=%d < %d parts", max_parts, parts);
+  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, cache_seqlens_dev, batch, parts, F,
+                     sched_dev, num_splits_dev);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(MLA_ERR_HIP, "mla_get_metadata_device: launch: %s", hipGetErrorString(e));
+  *num_parts_out = parts;
   return MLA_OK;
 }
 

@@ -98,6 +98,33 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q, int s_q, 
                      int force_splits, int32_t* sched_out, int max_parts,
                      int32_t* num_splits_out, int* num_parts_out, int* total_splits_out);
 
+/*
+ * mla_get_metadata_device — the same plan as mla_get_metadata (greedy walk,
+ * no force_splits) computed on the GPU from device lengths, enqueued on
+ * `stream` (the pages run their tile scheduler as a one-warp kernel,
+ * "FlashMLA new-kernel deep dive", Tile Scheduler), so that a captured
+ * decode step (planner + mla_decode_fwd) replans whenever the lengths in
+ * device memory change, with no host round trip.
+ *
+ *   cache_seqlens_dev device int32 [batch] (read when the kernel runs;
+ *                     negative lengths count as 0)
+ *   num_cus           CUs to fill; 0 = query the current HIP device
+ *   sched_dev         device int32 [max_parts * 8]; max_parts >= the policy's
+ *                     part count (mla_max_parts(..., force_splits = 0))
+ *   num_splits_dev    device int32 [batch + 1]
+ *   num_parts_out     host: the rows written = the policy's part count, the
+ *                     num_parts to pass to mla_decode_fwd; rows after the
+ *                     walk's last part are empty (begin_req 1 > end_req 0)
+ *   stream            hipStream_t (NULL = the null stream)
+ * A plan's partial slots never exceed num_parts + batch - 1, so a workspace of
+ * mla_workspace_bytes(num_parts + batch - 1, h_q, s_q) fits any lengths.
+ * Allocates nothing, does not synchronise; batch <= 65536.
+ * Errors: MLA_ERR_INVALID, MLA_ERR_CAPACITY, MLA_ERR_HIP.
+ */
+int mla_get_metadata_device(const int32_t* cache_seqlens_dev, int batch, int h_q, int s_q, int num_cus,
+                            int32_t* sched_dev, int max_parts, int32_t* num_splits_dev,
+                            int* num_parts_out, void* stream);
+
 /* Upper bound on the parts mla_get_metadata can emit for these sizes. */
 int mla_max_parts(const int32_t* cache_seqlens, int batch, int h_q, int s_q, int num_cus,
                   int force_splits);
