@@ -108,16 +108,24 @@ def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6
     plan_us = (time.perf_counter() - t) / reps * 1e6
     sched = torch.from_numpy(sched_np).to(dev)
     ns = torch.from_numpy(ns_np).to(dev)
-    # The same plan on the GPU (device lengths; capturable with the decode).
-    for _ in range(3):
-        mla.get_mla_metadata_device(sl, inp.h_q, inp.s_q)
+    # The same plan on the GPU (device lengths; capturable with the decode),
+    # timed as graph replays of 20 planner launches (no host launch cost).
+    mla.get_mla_metadata_device(sl, inp.h_q, inp.s_q)
+    torch.cuda.synchronize()
+    plan_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(plan_graph):
+        for _ in range(20):
+            mla.get_mla_metadata_device(sl, inp.h_q, inp.s_q)
+    plan_graph.replay()
+    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(reps):
-        mla.get_mla_metadata_device(sl, inp.h_q, inp.s_q)
+    for _ in range(5):
+        plan_graph.replay()
     e1.record()
     torch.cuda.synchronize()
-    plan_device_us = e0.elapsed_time(e1) / reps * 1e3
+    plan_device_us = e0.elapsed_time(e1) / 100 * 1e3
+    del plan_graph
     b = inp.batch
     out = torch.empty((b, inp.s_q, inp.h_q, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((b, inp.h_q, inp.s_q), dtype=torch.float32, device=dev)

@@ -1318,18 +1318,31 @@ __global__ void __launch_bounds__(kCombineWaves * 64) mla_combine_kernel(Params 
 // The split planner on the GPU ("FlashMLA new-kernel deep dive", Tile
 // Scheduler: the pages run their planner as a one-warp kernel), so that a
 // captured decode step can replan from lengths that change on the device.
-// It takes the same greedy walk as the host planner (planner.cpp), with the
-// same payload rule, and writes the same table: rows for the parts the walk
-// fills, then empty rows (begin_req = 1 > end_req = 0, which every split-KV
-// kernel skips) up to num_parts, column 5 = the largest piece count in every
-// row, and the per-request prefix of pieces.
-//   One wave: block counts are loaded 64 requests at a time into a register
-// (lane i holds request 64 c + i) and read with v_readlane by the walk,
-// whose state is wave-uniform (scalar arithmetic); lane 0 stores.
+// It produces the host planner's table (planner.cpp: same payload rule, same
+// greedy walk), then empty rows (begin_req = 1 > end_req = 0, which every
+// split-KV kernel skips) up to num_parts, column 5 = the largest piece count
+// in every row, and the per-request prefix of pieces.
+//   The walk is not stepped part by part.  One wave holds 64 requests at a
+// time; a ballot over the in-chunk prefix of costs (n_b + F) places the whole
+// run of requests that fit in the capacity left, and a request that does not
+// fit is settled in O(1): its first piece takes what the part has left beyond
+// F (or the part closes if that is nothing), every fresh part after it is
+// filled with payload - F of its blocks, k = (rem - 1) / (payload - F) times,
+// and its last piece opens the part the walk continues in.  Each fresh part
+// records where it begins (request, block, piece index) in LDS; a part ends
+// where the next one begins, so the rows are then written one lane per part.
 constexpr int kPlanMaxBatch = 1 << 16;
+constexpr int kPlanMaxParts = 4096;
+
+__device__ __forceinline__ long long readlane64(long long v, int lane) {
+  const int lo = __builtin_amdgcn_readlane((int)(v & 0xffffffff), lane);
+  const int hi = __builtin_amdgcn_readlane((int)(v >> 32), lane);
+  return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
 
 __global__ void __launch_bounds__(64) mla_plan_kernel(const int32_t* seqlens, int batch, int num_parts, int F,
                                                     int32_t* sched, int32_t* num_splits) {
+  __shared__ int pb_req[kPlanMaxParts], pb_blk[kPlanMaxParts], pb_piece[kPlanMaxParts];
   const int lane = threadIdx.x;
   auto blocks_of = [](int L) { return L > 0 ? (L + kPage - 1) / kPage : 0; };   // negative lengths count as 0
   // total = sum (n_b + F); payload = ceil(total / parts) + F
@@ -1337,66 +1350,92 @@ __global__ void __launch_bounds__(64) mla_plan_kernel(const int32_t* seqlens, in
   for (int b = lane; b < batch; b += 64) part_sum += blocks_of(seqlens[b]) + F;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) part_sum += __shfl_xor(part_sum, off);
-  const long long total = __builtin_amdgcn_readfirstlane((int)(part_sum & 0xffffffff)) |
-                          ((long long)__builtin_amdgcn_readfirstlane((int)(part_sum >> 32)) << 32);
-  const long long payload = (total + num_parts - 1) / num_parts + F;
+  const long long total = readlane64(part_sum, 0);
+  const long long P = (total + num_parts - 1) / num_parts + F;
+  const long long D = P - F;    // blocks a piece may take in a part of its own
+  const int last = num_parts - 1;
 
-  int chunk = -1, nv = 0;   // block counts of requests 64 chunk .. + 63 (lane i: request 64 chunk + i)
-  auto n_of = [&](int req) {
-    const int c = req >> 6;
-    if (c != chunk) {
-      chunk = c;
-      const int b = 64 * c + lane;
-      nv = b < batch ? blocks_of(seqlens[b]) : 0;
+  int p = 0;                    // the part the walk is in
+  long long cap = P;            // capacity left in part p
+  int acc = 0, max_pieces = 1;  // pieces of the requests before this chunk; largest piece count
+  if (lane == 0) {
+    pb_req[0] = pb_blk[0] = pb_piece[0] = 0;
+    num_splits[0] = 0;
+  }
+  for (int base = 0; base < batch; base += 64) {
+    const int cnt = min(64, batch - base);
+    const int n = lane < cnt ? blocks_of(seqlens[base + lane]) : 0;
+    long long z = (long long)n + F;   // inclusive prefix of costs in the chunk
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long t = __shfl_up(z, off);
+      if (lane >= off) z += t;
     }
-    return __builtin_amdgcn_readlane(nv, req & 63);
-  };
-
-  int req = 0, blk = 0, cur = 0, acc = 0, max_pieces = 0, np = 0;
-  if (lane == 0) num_splits[0] = 0;
-  for (int p = 0; p < num_parts && req < batch; ++p) {
-    const bool last_part = p == num_parts - 1;
-    long long cap = payload;
-    const int br = req, bb = blk, bp = cur;
-    int er = -1, eb = -1;
-    while (req < batch) {
-      const int n = n_of(req);
-      const long long rem = n - blk;
-      if (last_part || rem + F <= cap) {   // the rest of this request fits
-        cap -= rem + F;
-        ++cur;
-        er = req;
-        eb = n;
-        acc += cur;
-        max_pieces = max(max_pieces, cur);
-        if (lane == 0) num_splits[req + 1] = acc;
-        ++req;
-        blk = 0;
-        cur = 0;
-        continue;
+    int pieces = lane < cnt ? 1 : 0;
+    int i0 = 0;           // first request of the chunk not placed yet
+    long long zb = 0;     // prefix of costs before request i0
+    while (i0 < cnt && p < last) {   // in the last part every request fits whole
+      const unsigned long long fit = __ballot(lane >= i0 && lane < cnt && z - zb <= cap);
+      const int i1 = i0 + __popcll(fit);   // costs are >= 0: the fitting requests are i0 .. i1 - 1
+      if (i1 > i0) {
+        const long long zl = readlane64(z, i1 - 1);
+        cap -= zl - zb;
+        zb = zl;
+        i0 = i1;
+        if (i0 >= cnt) break;
       }
+      // request i0 does not fit whole in what part p has left
+      const int n0 = __builtin_amdgcn_readlane(n, i0);
       const long long take = cap - F;
-      if (take > 0) {                     // cut the request at a block boundary
-        blk += (int)take;
-        ++cur;
-        er = req;
-        eb = blk;
+      const int b0 = take > 0 ? (int)take : 0;   // its blocks in part p (take < n0 here)
+      const int pi0 = take > 0 ? 1 : 0;
+      const int rem = n0 - b0;
+      int k = 0;                                 // fresh parts it fills whole
+      if (p + 1 < last && rem > D) k = min((int)((unsigned)(rem - 1) / (unsigned)D), last - p - 1);
+      for (int j = lane; j <= k; j += 64) {      // parts p + 1 .. p + 1 + k begin inside it
+        pb_req[p + 1 + j] = base + i0;
+        pb_blk[p + 1 + j] = b0 + j * (int)D;
+        pb_piece[p + 1 + j] = pi0 + j;
       }
-      break;
+      p += 1 + k;
+      cap = P - F - (rem - (long long)k * D);    // after its last piece, in part p
+      const int pc = pi0 + k + 1;
+      if (lane == i0) pieces = pc;
+      max_pieces = max(max_pieces, pc);
+      zb = readlane64(z, i0);
+      ++i0;
     }
-    if (er < 0) continue;
-    if (lane == 0) {
-      int32_t* row = sched + (size_t)np * MLA_SCHED_INTS;
-      row[0] = br; row[1] = er; row[2] = bb; row[3] = eb; row[4] = bp;
-      row[6] = row[7] = 0;
+    int s = pieces;       // num_splits: inclusive prefix of pieces
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(s, off);
+      if (lane >= off) s += t;
     }
-    ++np;
+    if (lane < cnt) num_splits[base + lane + 1] = acc + s;
+    acc += __builtin_amdgcn_readlane(s, 63);
   }
-  for (int r = np + lane; r < num_parts; r += 64) {   // empty rows: no request
-    int32_t* row = sched + (size_t)r * MLA_SCHED_INTS;
-    row[0] = 1; row[1] = 0; row[2] = row[3] = row[4] = row[6] = row[7] = 0;
+  const int np = p + 1;   // parts the walk used
+  __syncthreads();
+  const int n_last = blocks_of(seqlens[batch - 1]);
+  for (int q = lane; q < num_parts; q += 64) {
+    int br = 1, er = 0, bb = 0, eb = 0, bp = 0;
+    if (q < np) {
+      br = pb_req[q];
+      bb = pb_blk[q];
+      bp = pb_piece[q];
+      if (q + 1 < np) {   // part q ends where part q + 1 begins
+        const int nr = pb_req[q + 1], nb = pb_blk[q + 1];
+        er = nb > 0 ? nr : nr - 1;
+        eb = nb > 0 ? nb : blocks_of(seqlens[er]);
+      } else {
+        er = batch - 1;
+        eb = n_last;
+      }
+    }
+    int4* row = reinterpret_cast<int4*>(sched + (size_t)q * MLA_SCHED_INTS);
+    row[0] = make_int4(br, er, bb, eb);
+    row[1] = make_int4(bp, max_pieces, 0, 0);
   }
-  for (int r = lane; r < num_parts; r += 64) sched[(size_t)r * MLA_SCHED_INTS + 5] = max_pieces;
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1477,6 +1516,8 @@ extern "C" int mla_get_metadata_device(const int32_t* cache_seqlens_dev, int bat
   if (rc) return rc;
   if (max_parts < parts)
     return set_error(MLA_ERR_CAPACITY, "mla_get_metadata_device: max_parts=%d < %d parts", max_parts, parts);
+  if (parts > kPlanMaxParts)
+    return set_error(MLA_ERR_INVALID, "mla_get_metadata_device: %d parts > %d", parts, kPlanMaxParts);
   hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, cache_seqlens_dev, batch, parts, F,
                      sched_dev, num_splits_dev);
   const hipError_t e = hipGetLastError();

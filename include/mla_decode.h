@@ -118,8 +118,10 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q, int s_q, 
  *   stream            hipStream_t (NULL = the null stream)
  * A plan's partial slots never exceed num_parts + batch - 1, so a workspace of
  * mla_workspace_bytes(num_parts + batch - 1, h_q, s_q) fits any lengths.
- * Allocates nothing, does not synchronise; batch <= 65536.
- * Errors: MLA_ERR_INVALID, MLA_ERR_CAPACITY, MLA_ERR_HIP.
+ * Allocates nothing, does not synchronise; batch <= 65536 and the policy's
+ * part count <= 4096 (one workgroup; LDS holds where each part begins).
+ * Errors: MLA_ERR_INVALID (also for the limits above), MLA_ERR_CAPACITY,
+ *         MLA_ERR_HIP.
  */
 int mla_get_metadata_device(const int32_t* cache_seqlens_dev, int batch, int h_q, int s_q, int num_cus,
                             int32_t* sched_dev, int max_parts, int32_t* num_splits_dev,

@@ -22,10 +22,10 @@ def _device_plan(seqlens, h_q, s_q, num_cus=0):
     return sched.cpu().numpy(), ns.cpu().numpy()
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_device_plan_equals_host_walk(seed):
     rng = np.random.default_rng(seed)
-    b = int(rng.choice([1, 3, 16, 64, 100, 130, 300]))
+    b = int(rng.choice([1, 3, 16, 64, 65, 100, 130, 300, 1000]))
     h_q, s_q = [(16, 1), (128, 1), (128, 2), (32, 2), (8, 1)][seed % 5]
     kind = seed % 4
     if kind == 0:
@@ -37,7 +37,7 @@ def test_device_plan_equals_host_walk(seed):
     else:
         sl = np.full(b, int(rng.integers(1, 20000)))
     sl = sl.astype(np.int32)
-    num_cus = int(rng.choice([0, 37, 256]))
+    num_cus = int(rng.choice([0, 1, 2, 3, 37, 256, 1024]))
     ds, dn = _device_plan(sl, h_q, s_q, num_cus=num_cus)
     hs, hn, total = mla.get_mla_metadata_host(sl, h_q, s_q, num_cus=num_cus)
     np_host = hs.shape[0]
@@ -46,6 +46,19 @@ def test_device_plan_equals_host_walk(seed):
     assert np.all(ds[np_host:, 0] == 1) and np.all(ds[np_host:, 1] == 0)   # empty rows
     assert np.all(ds[:, 5] == hs[0, 5])
     assert total == dn[-1] <= ds.shape[0] + b - 1
+
+
+@pytest.mark.parametrize("num_cus", [1, 3, 256])
+def test_device_plan_equals_host_walk_beyond_32_bits(num_cus):
+    """Lengths near 2^31 in a large batch: block totals and the payload pass
+    2^32, so the walk's capacity arithmetic must be 64-bit."""
+    rng = np.random.default_rng(num_cus)
+    sl = (2**31 - 1 - rng.integers(0, 2**20, size=5000)).astype(np.int32)
+    sl[::7] = rng.integers(0, 100, size=sl[::7].shape[0])
+    ds, dn = _device_plan(sl, 16, 1, num_cus=num_cus)
+    hs, hn, _ = mla.get_mla_metadata_host(sl, 16, 1, num_cus=num_cus)
+    assert np.array_equal(dn, hn)
+    assert np.array_equal(ds[:hs.shape[0]], hs)
 
 
 def test_decode_with_device_plan_equals_host_plan():

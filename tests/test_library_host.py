@@ -110,3 +110,17 @@ def test_decode_argument_errors_return_codes_without_launching():
     rc = L.mla_decode_fwd(dummy, dummy, dummy, dummy, 2, 1, 16, 8, 4, 0.1, 0, dummy, 3, dummy, dummy, 100,
                           dummy, dummy, None)
     assert rc == -3 and b"workspace" in L.mla_last_error()
+
+
+def test_device_planner_argument_errors_return_codes_without_launching():
+    L = mla.lib()
+    dummy = ctypes.c_void_p(16)   # never dereferenced: every check fails before any launch
+    n = ctypes.c_int(0)
+    rc = L.mla_get_metadata_device(dummy, 4, 16, 1, 256, None, 256, dummy, ctypes.byref(n), None)
+    assert rc == -1 and b"null" in L.mla_last_error()
+    rc = L.mla_get_metadata_device(dummy, 70000, 16, 1, 256, dummy, 256, dummy, ctypes.byref(n), None)
+    assert rc == -1 and b"batch" in L.mla_last_error()
+    rc = L.mla_get_metadata_device(dummy, 4, 16, 1, 256, dummy, 255, dummy, ctypes.byref(n), None)
+    assert rc == -2 and b"max_parts" in L.mla_last_error()
+    rc = L.mla_get_metadata_device(dummy, 4, 16, 1, 5000, dummy, 5000, dummy, ctypes.byref(n), None)
+    assert rc == -1 and b"4096" in L.mla_last_error()
