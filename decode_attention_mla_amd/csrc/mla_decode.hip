@@ -74,6 +74,7 @@ typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
 #define LDS_PTR(T) __attribute__((address_space(3))) T*
 
 constexpr int kRowBytes = kDqk * 2;                // 1152
@@ -287,15 +288,31 @@ struct PieceRange {
   int begin_req, end_req, begin_blk, end_blk, begin_piece;
 };
 
+// The whole 32-byte row in one scalar load (one round trip).
 __device__ __forceinline__ PieceRange load_part(const Params& p, int part) {
-  const int32_t* sp = p.sched + part * MLA_SCHED_INTS;
-  PieceRange r;
-  r.begin_req = ld_uniform(sp);
-  r.end_req = ld_uniform(sp + 1);
-  r.begin_blk = ld_uniform(sp + 2);
-  r.end_blk = ld_uniform(sp + 3);
-  r.begin_piece = ld_uniform(sp + 4);
-  return r;
+  const i32x8 v = ld_uniform((const i32x8*)(p.sched + part * MLA_SCHED_INTS));
+  return PieceRange{v[0], v[1], v[2], v[3], v[4]};
+}
+
+// What a piece needs of request `req` before its first copies: the length,
+// the partial slots [slot0, slot1) and the block ids of pages lo .. lo + 2
+// (clamped to the table row: entries past the request's pages are read but
+// their values are not used).  The loads do not depend on each other, so
+// they cost one round trip together.
+struct RequestMeta {
+  int L, slot0, slot1, blk[3];
+};
+
+__device__ __forceinline__ RequestMeta load_request(const Params& p, int req, int lo) {
+  const int32_t* bt = p.block_table + (size_t)req * p.max_blocks;
+  const int last = p.max_blocks - 1;
+  RequestMeta m;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) m.blk[i] = ld_uniform(bt + min(lo + i, last));
+  m.L = ld_uniform(p.seqlens + req);
+  m.slot0 = ld_uniform(p.num_splits + req);
+  m.slot1 = ld_uniform(p.num_splits + req + 1);
+  return m;
 }
 
 // ---------------------------------------------------------------------------
@@ -376,7 +393,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
   const unsigned wslice = (unsigned)(size_t)lds + wave * kStageBytes;   // this wave's slice of stage 0
   const unsigned dma_off[2] = {stage_dma_offset(lane, 0), stage_dma_offset(lane, 1)};
   // The request's query rows are staged like a page slice (row r in token
-  // slot r) in this wave's slice of stage 1; slots >= R copy row 0 instead
+  // slot r) in slice 0 of stage 1; slots >= R copy row 0 instead
   // (in bounds; their fragments are zeroed).
   unsigned q_dma_off[2];
 #pragma unroll
@@ -413,47 +430,55 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
   const int pw_off = ((wave >> 1) * 64 + (2 * (wave & 1) + (g >> 1)) * 16 + c16) * 16 + 8 * (g & 1);
 
   for (int req = pr.begin_req; req <= pr.end_req; ++req) {
-    const int L = ld_uniform(p.seqlens + req);
-    const int nblk = (L + kPage - 1) / kPage;
     const int lo = (req == pr.begin_req) ? pr.begin_blk : 0;
+    const RequestMeta m = load_request(p, req, lo);
+    const int L = m.L;
+    const int nblk = (L + kPage - 1) / kPage;
     const int hi = (req == pr.end_req) ? pr.end_blk : nblk;
-    const int slot0 = ld_uniform(p.num_splits + req);
-    const int slot = slot0 + ((req == pr.begin_req) ? pr.begin_piece : 0);
-    const bool split = (ld_uniform(p.num_splits + req + 1) - slot0) > 1;
+    const int slot = m.slot0 + ((req == pr.begin_req) ? pr.begin_piece : 0);
+    const bool split = m.slot1 - m.slot0 > 1;
     const int32_t* bt = p.block_table + (size_t)req * p.max_blocks;
-    auto rows_of = [&](int j) {
-      return uniform_ptr(p.kv + (size_t)ld_uniform(bt + j) * kPageBytes + (size_t)tok0 * kRowBytes);
+    auto page_rows = [&](int blk) {
+      return uniform_ptr(p.kv + (size_t)blk * kPageBytes + (size_t)tok0 * kRowBytes);
     };
 
     f32x4 o[8];
     float m_ref = -INFINITY, l_run = 0.f;
     // Q^T fragments (B operand): row c16, dims 32 ks + 8 g .. + 7.  Q is
-    // copied into this wave's slice of stage 1 ahead of the first page, read
-    // into registers as soon as it lands, and that slice then takes the
-    // second page, so both pages are in flight while Q is in use.  (All
-    // global reads here are explicit copies with explicit waits: no
-    // compiler-tracked load may be outstanding while page copies are in
-    // flight.)
+    // copied once per workgroup, into slice 0 of stage 1, ahead of the first
+    // page: wave w copies the 1 KiB pieces w, w + 4, ... of it (a CU moves its
+    // bytes at a bounded rate, so four private copies of Q would cost a
+    // quarter of a piece's traffic).  Every wave reads it into registers as
+    // soon as it has landed, and stage 1 then takes the second page, so
+    // both pages are in flight while Q is in use.  (All global reads here
+    // are explicit copies with explicit waits: no compiler-tracked load may
+    // be outstanding while page copies are in flight.)
     bf16x8 qf[kQkSteps];
-    issue_stage<false>(uniform_ptr(p.q + (size_t)req * p.R * kRowBytes), wslice + kPageBytes, q_dma_off);
+    {
+      const unsigned char* qrows = uniform_ptr(p.q + (size_t)req * p.R * kRowBytes);
+      const unsigned qslice = (unsigned)(size_t)lds + kPageBytes;
+      for (int i = wave; i < kStageSlices; i += 4) issue_stage_slice<false>(qrows, qslice, q_dma_off, i);
+    }
     for (int attempt = 0;; ++attempt) {
-      if (lo < hi) issue_stage<true>(rows_of(lo), wslice, dma_off);
+      if (lo < hi) issue_stage<true>(page_rows(m.blk[0]), wslice, dma_off);
       if (attempt == 0) {
         if (lo < hi)
-          wait_vmcnt<kStageSlices>();   // Q (the first page may still be in flight)
+          wait_vmcnt<kStageSlices>();   // this wave's pieces of Q (the first page may still be in flight)
         else
           wait_vmcnt<0>();
+        lds_barrier();                  // all of Q has landed
         const unsigned keep = row_ok ? ~0u : 0u;
-        LDS_PTR(unsigned char) qs = lds + kPageBytes + wave * kStageBytes;
+        LDS_PTR(unsigned char) qs = lds + kPageBytes;
 #pragma unroll
         for (int ks = 0; ks < kQkSteps; ++ks) {
           u32x4 v = *(LDS_PTR(u32x4))(qs + (ks >> 1) * kStageBlock + qk_off[ks & 1]);
           v &= keep;
           qf[ks] = __builtin_bit_cast(bf16x8, v);
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the Q slot is free again
+        lds_barrier();                  // every wave has read Q: stage 1 is free again
       }
-      if (lo + 1 < hi) issue_stage<true>(rows_of(lo + 1), wslice + kPageBytes, dma_off);
+      if (lo + 1 < hi) issue_stage<true>(page_rows(m.blk[1]), wslice + kPageBytes, dma_off);
+      int next_blk = m.blk[2];   // block ids are read one page ahead of their copy
 
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) o[ct] = f32x4{0, 0, 0, 0};
@@ -476,7 +501,10 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
         // Page j + 1 goes to the stage page j - 1 held (pages lo, lo + 1 were
         // issued ahead of the loop).  (A third page in flight from the start,
         // held in registers, was measured slower: every page then lands late.)
-        if (j > lo && j + 1 < hi) issue_stage<true>(rows_of(j + 1), wslice + ((j + 1 - lo) & 1) * kPageBytes, dma_off);
+        if (j > lo && j + 1 < hi) {
+          issue_stage<true>(page_rows(next_blk), wslice + ((j + 1 - lo) & 1) * kPageBytes, dma_off);
+          next_blk = ld_uniform(bt + min(j + 2, p.max_blocks - 1));
+        }
 
         // ---- S^T (this wave's 16 tokens x 16 rows) = K Q^T, three chains.
         LDS_PTR(unsigned char) own = buf + wave * kStageBytes;
@@ -642,22 +670,22 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_kernel(Params p) {
     }
 
   for (int req = pr.begin_req; req <= pr.end_req; ++req) {
-    const int L = ld_uniform(p.seqlens + req);
-    const int nblk = (L + kPage - 1) / kPage;
     const int lo = (req == pr.begin_req) ? pr.begin_blk : 0;
+    const RequestMeta m = load_request(p, req, lo);
+    const int L = m.L;
+    const int nblk = (L + kPage - 1) / kPage;
     const int hi = (req == pr.end_req) ? pr.end_blk : nblk;
-    const int slot0 = ld_uniform(p.num_splits + req);
-    const int slot = slot0 + ((req == pr.begin_req) ? pr.begin_piece : 0);
-    const bool split = (ld_uniform(p.num_splits + req + 1) - slot0) > 1;
+    const int slot = m.slot0 + ((req == pr.begin_req) ? pr.begin_piece : 0);
+    const bool split = m.slot1 - m.slot0 > 1;
     const int32_t* bt = p.block_table + (size_t)req * p.max_blocks;
-    auto rows_of = [&](int j) {
-      return uniform_ptr(p.kv + (size_t)ld_uniform(bt + j) * kPageBytes + (size_t)tok0 * kRowBytes);
+    auto page_rows = [&](int blk) {
+      return uniform_ptr(p.kv + (size_t)blk * kPageBytes + (size_t)tok0 * kRowBytes);
     };
 
     f32x16 o[kDv / 32];
     float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
     for (int attempt = 0;; ++attempt) {
-      if (lo < hi) issue_stage<false>(rows_of(lo), wlds0, dma_off);
+      if (lo < hi) issue_stage<false>(page_rows(m.blk[0]), wlds0, dma_off);
       bf16x8 qf[2][kQkSteps];
       load_q(qf[0], p, req, row0 + c16, g);
       load_q(qf[1], p, req, row0 + 16 + c16, g);
@@ -920,22 +948,22 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
     }
 
   for (int req = pr.begin_req; req <= pr.end_req; ++req) {
-    const int L = ld_uniform(p.seqlens + req);
-    const int nblk = (L + kPage - 1) / kPage;
     const int lo = (req == pr.begin_req) ? pr.begin_blk : 0;
+    const RequestMeta m = load_request(p, req, lo);
+    const int L = m.L;
+    const int nblk = (L + kPage - 1) / kPage;
     const int hi = (req == pr.end_req) ? pr.end_blk : nblk;
-    const int slot0 = ld_uniform(p.num_splits + req);
-    const int slot = slot0 + ((req == pr.begin_req) ? pr.begin_piece : 0);
-    const bool split = (ld_uniform(p.num_splits + req + 1) - slot0) > 1;
+    const int slot = m.slot0 + ((req == pr.begin_req) ? pr.begin_piece : 0);
+    const bool split = m.slot1 - m.slot0 > 1;
     const int32_t* bt = p.block_table + (size_t)req * p.max_blocks;
-    auto rows_of = [&](int j) {
-      return uniform_ptr(p.kv + (size_t)ld_uniform(bt + j) * kPageBytes + (size_t)tok0 * kRowBytes);
+    auto page_rows = [&](int blk) {
+      return uniform_ptr(p.kv + (size_t)blk * kPageBytes + (size_t)tok0 * kRowBytes);
     };
 
     f32x16 o[kWideTiles][4];   // O^T tiles: row tile x this wave's 4 column tiles
     float m_ref = -INFINITY, l_run = 0.f;
     for (int attempt = 0;; ++attempt) {
-      if (lo < hi) issue_stage<kStream>(rows_of(lo), lds0 + wave * kStageBytes, dma_off);
+      if (lo < hi) issue_stage<kStream>(page_rows(m.blk[0]), lds0 + wave * kStageBytes, dma_off);
       // Q^T fragments (B operand): row r, dims 16 ks + 8 h .. + 7.
       bf16x8 qf[kQkSteps16];
       {
@@ -959,7 +987,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
       l_run = 0.f;
       float l_part[4] = {0.f, 0.f, 0.f, 0.f};
       bool restart = false;
-      int next_blk = ld_uniform(bt + (lo + 1 < hi ? lo + 1 : lo));
+      int next_blk = m.blk[1];   // copied only if lo + 1 < hi
 
       for (int j = lo; j < hi; ++j) {
         const int stage = (j - lo) & 1;
@@ -1258,14 +1286,27 @@ __global__ void __launch_bounds__(kCombineWaves * 64) mla_combine_kernel(Params 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int pairs = p.batch * p.R;
   const size_t ostride = (size_t)p.R * kDv;
+  // The piece counts of both layouts' first pairs are read together with
+  // the table's largest piece count (one round trip), and the next pair's
+  // while the current one is merged.
+  auto splits_of = [&](int pair, int& slot0, int& slot1) {
+    const int req = min(pair, pairs - 1) / p.R;
+    slot0 = ld_uniform(p.num_splits + req);
+    slot1 = ld_uniform(p.num_splits + req + 1);
+  };
+  const int first_w = blockIdx.x * kCombineWaves + wave, first_g = blockIdx.x;
+  int sw0, sw1, sg0, sg1;
+  splits_of(first_w, sw0, sw1);
+  splits_of(first_g, sg0, sg1);
   const int max_pieces = ld_uniform(p.sched + 5);   // the schedule table's largest piece count
   if (max_pieces <= 1) return;
   if (max_pieces <= kCombineChunk) {
     // Many short merges: one pair per wave.
-    for (int pair = blockIdx.x * kCombineWaves + wave; pair < pairs; pair += gridDim.x * kCombineWaves) {
+    for (int pair = first_w; pair < pairs; pair += gridDim.x * kCombineWaves) {
       const int req = pair / p.R, row = pair - req * p.R;
-      const int slot0 = ld_uniform(p.num_splits + req);
-      const int n = ld_uniform(p.num_splits + req + 1) - slot0;
+      const int slot0 = sw0;
+      const int n = sw1 - sw0;
+      splits_of(pair + gridDim.x * kCombineWaves, sw0, sw1);
       if (n <= 1) continue;   // uniform over the wave
       float M = -INFINITY, l = 0.f;
       f32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
@@ -1276,10 +1317,11 @@ __global__ void __launch_bounds__(kCombineWaves * 64) mla_combine_kernel(Params 
     return;
   }
   // Few long merges: one pair per workgroup, wave w taking splits w, w + 4, ...
-  for (int pair = blockIdx.x; pair < pairs; pair += gridDim.x) {
+  for (int pair = first_g; pair < pairs; pair += gridDim.x) {
     const int req = pair / p.R, row = pair - req * p.R;
-    const int slot0 = ld_uniform(p.num_splits + req);
-    const int n = ld_uniform(p.num_splits + req + 1) - slot0;
+    const int slot0 = sg0;
+    const int n = sg1 - sg0;
+    splits_of(pair + gridDim.x, sg0, sg1);
     if (n <= 1) continue;   // uniform over the workgroup
     const int nw = (n - wave + kCombineWaves - 1) / kCombineWaves;   // this wave's splits
     float M = -INFINITY, l = 0.f;
