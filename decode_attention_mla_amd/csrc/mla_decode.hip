@@ -324,6 +324,11 @@ __device__ __forceinline__ RequestMeta load_request(const Params& p, int req, in
 // that XCD's L2.  The grid is 8 * row_groups * ceil(parts / 8); ids past the
 // last part exit.
 __device__ __forceinline__ void map_block(const Params& p, int& part, int& rg) {
+  // Every kernel argument the prologue needs is made to arrive in one round
+  // trip here (the compiler would otherwise load some only after the early
+  // exit below, one dependent round trip more before the first page copy).
+  asm volatile("" ::"s"(p.sched), "s"(p.seqlens), "s"(p.num_splits), "s"(p.block_table), "s"(p.q), "s"(p.kv),
+               "s"(p.out), "s"(p.lse), "s"(p.oacc), "s"(p.lacc));
   const int id = blockIdx.x;
   const int xcd = id & 7, slot = id >> 3;
   const int per = (p.num_parts + 7) / 8;
