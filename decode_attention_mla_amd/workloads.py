@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for dense MLA decode.
+"""Seeded synthetic inputs for dense and sparse MLA decode.
 
 This module only draws and lays out inputs; it holds none of the attention
 arithmetic.  Both the CPU oracle (tests) and the GPU path consume what it
@@ -155,6 +155,114 @@ def make_inputs(batch: int, s_q: int, h_q: int, seqlens, pool: int | None, max_b
             kv[block_table[b, n - 1], tail:] = poison
     return MlaInputs(name=name, q=q, kv_cache=kv, block_table=block_table,
                      cache_seqlens=lens, softmax_scale=float(softmax_scale))
+
+
+@dataclasses.dataclass
+class SparseInputs:
+    """Sparse (top-k) decode inputs ("[DeepSeek-3] FlashMLA", section 11)."""
+    name: str
+    q: np.ndarray             # uint16 [b, s_q, h_q, 576]
+    kv_cache: np.ndarray      # uint16 [num_blocks, 64, 1, 576]
+    indices: np.ndarray       # int32 [b, s_q, topk]: page_id * 64 + offset, -1 = no key
+    topk_length: np.ndarray | None   # int32 [b] or None (all topk entries count)
+    softmax_scale: float
+
+    @property
+    def batch(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def s_q(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def h_q(self) -> int:
+        return int(self.q.shape[2])
+
+    @property
+    def topk(self) -> int:
+        return int(self.indices.shape[2])
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.kv_cache.shape[0])
+
+
+def make_sparse_inputs(batch: int, s_q: int, h_q: int, topk: int, context, seed: int,
+                       pad_frac: float = 0.0, topk_length=None, softmax_scale: float = SOFTMAX_SCALE,
+                       name: str = "sparse") -> SparseInputs:
+    """Draw one seeded sparse workload.
+
+    Recipe, in draw order: each request's context length (``context`` is a
+    list or a ``(lo, hi)`` pair, uniform inclusive; at least ``topk``);
+    a permutation of a page pool holding every context plus one spare page;
+    q and the pool as fp32 N(0,1) rounded to bf16; then, per (request, query
+    token), ``topk`` distinct positions of that request's context drawn
+    uniformly without replacement (the output of a top-k selector over the
+    context, in arbitrary order), mapped to page_id * 64 + offset through the
+    request's pages.  With ``pad_frac`` > 0 that fraction of entries, at
+    random places, becomes -1 (padding).  ``topk_length`` (a list, or
+    None) is passed through.  Pool rows no list names are poisoned, so a
+    wrong gather shows as a gross error.
+    """
+    rng = np.random.default_rng(seed)
+    if isinstance(context, tuple):
+        lo, hi = context
+        ctx = rng.integers(lo, hi + 1, size=batch).astype(np.int64)
+    else:
+        ctx = np.asarray(context, dtype=np.int64)
+        assert ctx.shape == (batch,)
+    assert np.all(ctx >= topk)
+    npages = [(int(L) + PAGE - 1) // PAGE for L in ctx]
+    pool = sum(npages) + 1
+    perm = rng.permutation(pool).astype(np.int64)
+    q = _draw_normal_bf16(rng, (batch, s_q, h_q, D_QK))
+    kv = _draw_normal_bf16(rng, (pool, PAGE, 1, D_QK))
+    indices = np.empty((batch, s_q, topk), dtype=np.int32)
+    at = 0
+    for b in range(batch):
+        pages = perm[at:at + npages[b]]
+        at += npages[b]
+        for s in range(s_q):
+            pos = rng.choice(int(ctx[b]), size=topk, replace=False)
+            indices[b, s] = (pages[pos // PAGE] * PAGE + pos % PAGE).astype(np.int32)
+    if pad_frac > 0:
+        indices[rng.random(indices.shape) < pad_frac] = -1
+    named = np.zeros(pool * PAGE, dtype=bool)
+    named[indices[indices >= 0].astype(np.int64)] = True
+    flat = kv.reshape(pool * PAGE, D_QK)
+    flat[~named] = int(f32_to_bf16_bits(np.array([POISON], np.float32))[0])
+    tl = None if topk_length is None else np.asarray(topk_length, dtype=np.int32)
+    return SparseInputs(name=name, q=q, kv_cache=kv, indices=indices, topk_length=tl,
+                        softmax_scale=float(softmax_scale))
+
+
+# The sparse workload of the pages' FP8-sparse micro-benchmark shape
+# (batch 128, s_q 2, h_q 128, topk 2048; section 13 of the overview), here
+# on a bf16 cache, each request's context 4096..8192 tokens.
+SPARSE_CONFIG = dict(name="sparse_b128_sq2_hq128_topk2048", batch=128, s_q=2, h_q=128, topk=2048,
+                     context=(4096, 8192))
+
+
+def sparse_config_inputs(seed: int = 6) -> SparseInputs:
+    c = SPARSE_CONFIG
+    return make_sparse_inputs(c["batch"], c["s_q"], c["h_q"], c["topk"], c["context"], seed=seed, name=c["name"])
+
+
+def sparse_algorithmic_work(indices: np.ndarray, h_q: int, topk_length=None) -> tuple[float, float]:
+    """(FLOPs, bytes) of one sparse decode call: every counted entry of every
+    query token's list is one key (576 + 512 dims, 2 FLOPs each, h_q heads)
+    and one 1152-byte cache row read; plus the index list (4 B per entry),
+    q read, out written (bf16) and lse written (fp32)."""
+    b, s_q, topk = indices.shape
+    keys = 0
+    for i in range(b):
+        n = topk if topk_length is None else min(max(int(topk_length[i]), 0), topk)
+        keys += int((indices[i, :, :n] >= 0).sum())
+    rows = b * s_q * h_q
+    flops = 2.0 * h_q * keys * (D_QK + D_V)
+    nbytes = 2.0 * D_QK * keys + 4.0 * b * s_q * topk + 2.0 * rows * (D_QK + D_V) + 4.0 * rows
+    return flops, nbytes
 
 
 def config_inputs(index: int) -> MlaInputs:

@@ -1,4 +1,4 @@
-"""CPU oracle for dense MLA decode (weight-absorbed, paged).
+"""CPU oracle for dense and sparse MLA decode (weight-absorbed, paged).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or call anything under
@@ -137,6 +137,72 @@ def mla_decode_rows(q, kv_cache, block_table, cache_seqlens, softmax_scale, pick
         if i not in cache:
             cache[i] = request_keys(kv_cache, block_table[i], int(cache_seqlens[i]))
         keys = cache[i][:visible_keys(cache_seqlens[i], s_q, s, causal)]
+        o, ls = attend(bf16_to_f64(q[i, s, h])[None, :], keys, softmax_scale)
+        outs.append(o[0])
+        lses.append(ls[0])
+    return np.array(outs), np.array(lses)
+
+
+# ---------------------------------------------------------------------------
+# Sparse (top-k) decode ("[DeepSeek-3] FlashMLA", section 11): each query
+# token attends only to the cache rows its index list names; an entry is
+# page_id * 64 + offset, the row at slot `offset` of physical block
+# `page_id`, so no block table is involved.  Readings (listed in the design
+# notes): the list is a multiset (an index named twice is two keys); only the
+# first topk_length[b] entries of request b's lists count (the API's
+# topk_length, which the overview names among the values that set the work;
+# all topk entries when it is absent); an entry outside [0, num_blocks * 64),
+# -1 padding for example, names no key; a query token left with no key gets
+# out = 0 and lse = -inf, as an empty dense request does.
+
+def sparse_keys(kv_cache: np.ndarray, index_row: np.ndarray, n_valid: int) -> np.ndarray:
+    """The keys one query token's index list names, in list order.
+
+    kv_cache uint16 [nb, 64, 1, 576]; index_row int [topk]; only entries
+    0 .. n_valid - 1 count.  Returns float64 [k, 576].
+    """
+    rows = kv_cache.reshape(-1, D_QK)          # row page_id * 64 + offset
+    picked = [int(e) for e in np.asarray(index_row)[:max(0, int(n_valid))] if 0 <= int(e) < rows.shape[0]]
+    if not picked:
+        return np.zeros((0, D_QK), dtype=np.float64)
+    return bf16_to_f64(rows[np.asarray(picked, dtype=np.int64)])
+
+
+def sparse_valid(topk: int, topk_length, i: int) -> int:
+    """Entries of request i's index lists that count (see the reading above)."""
+    if topk_length is None:
+        return topk
+    return min(max(int(topk_length[i]), 0), topk)
+
+
+def mla_decode_sparse(q, kv_cache, indices, softmax_scale, topk_length=None):
+    """Sparse MLA decode for every (request, query token, head).
+
+    q uint16 [b, s_q, h_q, 576]; kv_cache uint16 [nb, 64, 1, 576];
+    indices int32 [b, s_q, topk]; topk_length int32 [b] or None.
+    Returns out float64 [b, s_q, h_q, 512] and lse float64 [b, h_q, s_q].
+    """
+    b, s_q, h_q, d = q.shape
+    assert d == D_QK and indices.shape[:2] == (b, s_q)
+    topk = indices.shape[2]
+    out = np.full((b, s_q, h_q, D_V), np.nan)
+    lse = np.full((b, h_q, s_q), np.nan)
+    for i in range(b):
+        n = sparse_valid(topk, topk_length, i)
+        for s in range(s_q):
+            o, ls = attend(bf16_to_f64(q[i, s]), sparse_keys(kv_cache, indices[i, s], n), softmax_scale)
+            out[i, s] = o
+            lse[i, :, s] = ls
+    return out, lse
+
+
+def mla_decode_sparse_rows(q, kv_cache, indices, softmax_scale, picks, topk_length=None):
+    """Sparse outputs for a sample of (request, query token, head) triples:
+    out float64 [n, 512] and lse float64 [n] in the order of ``picks``."""
+    topk = indices.shape[2]
+    outs, lses = [], []
+    for (i, s, h) in picks:
+        keys = sparse_keys(kv_cache, indices[i, s], sparse_valid(topk, topk_length, i))
         o, ls = attend(bf16_to_f64(q[i, s, h])[None, :], keys, softmax_scale)
         outs.append(o[0])
         lses.append(ls[0])

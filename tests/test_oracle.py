@@ -374,3 +374,103 @@ def test_causal_rows_sampler_matches_full():
             assert np.isneginf(l[k]) and np.all(o[k] == 0)
         else:
             assert np.allclose(o[k], out[i, s, h], rtol=0, atol=1e-13) and abs(l[k] - lse[i, h, s]) < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# Sparse (top-k) decode: pinned to the dense oracle through the identity
+# gather, to closed forms under uniform weights (multiplicity, page/offset
+# decoding), and to invariants (list order, padding, truncation).
+
+def _dense_as_sparse(inp, topk, pad_value=-1):
+    """Index lists naming each request's dense keys in logical order,
+    padded with ``pad_value`` up to ``topk`` (page_id * 64 + offset)."""
+    b, s_q = inp.batch, inp.s_q
+    idx = np.full((b, s_q, topk), pad_value, dtype=np.int32)
+    for i in range(b):
+        L = int(inp.cache_seqlens[i])
+        t = np.arange(L)
+        phys = inp.block_table[i, t // PAGE].astype(np.int64) * PAGE + t % PAGE
+        idx[i, :, :L] = phys
+    return idx
+
+
+def test_sparse_identity_gather_equals_dense():
+    inp = W.make_inputs(3, 2, 4, [100, 257, 64], pool=12, max_blocks=6, seed=5)
+    idx = _dense_as_sparse(inp, 300)
+    o_d, l_d = oracle.mla_decode(inp.q, inp.kv_cache, inp.block_table, inp.cache_seqlens, inp.softmax_scale)
+    o_s, l_s = oracle.mla_decode_sparse(inp.q, inp.kv_cache, idx, inp.softmax_scale)
+    assert np.allclose(o_s, o_d, rtol=0, atol=1e-12) and np.allclose(l_s, l_d, rtol=0, atol=1e-12)
+    # The same lists without padding, cut by topk_length instead.
+    idx2 = _dense_as_sparse(inp, 300, pad_value=0)
+    o_t, l_t = oracle.mla_decode_sparse(inp.q, inp.kv_cache, idx2[:, :, :257], inp.softmax_scale,
+                                        topk_length=inp.cache_seqlens)
+    assert np.allclose(o_t, o_d, rtol=0, atol=1e-12) and np.allclose(l_t, l_d, rtol=0, atol=1e-12)
+
+
+def test_sparse_index_decodes_page_and_offset():
+    """Row r of block p holds V = (p, r, 1, 0, ...) and K = 0: with uniform
+    weights out is the mean of the named (page, offset) pairs, so a swapped
+    page/offset decoding or a wrong block stride shows directly."""
+    pool = 5
+    kv = np.zeros((pool, PAGE, 1, D_QK), dtype=np.uint16)
+    for p in range(pool):
+        for r in range(PAGE):
+            kv[p, r, 0, :3] = _bits([p, r, 1.0])
+    q = _bits(np.zeros((1, 1, 1, D_QK), np.float32))
+    picks = [(3, 7), (0, 63), (4, 0), (1, 32)]
+    idx = np.array([[[p * PAGE + r for p, r in picks]]], dtype=np.int32)
+    out, lse = oracle.mla_decode_sparse(q, kv, idx, 0.5)
+    assert out[0, 0, 0, 0] == pytest.approx(np.mean([p for p, _ in picks]), abs=1e-12)
+    assert out[0, 0, 0, 1] == pytest.approx(np.mean([r for _, r in picks]), abs=1e-12)
+    assert out[0, 0, 0, 2] == pytest.approx(1.0, abs=1e-12)
+    assert lse[0, 0, 0] == pytest.approx(math.log(len(picks)), abs=1e-12)
+
+
+def test_sparse_list_is_a_multiset():
+    """softmax_scale = 0: every listed entry weighs the same, so an index
+    named twice counts twice (out = (2 V_a + V_b) / 3, lse = ln 3)."""
+    rng = np.random.default_rng(11)
+    kv = _bits(rng.standard_normal((2, PAGE, 1, D_QK)).astype(np.float32))
+    q = _bits(rng.standard_normal((1, 1, 2, D_QK)).astype(np.float32))
+    a, b = 70, 5
+    idx = np.array([[[a, b, a]]], dtype=np.int32)
+    out, lse = oracle.mla_decode_sparse(q, kv, idx, 0.0)
+    rows = oracle.bf16_to_f64(kv.reshape(-1, D_QK))
+    want = (2 * rows[a, :D_V] + rows[b, :D_V]) / 3
+    assert np.allclose(out[0, 0], want[None, :], rtol=0, atol=1e-12)
+    assert np.allclose(lse[0, :, 0], math.log(3), rtol=0, atol=1e-12)
+
+
+def test_sparse_padding_order_and_truncation():
+    inp = W.make_sparse_inputs(2, 2, 3, 40, [200, 130], seed=3, pad_frac=0.25)
+    o, l = oracle.mla_decode_sparse(inp.q, inp.kv_cache, inp.indices, inp.softmax_scale)
+    # Order of the list does not matter (padding included).
+    rng = np.random.default_rng(0)
+    shuf = inp.indices.copy()
+    for i in range(2):
+        for s in range(2):
+            shuf[i, s] = shuf[i, s, rng.permutation(40)]
+    o2, l2 = oracle.mla_decode_sparse(inp.q, inp.kv_cache, shuf, inp.softmax_scale)
+    assert np.allclose(o2, o, rtol=0, atol=1e-12) and np.allclose(l2, l, rtol=0, atol=1e-12)
+    # Padding entries (-1) and entries past the pool name no key: the same as dropping them.
+    big = inp.indices.copy()
+    big[big < 0] = inp.kv_cache.shape[0] * PAGE + 17
+    o3, l3 = oracle.mla_decode_sparse(inp.q, inp.kv_cache, big, inp.softmax_scale)
+    assert np.allclose(o3, o, rtol=0, atol=1e-12) and np.allclose(l3, l, rtol=0, atol=1e-12)
+    i, s = 1, 0
+    kept = inp.indices[i, s][inp.indices[i, s] >= 0]
+    o4, l4 = oracle.mla_decode_sparse(inp.q[i:i + 1, s:s + 1], inp.kv_cache, kept[None, None, :], inp.softmax_scale)
+    assert np.allclose(o4[0, 0], o[i, s], rtol=0, atol=1e-12) and np.allclose(l4[0, :, 0], l[i, :, s], atol=1e-12)
+    # topk_length keeps the first entries of each list of that request.
+    o5, l5 = oracle.mla_decode_sparse(inp.q, inp.kv_cache, inp.indices, inp.softmax_scale, topk_length=[40, 25])
+    o6, l6 = oracle.mla_decode_sparse(inp.q[1:], inp.kv_cache, inp.indices[1:, :, :25], inp.softmax_scale)
+    assert np.allclose(o5[0], o[0], atol=1e-12) and np.allclose(o5[1], o6[0], atol=1e-12)
+    assert np.allclose(l5[1], l6[0], atol=1e-12)
+
+
+def test_sparse_no_key_gives_zero_and_minus_inf():
+    inp = W.make_sparse_inputs(2, 1, 4, 8, [64, 64], seed=2)
+    idx = inp.indices.copy()
+    idx[0] = -1
+    out, lse = oracle.mla_decode_sparse(inp.q, inp.kv_cache, idx, inp.softmax_scale, topk_length=[8, 0])
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
