@@ -21,7 +21,8 @@ D_V = 512
 
 # Every symbol include/mla_decode.h declares.
 EXPORTED = ("mla_plan", "mla_get_metadata", "mla_get_metadata_device", "mla_max_parts", "mla_workspace_bytes",
-            "mla_decode_fwd", "mla_profile_start", "mla_profile_stop", "mla_last_error")
+            "mla_decode_fwd", "mla_max_parts_sparse", "mla_get_metadata_sparse", "mla_decode_sparse_fwd",
+            "mla_profile_start", "mla_profile_stop", "mla_last_error")
 
 _lib = None
 
@@ -59,6 +60,15 @@ def lib() -> ctypes.CDLL:
                                  ctypes.c_int, ctypes.c_float, ctypes.c_int, vp, ctypes.c_int, vp, vp,
                                  ctypes.c_size_t, vp, vp, vp]
     L.mla_decode_fwd.restype = ctypes.c_int
+    L.mla_max_parts_sparse.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.mla_max_parts_sparse.restype = ctypes.c_int
+    L.mla_get_metadata_sparse.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          i32p, ctypes.c_int, i32p, ip, ip]
+    L.mla_get_metadata_sparse.restype = ctypes.c_int
+    L.mla_decode_sparse_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_float, vp, ctypes.c_int, vp, vp, ctypes.c_size_t,
+                                        vp, vp, vp]
+    L.mla_decode_sparse_fwd.restype = ctypes.c_int
     L.mla_profile_start.argtypes = [ctypes.c_int]
     L.mla_profile_start.restype = ctypes.c_int
     fp = ctypes.POINTER(ctypes.c_float)
@@ -216,6 +226,88 @@ def mla_decode_fwd(q, kv_cache, block_table, cache_seqlens, softmax_scale: float
                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                               out.data_ptr(), lse.data_ptr(), stream)
     _check(rc, "mla_decode_fwd")
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Sparse (top-k) decode
+
+def get_mla_metadata_sparse_host(topk_length, batch: int, s_q: int, h_q: int, topk: int, num_cus: int = 0):
+    """mla_get_metadata_sparse: (sched [P, 8], num_splits [b * s_q + 1],
+    total_splits) host arrays.  topk_length: host int32 [b] or None."""
+    L = lib()
+    cap = L.mla_max_parts_sparse(int(batch), int(s_q), int(h_q), int(num_cus))
+    _check(cap if cap < 0 else 0, "mla_max_parts_sparse")
+    sched = np.zeros((max(cap, 1), SCHED_INTS), dtype=np.int32)
+    ns = np.zeros(int(batch) * int(s_q) + 1, dtype=np.int32)
+    nparts, total = ctypes.c_int(0), ctypes.c_int(0)
+    tl = None if topk_length is None else _i32_host(topk_length)
+    _check(L.mla_get_metadata_sparse(None if tl is None else _ptr(tl), int(batch), int(s_q), int(h_q), int(topk),
+                                     int(num_cus), _ptr(sched), sched.shape[0], _ptr(ns), ctypes.byref(nparts),
+                                     ctypes.byref(total)), "mla_get_metadata_sparse")
+    return sched[:nparts.value].copy(), ns, int(total.value)
+
+
+def get_mla_metadata_sparse(topk_length, batch: int, s_q: int, h_q: int, topk: int, device=None, num_cus: int = 0):
+    """The sparse plan as device tensors (sched int32 [P, 8], num_splits int32 [b * s_q + 1])."""
+    import torch
+    sched, ns, _ = get_mla_metadata_sparse_host(topk_length, batch, s_q, h_q, topk, num_cus)
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    return torch.from_numpy(sched).to(dev), torch.from_numpy(ns).to(dev)
+
+
+def mla_decode_sparse_fwd(q, kv_cache, indices, softmax_scale: float, sched, num_splits, topk_length=None,
+                          out=None, lse=None, workspace=None):
+    """Sparse MLA decode.  Returns (out bf16 [b, s_q, h_q, 512], lse fp32 [b, h_q, s_q]).
+
+    q bf16 [b, s_q, h_q, 576]; kv_cache bf16 [num_blocks, 64, 1, 576];
+    indices int32 [b, s_q, topk] (page_id * 64 + offset; out-of-range
+    entries name no key); topk_length int32 [b] (device) or None;
+    sched / num_splits from get_mla_metadata_sparse with the same sizes and
+    topk_length.  All tensors on the same GPU, contiguous; enqueued on the
+    current stream.
+    """
+    import torch
+    _need(q.dim() == 4 and q.shape[3] == D_QK, f"q must be [b, s_q, h_q, 576], got {tuple(q.shape)}")
+    b, s_q, h_q = (int(x) for x in q.shape[:3])
+    _need(kv_cache.dim() == 4 and tuple(kv_cache.shape[1:]) == (PAGE, 1, D_QK),
+          f"kv_cache must be [num_blocks, 64, 1, 576], got {tuple(kv_cache.shape)}")
+    _need(indices.dim() == 3 and tuple(indices.shape[:2]) == (b, s_q) and indices.shape[2] > 0,
+          "indices must be [b, s_q, topk]")
+    topk = int(indices.shape[2])
+    n = b * s_q
+    _need(sched.dim() == 2 and sched.shape[1] == SCHED_INTS and sched.shape[0] > 0, "sched must be [P, 8]")
+    _need(num_splits.dim() == 1 and num_splits.shape[0] == n + 1, "num_splits must be [b * s_q + 1]")
+    checks = [("q", q, torch.bfloat16), ("kv_cache", kv_cache, torch.bfloat16), ("indices", indices, torch.int32),
+              ("sched", sched, torch.int32), ("num_splits", num_splits, torch.int32)]
+    if topk_length is not None:
+        _need(topk_length.dim() == 1 and topk_length.shape[0] == b, "topk_length must be [b]")
+        checks.append(("topk_length", topk_length, torch.int32))
+    for name, t, dt in checks:
+        _need(t.dtype == dt, f"{name} must be {dt}, got {t.dtype}")
+        _need(t.is_cuda and t.device == q.device, f"{name} must be on {q.device}")
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+    num_parts = int(sched.shape[0])
+    if out is None:
+        out = torch.empty((b, s_q, h_q, D_V), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((b, h_q, s_q), dtype=torch.float32, device=q.device)
+    _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (b, s_q, h_q, D_V) and out.is_contiguous(),
+          "out must be contiguous bf16 [b, s_q, h_q, 512]")
+    _need(lse.dtype == torch.float32 and tuple(lse.shape) == (b, h_q, s_q) and lse.is_contiguous(),
+          "lse must be contiguous fp32 [b, h_q, s_q]")
+    ws_bytes = mla_workspace_bytes(num_parts + n - 1, h_q, 1)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    _need(workspace.numel() * workspace.element_size() >= ws_bytes, f"workspace needs {ws_bytes} bytes")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib().mla_decode_sparse_fwd(q.data_ptr(), kv_cache.data_ptr(), indices.data_ptr(),
+                                     None if topk_length is None else topk_length.data_ptr(),
+                                     b, s_q, h_q, int(kv_cache.shape[0]), topk, float(softmax_scale),
+                                     sched.data_ptr(), num_parts, num_splits.data_ptr(), workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), out.data_ptr(), lse.data_ptr(),
+                                     stream)
+    _check(rc, "mla_decode_sparse_fwd")
     return out, lse
 
 

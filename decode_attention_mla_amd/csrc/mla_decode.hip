@@ -41,6 +41,7 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -98,6 +99,12 @@ struct Params {
   int batch, R, h_q, s_q, max_blocks, num_parts, row_groups;
   int causal;                  // 1: query token s of s_q sees keys 0 .. L - s_q + s
   float scale_log2;            // softmax_scale * log2(e)
+  // Sparse decode (indices != nullptr): "request" v = b * fold + s is query
+  // token s of request b, with R = h_q rows and s_q = 1 here; fold is the
+  // real s_q (1 for dense decode), used to place lse.
+  const int32_t* indices;      // [batch * fold, topk]: page_id * 64 + offset
+  const int32_t* topk_len;     // [real batch]: entries of each list that count, or nullptr (all topk)
+  int topk, kv_tokens, fold;
 };
 
 // Keys query row `row` (= s * h_q + h) sees in a request of length L: all L,
@@ -198,6 +205,75 @@ __device__ __forceinline__ void zero_stage_tail(LDS_PTR(unsigned char) buf, int 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Sparse pages ("[DeepSeek-3] FlashMLA", section 11).  Page j of a query
+// token's key list is entries 64 j .. 64 j + 63 of its index list; entry e
+// names cache row e = page_id * 64 + offset.  A wave holds a page's 64
+// entries in one register (lane l: entry l), loaded one page ahead of the
+// page's copy by a plain load (the compiler waits for it where it is
+// first used, which is after the explicit wait that covers it).  An entry
+// is a key if it lies before the list's length and inside the pool; for
+// the others the copy reads pool row 0 instead (always in bounds), the row
+// is zeroed in LDS and its score masked.
+__device__ __forceinline__ int load_page_entries(const Params& p, int req, int j, int lane) {
+  const int e = min(kPage * j + lane, p.topk - 1);   // inside the list
+  return p.indices[(size_t)req * p.topk + e];
+}
+
+struct GatherPage {
+  unsigned long long mask;   // bit t: page token t is a key
+  // This lane's copy source for slice parity par (local token
+  // t = 8 par + lane / 8): cache row rel[par] + t, so that its byte address
+  // is kv + rel[par] * 1152 + the lane's dense slice offset.
+  int rel[2];
+};
+
+__device__ __forceinline__ GatherPage gather_page(const Params& p, int entry, int j, int L, int tok0, int lane) {
+  asm volatile("" : "+v"(entry));   // first use here, after the wait that covers the load
+  const bool key = kPage * j + lane < L && (unsigned)entry < (unsigned)p.kv_tokens;
+  const int row = key ? entry : 0;
+  GatherPage g;
+  g.mask = __ballot(key);
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int t = 8 * par + (lane >> 3);
+    g.rel[par] = __builtin_amdgcn_ds_bpermute((tok0 + t) << 2, row) - t;
+  }
+  return g;
+}
+
+// Copy slice i (block i / 2, tokens 8 (i % 2) .. + 7) of this wave's rows
+// of a sparse page: every lane has its own source row.
+template <bool kStream>
+__device__ __forceinline__ void issue_gather_slice(const Params& p, const GatherPage& g, const unsigned dma_off[2],
+                                                   unsigned stage_lds, int i) {
+  unsigned lane_off = dma_off[i & 1];
+  asm volatile("" : "+v"(lane_off));   // per copy (hoisted, 18 64-bit offsets would not fit in registers)
+  const unsigned long long a = (unsigned long long)(size_t)p.kv + (long long)g.rel[i & 1] * kRowBytes +
+                               (unsigned)(lane_off + (i >> 1) * 128);
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(stage_lds + (unsigned)i * 1024u);
+  if constexpr (kStream)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(a), "s"(m0) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(a), "s"(m0) : "memory");
+}
+
+template <bool kStream>
+__device__ __forceinline__ void issue_gather(const Params& p, const GatherPage& g, const unsigned dma_off[2],
+                                             unsigned stage_lds) {
+#pragma unroll
+  for (int i = 0; i < kStageSlices; ++i) issue_gather_slice<kStream>(p, g, dma_off, stage_lds, i);
+}
+
+// Zero the V part of this wave's slice rows whose bit in `keep` is clear
+// (bit t: local token t).
+__device__ __forceinline__ void zero_stage_rows(LDS_PTR(unsigned char) buf, unsigned keep, int lane) {
+  for (int u = lane; u < kWaveTokens * 64; u += 64) {
+    const int t = u >> 6, b = (u >> 3) & 7, c = u & 7;
+    if (!((keep >> t) & 1u)) *(LDS_PTR(u32x4))(buf + b * kStageBlock + t * 128 + c * 16) = u32x4{0, 0, 0, 0};
+  }
+}
+
 // Q^T fragments (B operand of 16x16x32): query row `row` (masked to zero when
 // >= R), dims 32 ks + 8 g .. + 7.
 __device__ __forceinline__ void load_q(bf16x8 (&qf)[kQkSteps], const Params& p, int req, int row, int g) {
@@ -260,10 +336,17 @@ __device__ __forceinline__ void merge_weights(const float (*st_m)[kRowGroup], co
 
 // Writes a finished row: lse (natural log) when the request is not split,
 // else the base-2 partial lse of slot `slot`.
+// lse is [batch, h_q, s_q]; request `req` is query token req % fold of
+// request req / fold (fold = 1 for dense decode).
+__device__ __forceinline__ size_t lse_index(const Params& p, int req, int row) {
+  const int b = req / p.fold, sv = req - b * p.fold;
+  const int s = row / p.h_q, hh = row - s * p.h_q;
+  return ((size_t)b * p.h_q + hh) * (size_t)(p.s_q * p.fold) + (size_t)s * p.fold + sv;
+}
+
 __device__ __forceinline__ void store_lse(const Params& p, int req, int row, bool split, int slot, float lse2) {
   if (!split) {
-    const int s = row / p.h_q, hh = row - s * p.h_q;
-    p.lse[((size_t)req * p.h_q + hh) * p.s_q + s] = lse2 * kLn2;
+    p.lse[lse_index(p, req, row)] = lse2 * kLn2;
   } else {
     p.lacc[(size_t)slot * p.R + row] = lse2;
   }
@@ -302,6 +385,18 @@ __device__ __forceinline__ PieceRange load_part(const Params& p, int part) {
 struct RequestMeta {
   int L, slot0, slot1, blk[3];
 };
+
+// Sparse decode: the length is the count of entries that count (topk, or
+// topk_length of the real request, clamped to [0, topk]); no block ids.
+__device__ __forceinline__ RequestMeta load_request_sparse(const Params& p, int req) {
+  RequestMeta m;
+  m.L = p.topk;
+  if (p.topk_len) m.L = min(max(ld_uniform(p.topk_len + req / p.fold), 0), p.topk);
+  m.slot0 = ld_uniform(p.num_splits + req);
+  m.slot1 = ld_uniform(p.num_splits + req + 1);
+  m.blk[0] = m.blk[1] = m.blk[2] = 0;
+  return m;
+}
 
 __device__ __forceinline__ RequestMeta load_request(const Params& p, int req, int lo) {
   const int32_t* bt = p.block_table + (size_t)req * p.max_blocks;
@@ -375,6 +470,9 @@ __device__ __forceinline__ float row_sum4(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// kSparse: the key lists of sparse decode instead of block-table pages
+// (gathered copies, per-token key masks).
+template <bool kSparse>
 __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kPageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char pbuf[kSmallPBytes];
@@ -436,7 +534,13 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
 
   for (int req = pr.begin_req; req <= pr.end_req; ++req) {
     const int lo = (req == pr.begin_req) ? pr.begin_blk : 0;
-    const RequestMeta m = load_request(p, req, lo);
+    const RequestMeta m = kSparse ? load_request_sparse(p, req) : load_request(p, req, lo);
+    // Sparse: the entries of pages lo .. lo + 2, read with the metadata.
+    int ent[3] = {0, 0, 0};
+    if constexpr (kSparse) {
+#pragma unroll
+      for (int i = 0; i < 3; ++i) ent[i] = load_page_entries(p, req, lo + i, lane);
+    }
     const int L = m.L;
     const int nblk = (L + kPage - 1) / kPage;
     const int hi = (req == pr.end_req) ? pr.end_blk : nblk;
@@ -459,13 +563,29 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
     // are explicit copies with explicit waits: no compiler-tracked load may
     // be outstanding while page copies are in flight.)
     bf16x8 qf[kQkSteps];
+    // Sparse: the copy sources and key masks of pages lo and lo + 1 (kept
+    // for a restart), computed before any copy is in flight, so that the
+    // wait for the entries waits for nothing else.
+    GatherPage g0{}, g1{};
+    if constexpr (kSparse) {
+      g0 = gather_page(p, ent[0], lo, L, tok0, lane);
+      g1 = gather_page(p, ent[1], lo + 1, L, tok0, lane);
+    }
     {
       const unsigned char* qrows = uniform_ptr(p.q + (size_t)req * p.R * kRowBytes);
       const unsigned qslice = (unsigned)(size_t)lds + kPageBytes;
       for (int i = wave; i < kStageSlices; i += 4) issue_stage_slice<false>(qrows, qslice, q_dma_off, i);
     }
     for (int attempt = 0;; ++attempt) {
-      if (lo < hi) issue_stage<true>(page_rows(m.blk[0]), wslice, dma_off);
+      // Sparse: key masks of the current page, of page lo + 1, and of the
+      // page whose copy was issued last; the entries of the next page to copy.
+      unsigned long long mk_cur = g0.mask, mk_lo1 = g1.mask, mk_pending = 0;
+      int ent_next = ent[2];
+      if constexpr (kSparse) {
+        if (lo < hi) issue_gather<true>(p, g0, dma_off, wslice);
+      } else {
+        if (lo < hi) issue_stage<true>(page_rows(m.blk[0]), wslice, dma_off);
+      }
       if (attempt == 0) {
         if (lo < hi)
           wait_vmcnt<kStageSlices>();   // this wave's pieces of Q (the first page may still be in flight)
@@ -482,7 +602,12 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
         }
         lds_barrier();                  // every wave has read Q: stage 1 is free again
       }
-      if (lo + 1 < hi) issue_stage<true>(page_rows(m.blk[1]), wslice + kPageBytes, dma_off);
+      if (lo + 1 < hi) {
+        if constexpr (kSparse)
+          issue_gather<true>(p, g1, dma_off, wslice + kPageBytes);
+        else
+          issue_stage<true>(page_rows(m.blk[1]), wslice + kPageBytes, dma_off);
+      }
       int next_blk = m.blk[2];   // block ids are read one page ahead of their copy
 
 #pragma unroll
@@ -500,15 +625,27 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
           wait_vmcnt<kStageSlices>();
         else
           wait_vmcnt<0>();
-        const int valid = min(kPage, L - j * kPage);
-        if (valid - tok0 < kWaveTokens) zero_stage_tail(buf + wave * kStageBytes, valid - tok0, lane);
+        if constexpr (kSparse) {
+          const unsigned keep = (unsigned)(mk_cur >> tok0) & 0xFFFFu;
+          if (keep != 0xFFFFu) zero_stage_rows(buf + wave * kStageBytes, keep, lane);
+        } else {
+          const int valid = min(kPage, L - j * kPage);
+          if (valid - tok0 < kWaveTokens) zero_stage_tail(buf + wave * kStageBytes, valid - tok0, lane);
+        }
         lds_barrier();   // page j is visible; every wave is past page j - 1
         // Page j + 1 goes to the stage page j - 1 held (pages lo, lo + 1 were
         // issued ahead of the loop).  (A third page in flight from the start,
         // held in registers, was measured slower: every page then lands late.)
         if (j > lo && j + 1 < hi) {
-          issue_stage<true>(page_rows(next_blk), wslice + ((j + 1 - lo) & 1) * kPageBytes, dma_off);
-          next_blk = ld_uniform(bt + min(j + 2, p.max_blocks - 1));
+          if constexpr (kSparse) {
+            const GatherPage gn = gather_page(p, ent_next, j + 1, L, tok0, lane);
+            issue_gather<true>(p, gn, dma_off, wslice + ((j + 1 - lo) & 1) * kPageBytes);
+            mk_pending = gn.mask;
+            ent_next = load_page_entries(p, req, j + 2, lane);
+          } else {
+            issue_stage<true>(page_rows(next_blk), wslice + ((j + 1 - lo) & 1) * kPageBytes, dma_off);
+            next_blk = ld_uniform(bt + min(j + 2, p.max_blocks - 1));
+          }
         }
 
         // ---- S^T (this wave's 16 tokens x 16 rows) = K Q^T, three chains.
@@ -526,11 +663,13 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
 
         // ---- softmax against the common reference (base 2).
         const int vis = row_keys(p, L, c16) - j * kPage;   // keys of this page row c16 sees (may be <= 0 or > 64)
+        const unsigned kw = (unsigned)(mk_cur >> tok0) & 0xFFFFu;   // sparse: keys among this wave's tokens
         float x[4], mloc = -INFINITY;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           // (softmax_scale >= 0, so masking before or after scaling is the same.)
-          x[v] = tok0 + 4 * g + v < vis ? sv[v] * p.scale_log2 : -INFINITY;
+          const bool key = kSparse ? ((kw >> (4 * g + v)) & 1u) != 0 : tok0 + 4 * g + v < vis;
+          x[v] = key ? sv[v] * p.scale_log2 : -INFINITY;
           mloc = fmaxf(mloc, x[v]);
         }
         mloc = row_max4(mloc);   // this wave's tokens of row c16
@@ -585,6 +724,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
             __builtin_amdgcn_sched_barrier(0);
           }
         }
+        if constexpr (kSparse) mk_cur = j == lo ? mk_lo1 : mk_pending;
       }
       wait_vmcnt<0>();
       if (!restart) break;
@@ -904,7 +1044,9 @@ __device__ __forceinline__ void wide_acc_settle() {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
-template <bool kStream>
+// kSparse: the key lists of sparse decode instead of block-table pages
+// (gathered copies, per-token key masks).
+template <bool kStream, bool kSparse>
 __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
   // Two page stages (4 slices of 18 KiB each) and the P^T exchange buffer: 160 KiB.
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kPageBytes];
@@ -954,7 +1096,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
 
   for (int req = pr.begin_req; req <= pr.end_req; ++req) {
     const int lo = (req == pr.begin_req) ? pr.begin_blk : 0;
-    const RequestMeta m = load_request(p, req, lo);
+    const RequestMeta m = kSparse ? load_request_sparse(p, req) : load_request(p, req, lo);
     const int L = m.L;
     const int nblk = (L + kPage - 1) / kPage;
     const int hi = (req == pr.end_req) ? pr.end_blk : nblk;
@@ -964,11 +1106,24 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
     auto page_rows = [&](int blk) {
       return uniform_ptr(p.kv + (size_t)blk * kPageBytes + (size_t)tok0 * kRowBytes);
     };
-
     f32x16 o[kWideTiles][4];   // O^T tiles: row tile x this wave's 4 column tiles
     float m_ref = -INFINITY, l_run = 0.f;
     for (int attempt = 0;; ++attempt) {
-      if (lo < hi) issue_stage<kStream>(page_rows(m.blk[0]), lds0 + wave * kStageBytes, dma_off);
+      // Sparse: the entries of pages lo and lo + 1 (read with the metadata on
+      // the first attempt, again on a restart rather than kept live).
+      int ent_next = 0;
+      GatherPage g0{};
+      if constexpr (kSparse) {
+        const int ent0 = load_page_entries(p, req, lo, lane);
+        ent_next = load_page_entries(p, req, lo + 1, lane);
+        g0 = gather_page(p, ent0, lo, L, tok0, lane);
+      }
+      if (lo < hi) {
+        if constexpr (kSparse)
+          issue_gather<kStream>(p, g0, dma_off, lds0 + wave * kStageBytes);
+        else
+          issue_stage<kStream>(page_rows(m.blk[0]), lds0 + wave * kStageBytes, dma_off);
+      }
       // Q^T fragments (B operand): row r, dims 16 ks + 8 h .. + 7.
       bf16x8 qf[kQkSteps16];
       {
@@ -993,6 +1148,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
       float l_part[4] = {0.f, 0.f, 0.f, 0.f};
       bool restart = false;
       int next_blk = m.blk[1];   // copied only if lo + 1 < hi
+      unsigned long long mk_cur = g0.mask;   // sparse: key mask of page j
 
       for (int j = lo; j < hi; ++j) {
         const int stage = (j - lo) & 1;
@@ -1002,8 +1158,13 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
         // every wave is past the previous page's PV: P buffer and the other
         // stage are free).
         wait_vmcnt<0>();
-        const int valid = min(kPage, L - j * kPage);
-        if (valid < kPage) zero_stage_tail(buf + wave * kStageBytes, valid - tok0, lane);
+        if constexpr (kSparse) {
+          const unsigned keep = (unsigned)(mk_cur >> tok0) & 0xFFFFu;
+          if (keep != 0xFFFFu) zero_stage_rows(buf + wave * kStageBytes, keep, lane);
+        } else {
+          const int valid = min(kPage, L - j * kPage);
+          if (valid < kPage) zero_stage_tail(buf + wave * kStageBytes, valid - tok0, lane);
+        }
         lds_barrier();
         // The next page's 18 slices go to the other stage during QK^T (none
         // on the last page: re-copying the current page instead, branch-free,
@@ -1011,8 +1172,19 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
         const bool has_next = j + 1 < hi;   // uniform
         const unsigned char* nrows =
             uniform_ptr(p.kv + (size_t)next_blk * kPageBytes + (size_t)tok0 * kRowBytes);
-        next_blk = ld_uniform(bt + (j + 2 < hi ? j + 2 : j));
         const unsigned nlds = lds0 + (stage ^ 1) * kPageBytes + wave * kStageBytes;
+        unsigned long long mk_next = 0;
+        if constexpr (kSparse) {
+          // Sparse pages: the next page's gathered copy is issued here at
+          // once (its per-lane 64-bit addresses do not fit in the register
+          // budget of the QK^T loop below).
+          const GatherPage gn = gather_page(p, ent_next, j + 1, L, tok0, lane);
+          mk_next = gn.mask;
+          if (has_next) issue_gather<kStream>(p, gn, dma_off, nlds);
+          ent_next = load_page_entries(p, req, j + 2, lane);   // covered by the next page's wait
+        } else {
+          next_blk = ld_uniform(bt + (j + 2 < hi ? j + 2 : j));
+        }
 
         // ---- S^T (64 tokens x this wave's 32 rows) in two 32-token tiles.
         // The softmax of each tile rides along the next MFMA stream (tile 0
@@ -1031,14 +1203,24 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
         // are masked in both passes.
         auto softmax_piece = [&](int tt, int k, f32x16& sacc) {
           WideSoftmax& t = sm[tt];
-          const bool ragged = vis_min < 32 * tt + 32;   // uniform
+          const bool ragged = kSparse ? (unsigned)(mk_cur >> (32 * tt)) != 0xFFFFFFFFu   // uniform
+                                      : vis_min < 32 * tt + 32;
           // Element v of the tile is a real token.  Only evaluated inside the
           // ragged branches: `lim_in` is re-materialised there so that the
           // compares cannot be hoisted onto the full-tile path.
-          auto ok = [&](int v, int lim_in) { return 32 * tt + 8 * (v >> 2) + (v & 3) < lim_in; };
+          auto ok = [&](int v, int lim_in) {
+            if constexpr (kSparse)
+              return ((unsigned)lim_in >> (8 * (v >> 2) + (v & 3))) & 1u;
+            else
+              return 32 * tt + 8 * (v >> 2) + (v & 3) < lim_in;
+          };
           auto branch_lim = [&]() {
             int l2;
-            asm volatile("v_mov_b32 %0, %1 ; ragged tile" : "=v"(l2) : "v"(lim));
+            if constexpr (kSparse)
+              // this lane's 16 tokens of the tile: bits 8 (v / 4) + v % 4
+              asm volatile("v_mov_b32 %0, %1 ; ragged tile" : "=v"(l2) : "v"((unsigned)(mk_cur >> (32 * tt + 4 * h))));
+            else
+              asm volatile("v_mov_b32 %0, %1 ; ragged tile" : "=v"(l2) : "v"(lim));
             return l2;
           };
           if (k == 0) {
@@ -1116,7 +1298,8 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
           for (int ks = 0; ks < kQkSteps16; ++ks) {
             qk_mfma(sacc[tt], kf[ks % kWideQkLead], qf[ks], ks == 0);
             if (ks + kWideQkLead < kQkSteps16) kf[ks % kWideQkLead] = kread(ks + kWideQkLead);
-            if (ks % 4 == 0 && has_next) issue_stage_slice<kStream>(nrows, nlds, dma_off, 9 * tt + ks / 4);
+            if constexpr (!kSparse)
+              if (ks % 4 == 0 && has_next) issue_stage_slice<kStream>(nrows, nlds, dma_off, 9 * tt + ks / 4);
             // Tile 0's softmax: one piece every other step from step 1.
             if (tt == 1 && ks == 1) wide_acc_settle();
             if (tt == 1 && ks % 2 == 1 && ks / 2 < kWideSoftmaxPieces) softmax_piece(0, ks / 2, sacc[0]);
@@ -1177,6 +1360,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
         pv_block(2, false);
 #pragma unroll
         for (int w = 0; w < kWideTiles; ++w) restart |= attempt == 0 && (flags[w] >> 15) != 0;
+        if constexpr (kSparse) mk_cur = mk_next;
       }
       wait_vmcnt<0>();   // no copy is outstanding (kept for the restart path's refill)
       wide_acc_settle();
@@ -1278,10 +1462,7 @@ __device__ __forceinline__ void combine_store(const Params& p, int req, int row,
     w[2 + e] = (unsigned)f32_to_bf16(a1[2 * e] * inv) | ((unsigned)f32_to_bf16(a1[2 * e + 1] * inv) << 16);
   }
   *(u32x4*)o = w;
-  if (lane == 0) {
-    const int sq = row / p.h_q, hh = row - sq * p.h_q;
-    p.lse[((size_t)req * p.h_q + hh) * p.s_q + sq] = l > 0.f ? (M + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
-  }
+  if (lane == 0) p.lse[lse_index(p, req, row)] = l > 0.f ? (M + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
 }
 
 __global__ void __launch_bounds__(kCombineWaves * 64) mla_combine_kernel(Params p) {
@@ -1506,22 +1687,28 @@ extern "C" int mla_plan(const int32_t* cache_seqlens, int batch, int num_parts, 
 // what a piece costs beyond its pages: the Q load and the first page's
 // latency in its prologue, the state merge and the output or partial store
 // in its epilogue, and for a split request its share of the combine.
-static int policy(const int32_t* seqlens, int batch, int h_q, int s_q, int* num_cus, int* parts, int* F) {
-  if (batch <= 0 || h_q <= 0 || s_q <= 0 || !seqlens)
-    return set_error(MLA_ERR_INVALID, "mla_get_metadata: batch=%d h_q=%d s_q=%d seqlens=%p", batch, h_q, s_q,
-                     (const void*)seqlens);
+// Parts and overhead for a launch geometry (CU count queried if <= 0);
+// `wide`: the 128-row kernel runs (R >= 128, or sparse decode above 16 rows).
+static int policy_for(const Geometry& g, bool wide, int* num_cus, int* parts, int* F) {
   if (*num_cus <= 0) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return set_error(MLA_ERR_HIP, "mla_get_metadata: cannot query the CU count");
   }
-  const Geometry g = geometry(h_q, s_q);
   *parts = *num_cus / g.row_groups;
   if (*parts < 1) *parts = 1;
   // Per-piece overhead in pages (prologue, epilogue, partial write + merge), measured per kernel.
-  *F = g.R <= kSmallRows ? 3 : g.R >= kWideRows ? 4 : 2;
+  *F = g.R <= kSmallRows ? 3 : wide ? 4 : 2;
   return MLA_OK;
+}
+
+static int policy(const int32_t* seqlens, int batch, int h_q, int s_q, int* num_cus, int* parts, int* F) {
+  if (batch <= 0 || h_q <= 0 || s_q <= 0 || !seqlens)
+    return set_error(MLA_ERR_INVALID, "mla_get_metadata: batch=%d h_q=%d s_q=%d seqlens=%p", batch, h_q, s_q,
+                     (const void*)seqlens);
+  const Geometry g = geometry(h_q, s_q);
+  return policy_for(g, g.R >= kWideRows, num_cus, parts, F);
 }
 
 extern "C" int mla_max_parts(const int32_t* cache_seqlens, int batch, int h_q, int s_q, int num_cus,
@@ -1570,6 +1757,43 @@ extern "C" int mla_get_metadata_device(const int32_t* cache_seqlens_dev, int bat
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(MLA_ERR_HIP, "mla_get_metadata_device: launch: %s", hipGetErrorString(e));
   *num_parts_out = parts;
+  return MLA_OK;
+}
+
+// Sparse decode ("[DeepSeek-3] FlashMLA", section 11): the planner walks
+// one "request" per (request, query token), whose length is the number of
+// entries of its index list that count (the pages' planner counts blocks
+// from topk for sparse decode).
+extern "C" int mla_max_parts_sparse(int batch, int s_q, int h_q, int num_cus) {
+  if (batch <= 0 || s_q <= 0 || h_q <= 0)
+    return set_error(MLA_ERR_INVALID, "mla_max_parts_sparse: batch=%d s_q=%d h_q=%d", batch, s_q, h_q);
+  const Geometry g = geometry_sparse(h_q);
+  int parts, F;
+  const int rc = policy_for(g, g.R > kSmallRows, &num_cus, &parts, &F);
+  return rc ? rc : parts;
+}
+
+extern "C" int mla_get_metadata_sparse(const int32_t* topk_length, int batch, int s_q, int h_q, int topk,
+                                       int num_cus, int32_t* sched_out, int max_parts, int32_t* num_splits_out,
+                                       int* num_parts_out, int* total_splits_out) {
+  if (batch <= 0 || s_q <= 0 || h_q <= 0 || topk <= 0 || (long long)batch * s_q > (1 << 30))
+    return set_error(MLA_ERR_INVALID, "mla_get_metadata_sparse: batch=%d s_q=%d h_q=%d topk=%d", batch, s_q, h_q,
+                     topk);
+  if (!sched_out || !num_splits_out || !num_parts_out || !total_splits_out)
+    return set_error(MLA_ERR_INVALID, "mla_get_metadata_sparse: null pointer argument");
+  const Geometry g = geometry_sparse(h_q);
+  int parts, F;
+  int rc = policy_for(g, g.R > kSmallRows, &num_cus, &parts, &F);
+  if (rc) return rc;
+  const int n = batch * s_q;
+  std::vector<int32_t> lens(n);
+  for (int b = 0; b < batch; ++b) {
+    const int L = topk_length ? std::min(std::max(topk_length[b], 0), topk) : topk;
+    for (int s = 0; s < s_q; ++s) lens[(size_t)b * s_q + s] = L;
+  }
+  rc = plan(lens.data(), n, parts, F, 0, sched_out, max_parts, num_splits_out, num_parts_out);
+  if (rc) return rc;
+  *total_splits_out = num_splits_out[n];
   return MLA_OK;
 }
 
@@ -1640,6 +1864,41 @@ static hipEvent_t* profile_slot() {
 
 constexpr int kCombineMaxGrid = 2048;   // about one round of resident workgroups
 
+// Enqueues the split-KV kernel picked by the row count (and, for sparse
+// decode, its gather variant), then the combine kernel.
+static int launch_decode(Params& prm, const Geometry& g, bool sparse, hipStream_t st, const char* who) {
+  hipEvent_t* ev = profile_slot();
+  void* args[] = {&prm};
+  const void* main_fn;
+  // The XCD-aware block mapping (map_block) needs 8 * row_groups * ceil(parts / 8) workgroups.
+  const int grid = 8 * g.row_groups * ((prm.num_parts + 7) / 8);
+  if (g.R <= kSmallRows) {
+    main_fn = sparse ? (const void*)mla_splitkv_small_kernel<true> : (const void*)mla_splitkv_small_kernel<false>;
+  } else if (g.R >= kWideRows || sparse) {
+    // Row groups of one part share pages through L2 (cached copies); a single
+    // group streams every page once (nontemporal copies).
+    if (g.row_groups == 1)
+      main_fn = sparse ? (const void*)mla_splitkv_wide_kernel<true, true> : (const void*)mla_splitkv_wide_kernel<true, false>;
+    else
+      main_fn = sparse ? (const void*)mla_splitkv_wide_kernel<false, true> : (const void*)mla_splitkv_wide_kernel<false, false>;
+  } else {
+    main_fn = (const void*)mla_splitkv_kernel;
+  }
+  // Plain launches unless profiling (these are what stream capture records).
+  hipError_t e = ev ? hipExtLaunchKernel(main_fn, dim3(grid), dim3(256), args, 0, st, ev[0], ev[1], 0)
+                    : hipLaunchKernel(main_fn, dim3(grid), dim3(256), args, 0, st);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return set_error(MLA_ERR_HIP, "%s: main kernel launch: %s", who, hipGetErrorString(e));
+  const long long pairs = (long long)prm.batch * g.R;
+  const int cgrid = (int)(pairs < kCombineMaxGrid ? pairs : kCombineMaxGrid);
+  e = ev ? hipExtLaunchKernel((const void*)mla_combine_kernel, dim3(cgrid), dim3(kCombineWaves * 64), args, 0, st,
+                              ev[2], ev[3], 0)
+         : hipLaunchKernel((const void*)mla_combine_kernel, dim3(cgrid), dim3(kCombineWaves * 64), args, 0, st);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return set_error(MLA_ERR_HIP, "%s: combine launch: %s", who, hipGetErrorString(e));
+  return MLA_OK;
+}
+
 extern "C" int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* block_table,
                               const int32_t* cache_seqlens, int batch, int s_q, int h_q, int num_blocks,
                               int max_blocks_per_seq, float softmax_scale, int causal, const int32_t* sched,
@@ -1681,34 +1940,61 @@ extern "C" int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t
   prm.row_groups = g.row_groups;
   prm.causal = causal;
   prm.scale_log2 = softmax_scale * kLog2e;
+  prm.indices = nullptr;
+  prm.topk_len = nullptr;
+  prm.topk = 0;
+  prm.kv_tokens = num_blocks * kPage;
+  prm.fold = 1;
 
-  hipStream_t st = (hipStream_t)stream;
-  hipEvent_t* ev = profile_slot();
-  void* args[] = {&prm};
-  const void* main_fn;
-  int grid;
-  // The XCD-aware block mapping (map_block) needs 8 * row_groups * ceil(parts / 8) workgroups.
-  grid = 8 * g.row_groups * ((num_parts + 7) / 8);
-  if (g.R <= kSmallRows) {
-    main_fn = (const void*)mla_splitkv_small_kernel;
-  } else if (g.R >= kWideRows) {
-    // Row groups of one part share pages through L2 (cached copies); a single
-    // group streams every page once (nontemporal copies).
-    main_fn = g.row_groups == 1 ? (const void*)mla_splitkv_wide_kernel<true> : (const void*)mla_splitkv_wide_kernel<false>;
-  } else {
-    main_fn = (const void*)mla_splitkv_kernel;
-  }
-  // Plain launches unless profiling (these are what stream capture records).
-  hipError_t e = ev ? hipExtLaunchKernel(main_fn, dim3(grid), dim3(256), args, 0, st, ev[0], ev[1], 0)
-                    : hipLaunchKernel(main_fn, dim3(grid), dim3(256), args, 0, st);
-  if (e == hipSuccess) e = hipGetLastError();
-  if (e != hipSuccess) return set_error(MLA_ERR_HIP, "mla_decode_fwd: main kernel launch: %s", hipGetErrorString(e));
-  const long long pairs = (long long)batch * g.R;
-  const int cgrid = (int)(pairs < kCombineMaxGrid ? pairs : kCombineMaxGrid);
-  e = ev ? hipExtLaunchKernel((const void*)mla_combine_kernel, dim3(cgrid), dim3(kCombineWaves * 64), args, 0, st,
-                              ev[2], ev[3], 0)
-         : hipLaunchKernel((const void*)mla_combine_kernel, dim3(cgrid), dim3(kCombineWaves * 64), args, 0, st);
-  if (e == hipSuccess) e = hipGetLastError();
-  if (e != hipSuccess) return set_error(MLA_ERR_HIP, "mla_decode_fwd: combine launch: %s", hipGetErrorString(e));
-  return MLA_OK;
+  return launch_decode(prm, g, false, (hipStream_t)stream, "mla_decode_fwd");
 }
+
+extern "C" int mla_decode_sparse_fwd(const void* q, const void* kv_cache, const int32_t* indices,
+                                     const int32_t* topk_length, int batch, int s_q, int h_q, int num_blocks,
+                                     int topk, float softmax_scale, const int32_t* sched, int num_parts,
+                                     const int32_t* num_splits, void* workspace, size_t workspace_bytes, void* out,
+                                     float* lse, void* stream) {
+  if (!q || !kv_cache || !indices || !sched || !num_splits || !out || !lse)
+    return set_error(MLA_ERR_INVALID, "mla_decode_sparse_fwd: null pointer argument");
+  if (batch <= 0 || s_q <= 0 || h_q <= 0 || num_blocks <= 0 || num_blocks > (1 << 24) || topk <= 0 ||
+      num_parts <= 0 || (long long)batch * s_q > (1 << 30))
+    return set_error(MLA_ERR_INVALID, "mla_decode_sparse_fwd: batch=%d s_q=%d h_q=%d num_blocks=%d topk=%d num_parts=%d",
+                     batch, s_q, h_q, num_blocks, topk, num_parts);
+  if (!std::isfinite(softmax_scale) || softmax_scale < 0.f)
+    return set_error(MLA_ERR_INVALID, "mla_decode_sparse_fwd: softmax_scale must be finite and >= 0");
+  const Geometry g = geometry_sparse(h_q);
+  const int n = batch * s_q;   // one split-KV "request" per (request, query token)
+  const int slots = num_parts + n - 1;
+  const size_t need = mla_workspace_bytes(slots, h_q, 1);
+  if (!workspace || workspace_bytes < need)
+    return set_error(MLA_ERR_WORKSPACE, "mla_decode_sparse_fwd: workspace %zu bytes < %zu needed", workspace_bytes,
+                     need);
+  Params prm;
+  prm.q = (const unsigned char*)q;
+  prm.kv = (const unsigned char*)kv_cache;
+  prm.block_table = nullptr;
+  prm.seqlens = nullptr;
+  prm.sched = sched;
+  prm.num_splits = num_splits;
+  prm.out = (unsigned short*)out;
+  prm.lse = lse;
+  const size_t rows = (size_t)slots * g.R;
+  prm.oacc = (float*)workspace;
+  prm.lacc = (float*)((char*)workspace + align256(rows * kDv * sizeof(float)));
+  prm.batch = n;
+  prm.R = g.R;
+  prm.h_q = h_q;
+  prm.s_q = 1;
+  prm.max_blocks = 1;
+  prm.num_parts = num_parts;
+  prm.row_groups = g.row_groups;
+  prm.causal = 0;
+  prm.scale_log2 = softmax_scale * kLog2e;
+  prm.indices = indices;
+  prm.topk_len = topk_length;
+  prm.topk = topk;
+  prm.kv_tokens = num_blocks * kPage;
+  prm.fold = s_q;
+  return launch_decode(prm, g, true, (hipStream_t)stream, "mla_decode_sparse_fwd");
+}
+

@@ -35,4 +35,14 @@ inline Geometry geometry(int h_q, int s_q) {
   return g;
 }
 
+// Sparse decode: every (request, query token) has its own key list, so a
+// "request" of the split-KV kernels is one (request, query token) with
+// R = h_q rows; above 16 rows it takes the 128-row kernel.
+inline Geometry geometry_sparse(int h_q) {
+  Geometry g;
+  g.R = h_q;
+  g.row_groups = g.R <= kSmallRows ? 1 : (g.R + kWideRows - 1) / kWideRows;
+  return g;
+}
+
 }  // namespace mla

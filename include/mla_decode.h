@@ -144,7 +144,7 @@ size_t mla_workspace_bytes(int total_splits, int h_q, int s_q);
 
 /*
  * mla_decode_fwd — dense MLA decode forward (the pages' flash_mla_with_kvcache,
- * dense path, non-causal, bf16, one KV head, head_dim_v = 512).
+ * dense path, bf16, one KV head, head_dim_v = 512).
  *
  *   q             device bf16 [batch, s_q, h_q, 576]
  *   kv_cache      device bf16 [num_blocks, 64, 1, 576]; K = all 576 dims,
@@ -181,6 +181,72 @@ int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* block_tab
                    int max_blocks_per_seq, float softmax_scale, int causal, const int32_t* sched,
                    int num_parts, const int32_t* num_splits, void* workspace,
                    size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/*
+ * Sparse (top-k) decode ("[DeepSeek-3] FlashMLA", section 11): query token s
+ * of request b attends only to the cache rows its index list names,
+ *
+ *   indices[b][s][i] = page_id * 64 + offset   (cache row `offset` of block
+ *                                               `page_id`; no block table)
+ *
+ * with the dense path's score, softmax and output definitions.  Readings of
+ * points the pages leave open: the list is a multiset (a row named twice is
+ * two keys); only the first topk_length[b] entries of request b's lists
+ * count (all topk when topk_length is NULL; values are clamped to
+ * [0, topk]); an entry outside [0, num_blocks * 64), -1 padding for
+ * example, names no key and is never dereferenced; a query token left with
+ * no key gets out = 0 and lse = -inf.  There is no causal mask (the
+ * selector decides what each token sees).
+ *
+ * The split-KV kernels treat each (request, query token) as one request of
+ * h_q query rows whose 64-token "pages" are consecutive runs of its list, so
+ * the planner walks batch * s_q lengths.
+ */
+
+/* Part count of the sparse planner policy (the max_parts a plan needs). */
+int mla_max_parts_sparse(int batch, int s_q, int h_q, int num_cus);
+
+/*
+ * mla_get_metadata_sparse — plan one sparse decode step (host only).
+ *
+ *   topk_length    host int32 [batch] or NULL
+ *   topk           entries per index list (> 0)
+ *   num_cus        CUs to fill; 0 = query the current HIP device
+ *   sched_out      host int32 [max_parts * 8]; max_parts >= mla_max_parts_sparse(...)
+ *   num_splits_out host int32 [batch * s_q + 1]: prefix of pieces over
+ *                  (request, query token) pairs in the order b * s_q + s
+ *   num_parts_out, total_splits_out  parts written, partial slots needed
+ * Errors: MLA_ERR_INVALID, MLA_ERR_CAPACITY, MLA_ERR_HIP (device query).
+ */
+int mla_get_metadata_sparse(const int32_t* topk_length, int batch, int s_q, int h_q, int topk, int num_cus,
+                            int32_t* sched_out, int max_parts, int32_t* num_splits_out, int* num_parts_out,
+                            int* total_splits_out);
+
+/*
+ * mla_decode_sparse_fwd — sparse MLA decode forward (the pages'
+ * flash_mla_with_kvcache with indices, bf16 cache, head_dim_v = 512).
+ *
+ *   q             device bf16 [batch, s_q, h_q, 576]
+ *   kv_cache      device bf16 [num_blocks, 64, 1, 576]; num_blocks <= 2^24
+ *   indices       device int32 [batch, s_q, topk]
+ *   topk_length   device int32 [batch] or NULL
+ *   softmax_scale finite and >= 0
+ *   sched, num_parts, num_splits  from mla_get_metadata_sparse with the same
+ *                 batch, s_q, h_q, topk and topk_length
+ *   workspace     device, >= mla_workspace_bytes(num_parts + batch * s_q - 1, h_q, 1)
+ *   out           device bf16 [batch, s_q, h_q, 512] (written)
+ *   lse           device fp32 [batch, h_q, s_q] (written)
+ *   stream        hipStream_t (NULL = the null stream)
+ * Enqueues the split-KV kernel (gathered copies; h_q <= 16 rows in one
+ * workgroup, otherwise 128-row workgroups) and the combine kernel; returns
+ * without synchronising and allocates nothing.  The device topk_length must
+ * match the plan (not checked on the device).
+ * Errors: MLA_ERR_INVALID, MLA_ERR_WORKSPACE, MLA_ERR_HIP.
+ */
+int mla_decode_sparse_fwd(const void* q, const void* kv_cache, const int32_t* indices, const int32_t* topk_length,
+                          int batch, int s_q, int h_q, int num_blocks, int topk, float softmax_scale,
+                          const int32_t* sched, int num_parts, const int32_t* num_splits, void* workspace,
+                          size_t workspace_bytes, void* out, float* lse, void* stream);
 
 /*
  * Kernel timing for benchmarks.  mla_profile_start(max_calls) makes the next

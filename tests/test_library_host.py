@@ -124,3 +124,42 @@ def test_device_planner_argument_errors_return_codes_without_launching():
     assert rc == -2 and b"max_parts" in L.mla_last_error()
     rc = L.mla_get_metadata_device(dummy, 4, 16, 1, 5000, dummy, 5000, dummy, ctypes.byref(n), None)
     assert rc == -1 and b"4096" in L.mla_last_error()
+
+
+@pytest.mark.parametrize("h_q,s_q,topk_length", [(16, 1, None), (16, 2, [100, 0, 5000, 64]), (64, 2, None),
+                                                 (128, 2, [3000, 1, -5, 4096]), (256, 1, [64, 65, 129, 2048])])
+def test_sparse_policy_matches_reference_plan_over_token_lists(h_q, s_q, topk_length):
+    """The sparse plan walks one request per (request, query token), of length
+    the entries that count, with the 128-row kernel's policy above 16 rows."""
+    b, topk = 4, 4096
+    sched, ns, total = mla.get_mla_metadata_sparse_host(topk_length, b, s_q, h_q, topk, num_cus=256)
+    lens = []
+    for i in range(b):
+        n = topk if topk_length is None else min(max(topk_length[i], 0), topk)
+        lens += [n] * s_q
+    groups = 1 if h_q <= 16 else -(-h_q // 128)
+    F = 3 if h_q <= 16 else 4
+    s_ref, n_ref = oracle.plan(np.array(lens, dtype=np.int32), num_parts=max(1, 256 // groups), fixed_overhead=F)
+    assert np.array_equal(sched, s_ref) and np.array_equal(ns, n_ref) and total == n_ref[-1]
+
+
+def test_sparse_argument_errors_return_codes_without_launching():
+    L = mla.lib()
+    dummy = ctypes.c_void_p(16)   # never dereferenced: every check fails before any launch
+    rc = L.mla_decode_sparse_fwd(None, dummy, dummy, None, 1, 1, 16, 1, 64, 0.1, dummy, 1, dummy, dummy, 1 << 30,
+                                 dummy, dummy, None)
+    assert rc == -1 and b"null" in L.mla_last_error()
+    rc = L.mla_decode_sparse_fwd(dummy, dummy, dummy, None, 1, 1, 16, 1, 0, 0.1, dummy, 1, dummy, dummy, 1 << 30,
+                                 dummy, dummy, None)
+    assert rc == -1 and b"topk=0" in L.mla_last_error()
+    rc = L.mla_decode_sparse_fwd(dummy, dummy, dummy, None, 1, 1, 16, (1 << 24) + 1, 64, 0.1, dummy, 1, dummy, dummy,
+                                 1 << 30, dummy, dummy, None)
+    assert rc == -1 and b"num_blocks" in L.mla_last_error()
+    rc = L.mla_decode_sparse_fwd(dummy, dummy, dummy, None, 2, 2, 16, 8, 64, -1.0, dummy, 3, dummy, dummy, 1 << 30,
+                                 dummy, dummy, None)
+    assert rc == -1 and b"softmax_scale" in L.mla_last_error()
+    rc = L.mla_decode_sparse_fwd(dummy, dummy, dummy, None, 2, 2, 16, 8, 64, 0.1, dummy, 3, dummy, dummy, 100,
+                                 dummy, dummy, None)
+    assert rc == -3 and b"workspace" in L.mla_last_error()
+    with pytest.raises(mla.MlaError, match="topk"):
+        mla.get_mla_metadata_sparse_host(None, 2, 1, 16, 0, num_cus=8)
