@@ -68,17 +68,65 @@ def measured_traffic(config_name: str):
     return e.get("bytes_per_launch")
 
 
-def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6, causal: bool = False):
-    """Times one workload three ways:
+def time_steps(step, rot: int, steps: int, warmup: int):
+    """Times decode calls ``step(i)`` (i picks the rotating input copy):
 
-    * graph: ``rot`` decode steps (one per rotating copy of q and the KV
-      pool) captured once in a HIP graph and replayed -- how serving engines
-      run a decode step, and the whole-job throughput reported as ``value``;
+    * graph: ``rot`` steps captured once in a HIP graph and replayed -- how
+      serving engines run a decode step; the whole-job rate reported;
     * kernels: eager calls enqueued behind a GPU sleep so the host runs
       ahead, with the library's per-kernel HIP events (recorded by the
       dispatch itself) -> the average main / combine kernel durations;
     * eager: plain back-to-back calls from Python, wall clock (reference).
-    """
+    Returns (ms_per_step, graph_steps, main_ms, combine_ms, eager_ms)."""
+    import torch
+    import decode_attention_mla_amd as mla
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step(0)                       # warm the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            for i in range(rot):
+                step(i)
+    torch.cuda.synchronize()
+    replays = max(1, steps // rot)
+    for _ in range(max(1, warmup // rot)):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(replays):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    graph_wall_ms = (time.perf_counter() - t0) * 1e3
+    graph_steps = replays * rot
+    ms_per_step = max(graph_wall_ms, ev0.elapsed_time(ev1)) / graph_steps
+    del graph
+    torch.cuda._sleep(int(2.0e9 * 0.002 * steps))   # ~2 ms of GPU time per 100 calls at 2 GHz
+    mla.profile_start(steps)
+    for i in range(steps):
+        step(i)
+    main_ms, comb_ms, calls = mla.profile_stop()
+    torch.cuda.synchronize()
+    assert calls == steps, (calls, steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / steps
+    return ms_per_step, graph_steps, main_ms / calls, comb_ms / calls, eager_ms
+
+
+def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6, causal: bool = False):
+    """Times one dense workload (see time_steps), one step per rotating copy
+    of q and the KV pool so that no step finds its pages in cache."""
     import torch
     import decode_attention_mla_amd as mla
     from decode_attention_mla_amd import workloads as W
@@ -136,55 +184,7 @@ def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6
         mla.mla_decode_fwd(qs[i % rot], kvs[i % rot], bt, sl, inp.softmax_scale, sched, ns, out=out, lse=lse,
                            workspace=ws, causal=causal)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # -- graph replay (value)
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(s):
-        step(0)                       # warm the capture stream
-        torch.cuda.synchronize()
-        with torch.cuda.graph(graph, stream=s):
-            for i in range(rot):
-                step(i)
-    torch.cuda.synchronize()
-    replays = max(1, steps // rot)
-    for _ in range(max(1, warmup // rot)):
-        graph.replay()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(replays):
-        graph.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    graph_wall_ms = (time.perf_counter() - t0) * 1e3
-    graph_steps = replays * rot
-    ms_per_step = max(graph_wall_ms, ev0.elapsed_time(ev1)) / graph_steps
-    del graph
-
-    # -- per-kernel durations (eager, host ahead of the GPU)
-    torch.cuda._sleep(int(2.0e9 * 0.002 * steps))   # ~2 ms of GPU time per 100 calls at 2 GHz
-    mla.profile_start(steps)
-    for i in range(steps):
-        step(i)
-    main_ms, comb_ms, calls = mla.profile_stop()
-    torch.cuda.synchronize()
-    assert calls == steps, (calls, steps)
-    main_avg = main_ms / calls
-    comb_avg = comb_ms / calls
-
-    # -- plain eager wall clock (reference)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(i)
-    torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ms_per_step, graph_steps, main_avg, comb_avg, eager_ms = time_steps(step, rot, steps, warmup)
 
     res = dict(
         workload=inp.name + ("_causal" if causal else ""), batch=b, s_q=inp.s_q, h_q=inp.h_q,
@@ -197,6 +197,53 @@ def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6
     )
     log(f"[bench] config {idx}{' causal' if causal else ''}: "
         f"{json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()})}")
+    del kvs, qs
+    torch.cuda.empty_cache()
+    return inp, res
+
+
+def run_sparse_workload(steps: int, warmup: int, min_rot_bytes: float = 640e6):
+    """Times the sparse workload (batch 128, s_q 2, h_q 128, topk 2048; each
+    query token's 2048 keys drawn from its request's 4096..8192-token
+    context) the same way as the dense ones."""
+    import torch
+    import decode_attention_mla_amd as mla
+    from decode_attention_mla_amd import workloads as W
+
+    t = time.perf_counter()
+    inp = W.sparse_config_inputs()
+    log(f"[bench] sparse {inp.name}: inputs drawn in {time.perf_counter() - t:.1f}s")
+    flops, nbytes = W.sparse_algorithmic_work(inp.indices, inp.h_q, inp.topk_length)
+    dev = torch.device("cuda", 0)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    kv0, q0 = bf16(inp.kv_cache), bf16(inp.q)
+    rot = int(min(8, max(1, np.ceil(min_rot_bytes / (kv0.numel() * 2)))))
+    kvs = [kv0] + [kv0.clone() for _ in range(rot - 1)]
+    qs = [q0] + [q0.clone() for _ in range(rot - 1)]
+    idx = torch.from_numpy(inp.indices).to(dev)
+    sched, ns = mla.get_mla_metadata_sparse(inp.topk_length, inp.batch, inp.s_q, inp.h_q, inp.topk)
+    n = inp.batch * inp.s_q
+    out = torch.empty((inp.batch, inp.s_q, inp.h_q, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((inp.batch, inp.h_q, inp.s_q), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(256, mla.mla_workspace_bytes(sched.shape[0] + n - 1, inp.h_q, 1)), dtype=torch.uint8,
+                     device=dev)
+
+    def step(i):
+        mla.mla_decode_sparse_fwd(qs[i % rot], kvs[i % rot], idx, inp.softmax_scale, sched, ns, out=out, lse=lse,
+                                  workspace=ws)
+
+    ms_per_step, graph_steps, main_avg, comb_avg, eager_ms = time_steps(step, rot, steps, warmup)
+    res = dict(
+        workload=inp.name, batch=inp.batch, s_q=inp.s_q, h_q=inp.h_q, topk=inp.topk, parts=int(sched.shape[0]),
+        total_splits=int(ns[-1].item()), rotating_copies=rot, graph_steps=graph_steps, flops=flops, bytes=nbytes,
+        ms_per_step=ms_per_step, eager_ms_per_step=eager_ms, main_kernel_ms=main_avg, combine_kernel_ms=comb_avg,
+        tflops=flops / (ms_per_step * 1e-3) / 1e12, gbs=nbytes / (ms_per_step * 1e-3) / 1e9,
+        main_kernel_tflops=flops / (main_avg * 1e-3) / 1e12, main_kernel_gbs=nbytes / (main_avg * 1e-3) / 1e9,
+    )
+    log(f"[bench] sparse: {json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()})}")
     del kvs, qs
     torch.cuda.empty_cache()
     return inp, res
@@ -229,7 +276,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, help="headline workload (1..5)")
+    ap.add_argument("--config", type=int, default=2,
+                    help="headline workload (1..5); 6 times the sparse workload alone (for profiling)")
     ap.add_argument("--no-extra", action="store_true", help="skip the h_q=128 workloads")
     ap.add_argument("--extra-steps", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -244,6 +292,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     mla.lib()
+    if args.config == 6:
+        _, r = run_sparse_workload(args.steps, args.warmup)
+        print(json.dumps(dict(metric="sparse decode TFLOP/s", value=r["tflops"], unit="TFLOP/s", n_gpus=1,
+                              steps=args.steps, warmup=args.warmup, ms_per_step=r["ms_per_step"],
+                              higher_is_better=True, dtype="bf16", data="synthetic", detail=r)), flush=True)
+        return
 
     inp, head = run_workload(args.config, args.steps, args.warmup)
     bound_hbm = head["h_q"] * head["s_q"] <= 64
@@ -278,6 +332,13 @@ def main():
                 main_kernel_ms=r["main_kernel_ms"], combine_kernel_ms=r["combine_kernel_ms"],
                 parts=r["parts"], total_splits=r["total_splits"], plan_us=r["plan_us"],
                 plan_device_us=r["plan_device_us"])
+        _, r = run_sparse_workload(args.extra_steps, max(2, args.extra_steps // 5))
+        extra["sparse"] = dict(
+            workload=r["workload"], tflops=r["tflops"], frac_mfma_peak=r["tflops"] / MFMA_PEAK_TFLOPS,
+            gbs=r["gbs"], frac_hbm_peak=r["gbs"] / HBM_PEAK_GBS, ms_per_step=r["ms_per_step"],
+            eager_ms_per_step=r["eager_ms_per_step"], main_kernel_tflops=r["main_kernel_tflops"],
+            main_kernel_ms=r["main_kernel_ms"], combine_kernel_ms=r["combine_kernel_ms"],
+            parts=r["parts"], total_splits=r["total_splits"])
 
     line = dict(
         metric=METRIC, value=value, unit=unit, n_gpus=1, steps=args.steps, warmup=args.warmup,
