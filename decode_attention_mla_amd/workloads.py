@@ -265,6 +265,64 @@ def sparse_algorithmic_work(indices: np.ndarray, h_q: int, topk_length=None) -> 
     return flops, nbytes
 
 
+# ---------------------------------------------------------------------------
+# FP8 cache records ("[DeepSeek-3] FlashMLA", section 12): 656 bytes per token,
+#   bytes   0 .. 511  the 512 latent dims as float8 e4m3 (OCP e4m3fn);
+#   bytes 512 .. 527  four fp32 scales, scale i covering dims 128 i .. 128 i + 127;
+#   bytes 528 .. 655  the 64 RoPE dims, bf16, not quantized.
+FP8_RECORD = 656
+FP8_MAX = 448.0
+
+
+def _e4m3_table() -> np.ndarray:
+    """The 256 e4m3fn values (byte -> float64; 0x7f / 0xff are NaN)."""
+    v = np.empty(256, np.float64)
+    for b in range(256):
+        s = -1.0 if b & 0x80 else 1.0
+        e, m = (b >> 3) & 0xF, b & 7
+        if e == 0xF and m == 7:
+            v[b] = np.nan
+        elif e == 0:
+            v[b] = s * m / 8.0 * 2.0 ** -6
+        else:
+            v[b] = s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return v
+
+
+E4M3 = _e4m3_table()
+
+
+def quantize_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round float values to the nearest e4m3fn byte (ties to the even
+    mantissa), saturating at +-448.  Input generation only: the cache's
+    writer quantizes, the method reads the bytes."""
+    x = np.clip(np.asarray(x, np.float64), -FP8_MAX, FP8_MAX)
+    pos = E4M3[:0x7f]                 # 0x00 .. 0x7e: ascending non-negative values
+    mag = np.abs(x)
+    hi = np.clip(np.searchsorted(pos, mag, side="left"), 0, 0x7e)
+    lo = np.clip(hi - 1, 0, 0x7e)
+    dlo, dhi = mag - pos[lo], pos[hi] - mag
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    return (pick | np.where(np.signbit(x) & (pick != 0), 0x80, 0)).astype(np.uint8)
+
+
+def to_fp8_records(kv_bf16: np.ndarray) -> np.ndarray:
+    """FP8 records of a bf16 cache [nb, 64, 1, 576]: per token and 128-dim
+    tile, scale = max |x| / 448 (1 for an all-zero tile), bytes =
+    e4m3(x / scale); RoPE dims copied.  Returns uint8 [nb, 64, 1, 656]."""
+    nb = kv_bf16.shape[0]
+    x = bf16_bits_to_f32(kv_bf16.reshape(nb, PAGE, D_QK)).astype(np.float64)
+    lat = x[..., :D_V].reshape(nb, PAGE, 4, 128)
+    amax = np.abs(lat).max(axis=-1)
+    scale = np.where(amax > 0, amax / FP8_MAX, 1.0).astype(np.float32)
+    q8 = quantize_e4m3(lat / scale[..., None].astype(np.float64)).reshape(nb, PAGE, D_V)
+    rec = np.empty((nb, PAGE, FP8_RECORD), np.uint8)
+    rec[..., :D_V] = q8
+    rec[..., D_V:D_V + 16] = scale.view(np.uint8).reshape(nb, PAGE, 16)
+    rec[..., D_V + 16:] = kv_bf16.reshape(nb, PAGE, D_QK)[..., D_V:].view(np.uint8).reshape(nb, PAGE, 128)
+    return rec.reshape(nb, PAGE, 1, FP8_RECORD)
+
+
 def config_inputs(index: int) -> MlaInputs:
     """Workload ``index`` (1..5) with seed ``index``."""
     c = CONFIGS[index]

@@ -210,6 +210,54 @@ def mla_decode_sparse_rows(q, kv_cache, indices, softmax_scale, picks, topk_leng
 
 
 # ---------------------------------------------------------------------------
+# FP8 cache ("[DeepSeek-3] FlashMLA", section 12).  A token's record is 656
+# bytes: the 512 latent dims as float8 e4m3, four fp32 scales (scale i covers
+# dims 128 i .. 128 i + 127), the 64 RoPE dims as bf16.  The kernel
+# dequantizes the latent to bf16 and joins the bf16 RoPE; QK^T and PV then
+# run on bf16 inputs.  Reading (listed in the design notes): a latent value
+# is bf16_rne(fp32(e4m3 * scale)) -- the product rounded to fp32, then to
+# bf16 --, so the method on an FP8 cache is the bf16 method on that
+# dequantized cache.  e4m3 is the OCP format (bias 7, no infinities, S.1111.111
+# is NaN).
+
+RECORD_FP8 = 656
+
+
+def e4m3_value(byte: int) -> float:
+    """One OCP e4m3 byte as a float (bias 7; subnormals below exponent 1)."""
+    b = int(byte) & 0xFF
+    sign = -1.0 if b & 0x80 else 1.0
+    exp, man = (b >> 3) & 0xF, b & 0x7
+    if exp == 0xF and man == 0x7:
+        return math.nan
+    if exp == 0:
+        return sign * math.ldexp(man, -9)             # man/8 * 2^-6
+    return sign * math.ldexp(8 + man, exp - 10)       # (1 + man/8) * 2^(exp-7)
+
+
+def _f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
+    """fp32 values -> bf16 bit patterns, round to nearest even."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def dequantize_fp8_cache(kv_fp8: np.ndarray) -> np.ndarray:
+    """uint8 [nb, 64, 1, 656] records -> the bf16 cache (uint16 bit patterns
+    [nb, 64, 1, 576]) the method computes with."""
+    nb = kv_fp8.shape[0]
+    rec = np.asarray(kv_fp8, np.uint8).reshape(nb * PAGE, RECORD_FP8)
+    table = np.array([e4m3_value(b) for b in range(256)])
+    lat = table[rec[:, :D_V]]                                           # float64, exact
+    scale = rec[:, D_V:D_V + 16].copy().view(np.float32).astype(np.float64)   # [n, 4]
+    prod = np.float32(1) * (lat.reshape(-1, 4, 128) * scale[:, :, None]).astype(np.float32)  # fp32 rounding
+    out = np.empty((nb * PAGE, D_QK), np.uint16)
+    out[:, :D_V] = _f32_to_bf16_rne(prod.reshape(-1, D_V))
+    out[:, D_V:] = rec[:, D_V + 16:].copy().view(np.uint16)
+    return out.reshape(nb, PAGE, 1, D_QK)
+
+
+# ---------------------------------------------------------------------------
 # Online softmax and the merge of partial states (attention-kernel page,
 # online-softmax section; overview page, section 7).
 

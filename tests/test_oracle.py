@@ -474,3 +474,66 @@ def test_sparse_no_key_gives_zero_and_minus_inf():
     idx[0] = -1
     out, lse = oracle.mla_decode_sparse(inp.q, inp.kv_cache, idx, inp.softmax_scale, topk_length=[8, 0])
     assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+# ---------------------------------------------------------------------------
+# FP8 cache records: the e4m3 code points of the OCP format, the record
+# layout (latent | 4 fp32 scales | bf16 RoPE), per-tile scales, and the
+# fp32-then-bf16 rounding of the dequantized value, all against hand values.
+
+def test_e4m3_code_points():
+    ocp = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x39: 1.125,
+           0x40: 2.0, 0x7e: 448.0, 0xc0: -2.0, 0xb8: -1.0, 0xfe: -448.0}
+    for b, v in ocp.items():
+        assert oracle.e4m3_value(b) == v, hex(b)
+    assert math.isnan(oracle.e4m3_value(0x7f)) and math.isnan(oracle.e4m3_value(0xff))
+    assert math.copysign(1.0, oracle.e4m3_value(0x80)) == -1.0 and oracle.e4m3_value(0x80) == 0.0
+    vals = [oracle.e4m3_value(b) for b in range(0x7f)]
+    assert all(a < b for a, b in zip(vals, vals[1:]))                       # 0x00..0x7e ascending
+    assert all(oracle.e4m3_value(b | 0x80) == -oracle.e4m3_value(b) for b in range(1, 0x7f))
+
+
+def _record(lat_bytes, scales, rope_bits):
+    rec = np.zeros((1, PAGE, 1, 656), np.uint8)
+    rec[0, :, 0, :512] = np.asarray(lat_bytes, np.uint8)
+    rec[0, :, 0, 512:528] = np.asarray(scales, np.float32).view(np.uint8)
+    rec[0, :, 0, 528:] = np.asarray(rope_bits, np.uint16).view(np.uint8)
+    return rec
+
+
+def test_fp8_record_layout_and_tile_scales():
+    rope = (np.arange(64, dtype=np.uint16) + 0x3F00)        # distinct bf16 patterns
+    k = oracle.dequantize_fp8_cache(_record(np.full(512, 0x38), [0.5, 2.0, 3.0, 1e-3], rope))
+    assert k.shape == (1, PAGE, 1, D_QK)
+    row = k[0, 5, 0]
+    assert np.all(row[0:128] == 0x3F00)       # 1.0 * 0.5
+    assert np.all(row[128:256] == 0x4000)     # 1.0 * 2
+    assert np.all(row[256:384] == 0x4040)     # 1.0 * 3
+    assert np.all(row[384:512] == 0x3A83)     # fp32(1e-3) = 0x3A83126F -> bf16 0x3A83
+    assert np.array_equal(row[512:], rope)    # RoPE copied, not scaled
+
+
+def test_fp8_dequantize_rounds_to_fp32_then_bf16_nearest_even():
+    # 1.125 * 1.0078125 = 1.1337890625 = 1 + 17.125/128 -> bf16 1 + 17/128 = 1.1328125 (0x3F91)
+    # 1.0 * (1 + 2^-8) is a tie between 1 and 1 + 2^-7: even mantissa, 1.0 (0x3F80)
+    # 1.0 * (1 + 3 * 2^-8) is a tie between 1 + 2^-7 and 1 + 2^-6: even, 1 + 2^-6 (0x3F82)
+    # 2^-9 * 2^-126 = 2^-135: an fp32 subnormal, below half of the smallest bf16 one (2^-133), so 0
+    lat = np.array([0x39] * 128 + [0x38] * 128 + [0x38] * 128 + [0x01] * 128)
+    k = oracle.dequantize_fp8_cache(_record(lat, [1.0078125, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 2.0 ** -126],
+                                            np.zeros(64)))
+    row = k[0, 0, 0]
+    assert np.all(row[0:128] == 0x3F91) and np.all(row[128:256] == 0x3F80)
+    assert np.all(row[256:384] == 0x3F82) and np.all(row[384:512] == 0x0000)
+
+
+def test_fp8_records_round_trip_within_e4m3_precision():
+    inp = W.make_inputs(1, 1, 16, [128], pool=3, max_blocks=2, seed=8)
+    kv = inp.kv_cache[inp.block_table[0, :2]]
+    back = W.bf16_bits_to_f32(oracle.dequantize_fp8_cache(W.to_fp8_records(kv))).astype(np.float64)
+    x = W.bf16_bits_to_f32(kv).astype(np.float64)
+    # e4m3 keeps 4 significant bits: |error| <= 2^-4 |x| + (subnormal step) * scale, plus bf16 rounding.
+    amax = np.abs(x[..., :512]).reshape(2, PAGE, 1, 4, 128).max(-1, keepdims=True)
+    step = np.broadcast_to(amax / 448 * 2.0 ** -9, (2, PAGE, 1, 4, 128)).reshape(2, PAGE, 1, 512)
+    err = np.abs(back - x)[..., :512]
+    assert np.all(err <= 2.0 ** -4 * np.abs(x[..., :512]) + step + 2.0 ** -8 * np.abs(x[..., :512]))
+    assert np.array_equal(back[..., 512:], x[..., 512:])
