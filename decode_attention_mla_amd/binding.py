@@ -18,6 +18,7 @@ SCHED_INTS = 8
 PAGE = 64
 D_QK = 576
 D_V = 512
+FP8_RECORD = 656   # bytes per token of an FP8 cache (512 e4m3 + 4 fp32 scales + 64 bf16)
 
 # Every symbol include/mla_decode.h declares.
 EXPORTED = ("mla_plan", "mla_get_metadata", "mla_get_metadata_device", "mla_max_parts", "mla_workspace_bytes",
@@ -57,7 +58,7 @@ def lib() -> ctypes.CDLL:
                                           ctypes.c_int, vp, ip, vp]
     L.mla_get_metadata_device.restype = ctypes.c_int
     L.mla_decode_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                 ctypes.c_int, ctypes.c_float, ctypes.c_int, vp, ctypes.c_int, vp, vp,
+                                 ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, vp, vp,
                                  ctypes.c_size_t, vp, vp, vp]
     L.mla_decode_fwd.restype = ctypes.c_int
     L.mla_max_parts_sparse.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
@@ -66,8 +67,8 @@ def lib() -> ctypes.CDLL:
                                           i32p, ctypes.c_int, i32p, ip, ip]
     L.mla_get_metadata_sparse.restype = ctypes.c_int
     L.mla_decode_sparse_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                        ctypes.c_int, ctypes.c_float, vp, ctypes.c_int, vp, vp, ctypes.c_size_t,
-                                        vp, vp, vp]
+                                        ctypes.c_int, ctypes.c_float, ctypes.c_int, vp, ctypes.c_int, vp, vp,
+                                        ctypes.c_size_t, vp, vp, vp]
     L.mla_decode_sparse_fwd.restype = ctypes.c_int
     L.mla_profile_start.argtypes = [ctypes.c_int]
     L.mla_profile_start.restype = ctypes.c_int
@@ -179,11 +180,24 @@ def _need(cond: bool, msg: str) -> None:
         raise ValueError(msg)
 
 
+def _kv_check(kv_cache, fp8: bool):
+    import torch
+    if fp8:
+        _need(kv_cache.dim() == 4 and tuple(kv_cache.shape[1:]) == (PAGE, 1, FP8_RECORD) and
+              kv_cache.dtype == torch.uint8, f"an FP8 kv_cache must be uint8 [num_blocks, 64, 1, 656], got "
+              f"{kv_cache.dtype} {tuple(kv_cache.shape)}")
+    else:
+        _need(kv_cache.dim() == 4 and tuple(kv_cache.shape[1:]) == (PAGE, 1, D_QK) and
+              kv_cache.dtype == torch.bfloat16,
+              f"kv_cache must be bf16 [num_blocks, 64, 1, 576], got {kv_cache.dtype} {tuple(kv_cache.shape)}")
+
+
 def mla_decode_fwd(q, kv_cache, block_table, cache_seqlens, softmax_scale: float, sched, num_splits,
-                   out=None, lse=None, workspace=None, causal: bool = False):
+                   out=None, lse=None, workspace=None, causal: bool = False, fp8: bool = False):
     """Dense MLA decode.  Returns (out bf16 [b, s_q, h_q, 512], lse fp32 [b, h_q, s_q]).
 
-    q bf16 [b, s_q, h_q, 576]; kv_cache bf16 [num_blocks, 64, 1, 576];
+    q bf16 [b, s_q, h_q, 576]; kv_cache bf16 [num_blocks, 64, 1, 576], or with
+    fp8=True the FP8 records uint8 [num_blocks, 64, 1, 656];
     block_table int32 [b, max_blocks]; cache_seqlens int32 [b];
     sched / num_splits from get_mla_metadata for the same cache_seqlens.
     causal: query token s of s_q sees keys 0 .. L - s_q + s (multi-token
@@ -193,13 +207,12 @@ def mla_decode_fwd(q, kv_cache, block_table, cache_seqlens, softmax_scale: float
     import torch
     _need(q.dim() == 4 and q.shape[3] == D_QK, f"q must be [b, s_q, h_q, 576], got {tuple(q.shape)}")
     b, s_q, h_q = (int(x) for x in q.shape[:3])
-    _need(kv_cache.dim() == 4 and tuple(kv_cache.shape[1:]) == (PAGE, 1, D_QK),
-          f"kv_cache must be [num_blocks, 64, 1, 576], got {tuple(kv_cache.shape)}")
+    _kv_check(kv_cache, fp8)
     _need(block_table.dim() == 2 and block_table.shape[0] == b, "block_table must be [b, max_blocks]")
     _need(cache_seqlens.dim() == 1 and cache_seqlens.shape[0] == b, "cache_seqlens must be [b]")
     _need(sched.dim() == 2 and sched.shape[1] == SCHED_INTS and sched.shape[0] > 0, "sched must be [P, 8]")
     _need(num_splits.dim() == 1 and num_splits.shape[0] == b + 1, "num_splits must be [b + 1]")
-    for name, t, dt in (("q", q, torch.bfloat16), ("kv_cache", kv_cache, torch.bfloat16),
+    for name, t, dt in (("q", q, torch.bfloat16), ("kv_cache", kv_cache, kv_cache.dtype),
                         ("block_table", block_table, torch.int32), ("cache_seqlens", cache_seqlens, torch.int32),
                         ("sched", sched, torch.int32), ("num_splits", num_splits, torch.int32)):
         _need(t.dtype == dt, f"{name} must be {dt}, got {t.dtype}")
@@ -221,7 +234,7 @@ def mla_decode_fwd(q, kv_cache, block_table, cache_seqlens, softmax_scale: float
     stream = torch.cuda.current_stream(q.device).cuda_stream
     rc = lib().mla_decode_fwd(q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(), cache_seqlens.data_ptr(),
                               b, s_q, h_q, int(kv_cache.shape[0]), int(block_table.shape[1]),
-                              float(softmax_scale), 1 if causal else 0, sched.data_ptr(), num_parts,
+                              float(softmax_scale), 1 if causal else 0, 1 if fp8 else 0, sched.data_ptr(), num_parts,
                               num_splits.data_ptr(),
                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                               out.data_ptr(), lse.data_ptr(), stream)
@@ -257,7 +270,7 @@ def get_mla_metadata_sparse(topk_length, batch: int, s_q: int, h_q: int, topk: i
 
 
 def mla_decode_sparse_fwd(q, kv_cache, indices, softmax_scale: float, sched, num_splits, topk_length=None,
-                          out=None, lse=None, workspace=None):
+                          out=None, lse=None, workspace=None, fp8: bool = False):
     """Sparse MLA decode.  Returns (out bf16 [b, s_q, h_q, 512], lse fp32 [b, h_q, s_q]).
 
     q bf16 [b, s_q, h_q, 576]; kv_cache bf16 [num_blocks, 64, 1, 576];
@@ -270,15 +283,14 @@ def mla_decode_sparse_fwd(q, kv_cache, indices, softmax_scale: float, sched, num
     import torch
     _need(q.dim() == 4 and q.shape[3] == D_QK, f"q must be [b, s_q, h_q, 576], got {tuple(q.shape)}")
     b, s_q, h_q = (int(x) for x in q.shape[:3])
-    _need(kv_cache.dim() == 4 and tuple(kv_cache.shape[1:]) == (PAGE, 1, D_QK),
-          f"kv_cache must be [num_blocks, 64, 1, 576], got {tuple(kv_cache.shape)}")
+    _kv_check(kv_cache, fp8)
     _need(indices.dim() == 3 and tuple(indices.shape[:2]) == (b, s_q) and indices.shape[2] > 0,
           "indices must be [b, s_q, topk]")
     topk = int(indices.shape[2])
     n = b * s_q
     _need(sched.dim() == 2 and sched.shape[1] == SCHED_INTS and sched.shape[0] > 0, "sched must be [P, 8]")
     _need(num_splits.dim() == 1 and num_splits.shape[0] == n + 1, "num_splits must be [b * s_q + 1]")
-    checks = [("q", q, torch.bfloat16), ("kv_cache", kv_cache, torch.bfloat16), ("indices", indices, torch.int32),
+    checks = [("q", q, torch.bfloat16), ("kv_cache", kv_cache, kv_cache.dtype), ("indices", indices, torch.int32),
               ("sched", sched, torch.int32), ("num_splits", num_splits, torch.int32)]
     if topk_length is not None:
         _need(topk_length.dim() == 1 and topk_length.shape[0] == b, "topk_length must be [b]")
@@ -304,7 +316,7 @@ def mla_decode_sparse_fwd(q, kv_cache, indices, softmax_scale: float, sched, num
     rc = lib().mla_decode_sparse_fwd(q.data_ptr(), kv_cache.data_ptr(), indices.data_ptr(),
                                      None if topk_length is None else topk_length.data_ptr(),
                                      b, s_q, h_q, int(kv_cache.shape[0]), topk, float(softmax_scale),
-                                     sched.data_ptr(), num_parts, num_splits.data_ptr(), workspace.data_ptr(),
+                                     1 if fp8 else 0, sched.data_ptr(), num_parts, num_splits.data_ptr(), workspace.data_ptr(),
                                      workspace.numel() * workspace.element_size(), out.data_ptr(), lse.data_ptr(),
                                      stream)
     _check(rc, "mla_decode_sparse_fwd")

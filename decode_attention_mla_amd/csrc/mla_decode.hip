@@ -226,6 +226,7 @@ struct GatherPage {
   // t = 8 par + lane / 8): cache row rel[par] + t, so that its byte address
   // is kv + rel[par] * 1152 + the lane's dense slice offset.
   int rel[2];
+  int row;   // the entry of page token `lane`, pool row 0 if it is not a key (FP8 record gathers)
 };
 
 __device__ __forceinline__ GatherPage gather_page(const Params& p, int entry, int j, int L, int tok0, int lane) {
@@ -234,6 +235,7 @@ __device__ __forceinline__ GatherPage gather_page(const Params& p, int entry, in
   const int row = key ? entry : 0;
   GatherPage g;
   g.mask = __ballot(key);
+  g.row = row;
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
     const int t = 8 * par + (lane >> 3);
@@ -271,6 +273,90 @@ __device__ __forceinline__ void zero_stage_rows(LDS_PTR(unsigned char) buf, unsi
   for (int u = lane; u < kWaveTokens * 64; u += 64) {
     const int t = u >> 6, b = (u >> 3) & 7, c = u & 7;
     if (!((keep >> t) & 1u)) *(LDS_PTR(u32x4))(buf + b * kStageBlock + t * 128 + c * 16) = u32x4{0, 0, 0, 0};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// FP8 cache ("[DeepSeek-3] FlashMLA", section 12): a token's record is 656
+// bytes -- the 512 latent dims as e4m3 (OCP), four fp32 scales (scale i for
+// dims 128 i .. 128 i + 127), the 64 RoPE dims as bf16.  A wave copies its
+// 16 records as they are (10,496 contiguous bytes of LDS) and then
+// dequantizes them into its bf16 slice of the page stage: latent value =
+// bf16_rne(fp32(e4m3 * scale)), RoPE copied; the rest of the kernel runs on
+// bf16 as for a bf16 cache.
+constexpr int kFp8Row = 656;
+constexpr int kFp8Slice = kWaveTokens * kFp8Row;      // 10,496 bytes: one wave's records
+constexpr int kFp8Page = kPage * kFp8Row;             // 41,984 bytes
+constexpr int kFp8Copies = (kFp8Slice + 1023) / 1024;   // 11 (the last: 256 bytes, lanes 0..15)
+static_assert(kFp8Slice == 10 * 1024 + 256, "FP8 slice copy split");
+
+// Copy i of this wave's records of a block-table page (contiguous).
+template <bool kStream>
+__device__ __forceinline__ void issue_fp8_copy(const unsigned char* rows, unsigned slice_lds, int i, int lane) {
+  unsigned voff = (unsigned)(i * 1024 + lane * 16);
+  asm volatile("" : "+v"(voff));
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(slice_lds + (unsigned)i * 1024u);
+  if (i < kFp8Copies - 1 || lane < 16) {
+    if constexpr (kStream)
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(rows), "s"(m0)
+                   : "memory");
+    else
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(rows), "s"(m0)
+                   : "memory");
+  }
+}
+
+// Copy i of this wave's records of a sparse page: chunk u = 64 i + lane of
+// the slice is chunk u % 41 of local token u / 41, whose cache row is the
+// (clamped) entry held by lane tok0 + u / 41.
+template <bool kStream>
+__device__ __forceinline__ void issue_fp8_gather(const Params& p, int entry_row, int tok0, unsigned slice_lds, int i,
+                                                 int lane) {
+  int u = i * 64 + lane;
+  asm volatile("" : "+v"(u));   // per copy (hoisted, the 11 copies' offsets would not fit in registers)
+  const int t = min((u * 1599) >> 16, kWaveTokens - 1);   // u / 41 for u < 656
+  const int row = __builtin_amdgcn_ds_bpermute((tok0 + t) << 2, entry_row);
+  const unsigned long long a = (unsigned long long)(size_t)p.kv + (unsigned long long)(unsigned)row * kFp8Row +
+                               (unsigned)((u - 41 * t) * 16);
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(slice_lds + (unsigned)i * 1024u);
+  if (i < kFp8Copies - 1 || lane < 16) {
+    if constexpr (kStream)
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(a), "s"(m0) : "memory");
+    else
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(a), "s"(m0) : "memory");
+  }
+}
+
+// Dequantize this wave's 16 records (fp8 slice) into its bf16 stage slice
+// (the 16-token layout above).  Lane (t = lane / 4, q = lane % 4) converts
+// dims 128 q .. 128 q + 127 of token t with scale q, and copies RoPE bytes
+// 32 q .. 32 q + 31 of the token.
+__device__ __forceinline__ void dequant_fp8_slice(LDS_PTR(unsigned char) fp8, LDS_PTR(unsigned char) bf, int lane) {
+  const int t = lane >> 2, q = lane & 3;
+  LDS_PTR(unsigned char) rec = fp8 + t * kFp8Row;
+  const float sc = *(LDS_PTR(float))(rec + kDv + 4 * q);
+  const int swz = stage_swizzle(t);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const u32x4 v = *(LDS_PTR(u32x4))(rec + 128 * q + 16 * k);
+    u32x4 w[2];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[e], false);   // bytes 0, 1
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[e], true);    // bytes 2, 3
+      w[e >> 1][2 * (e & 1)] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)(lo[0] * sc), (__bf16)(lo[1] * sc)});
+      w[e >> 1][2 * (e & 1) + 1] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)(hi[0] * sc), (__bf16)(hi[1] * sc)});
+    }
+    // dims d0 = 128 q + 16 k: block d0 / 64, in-block chunks c0, c0 + 1
+    const int b = 2 * q + (k >> 2), c0 = 2 * (k & 3);
+    LDS_PTR(unsigned char) row = bf + b * kStageBlock + t * 128;
+    *(LDS_PTR(u32x4))(row + ((c0 ^ swz) << 4)) = w[0];
+    *(LDS_PTR(u32x4))(row + (((c0 + 1) ^ swz) << 4)) = w[1];
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {   // RoPE dims 512 + 8 (2 q + k) .. + 7: block 8, chunk 2 q + k
+    const u32x4 v = *(LDS_PTR(u32x4))(rec + kDv + 16 + 32 * q + 16 * k);
+    *(LDS_PTR(u32x4))(bf + 8 * kStageBlock + t * 128 + (((2 * q + k) ^ swz) << 4)) = v;
   }
 }
 
@@ -471,10 +557,12 @@ __device__ __forceinline__ float row_sum4(float v) {
 }
 
 // kSparse: the key lists of sparse decode instead of block-table pages
-// (gathered copies, per-token key masks).
-template <bool kSparse>
+// (gathered copies, per-token key masks).  kFp8: an FP8 cache; one bf16
+// page stage (the dequantized page being computed) and one stage of FP8
+// records (the next page, in flight) replace the two bf16 stages.
+template <bool kSparse, bool kFp8>
 __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kPageBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kFp8 ? kPageBytes + kFp8Page : 2 * kPageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char pbuf[kSmallPBytes];
   __shared__ float red[4][kSmallRows];   // per-wave row maxima, then row sums
   __shared__ int vote[4];                // per-wave restart votes
@@ -495,9 +583,12 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
   LDS_PTR(unsigned char) pb = (LDS_PTR(unsigned char))pbuf;
   const unsigned wslice = (unsigned)(size_t)lds + wave * kStageBytes;   // this wave's slice of stage 0
   const unsigned dma_off[2] = {stage_dma_offset(lane, 0), stage_dma_offset(lane, 1)};
+  // FP8: this wave's records in the FP8 stage (after the bf16 stage).
+  LDS_PTR(unsigned char) fp8s = lds + kPageBytes + wave * kFp8Slice;
+  const unsigned fslice = (unsigned)(size_t)lds + kPageBytes + wave * kFp8Slice;
   // The request's query rows are staged like a page slice (row r in token
-  // slot r) in slice 0 of stage 1; slots >= R copy row 0 instead
-  // (in bounds; their fragments are zeroed).
+  // slot r) in slice 0 of stage 1 (of the bf16 stage for an FP8 cache);
+  // slots >= R copy row 0 instead (in bounds; their fragments are zeroed).
   unsigned q_dma_off[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
@@ -550,6 +641,17 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
     auto page_rows = [&](int blk) {
       return uniform_ptr(p.kv + (size_t)blk * kPageBytes + (size_t)tok0 * kRowBytes);
     };
+    // FP8: copy this wave's records of a page (block id, or gathered rows).
+    auto issue_fp8_page = [&](int blk, int entry_row) {
+      const unsigned char* rows = uniform_ptr(p.kv + (size_t)blk * kFp8Page + (size_t)tok0 * kFp8Row);
+#pragma unroll
+      for (int i = 0; i < kFp8Copies; ++i) {
+        if constexpr (kSparse)
+          issue_fp8_gather<true>(p, entry_row, tok0, fslice, i, lane);
+        else
+          issue_fp8_copy<true>(rows, fslice, i, lane);
+      }
+    };
 
     f32x4 o[8];
     float m_ref = -INFINITY, l_run = 0.f;
@@ -573,27 +675,29 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
     }
     {
       const unsigned char* qrows = uniform_ptr(p.q + (size_t)req * p.R * kRowBytes);
-      const unsigned qslice = (unsigned)(size_t)lds + kPageBytes;
+      const unsigned qslice = (unsigned)(size_t)lds + (kFp8 ? 0 : kPageBytes);
       for (int i = wave; i < kStageSlices; i += 4) issue_stage_slice<false>(qrows, qslice, q_dma_off, i);
     }
     for (int attempt = 0;; ++attempt) {
       // Sparse: key masks of the current page, of page lo + 1, and of the
       // page whose copy was issued last; the entries of the next page to copy.
       unsigned long long mk_cur = g0.mask, mk_lo1 = g1.mask, mk_pending = 0;
-      int ent_next = ent[2];
-      if constexpr (kSparse) {
+      int ent_next = kFp8 ? ent[1] : ent[2];
+      if constexpr (kFp8) {
+        if (lo < hi) issue_fp8_page(m.blk[0], g0.row);
+      } else if constexpr (kSparse) {
         if (lo < hi) issue_gather<true>(p, g0, dma_off, wslice);
       } else {
         if (lo < hi) issue_stage<true>(page_rows(m.blk[0]), wslice, dma_off);
       }
       if (attempt == 0) {
-        if (lo < hi)
+        if (lo < hi && !kFp8)
           wait_vmcnt<kStageSlices>();   // this wave's pieces of Q (the first page may still be in flight)
         else
           wait_vmcnt<0>();
         lds_barrier();                  // all of Q has landed
         const unsigned keep = row_ok ? ~0u : 0u;
-        LDS_PTR(unsigned char) qs = lds + kPageBytes;
+        LDS_PTR(unsigned char) qs = lds + (kFp8 ? 0 : kPageBytes);
 #pragma unroll
         for (int ks = 0; ks < kQkSteps; ++ks) {
           u32x4 v = *(LDS_PTR(u32x4))(qs + (ks >> 1) * kStageBlock + qk_off[ks & 1]);
@@ -602,13 +706,13 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
         }
         lds_barrier();                  // every wave has read Q: stage 1 is free again
       }
-      if (lo + 1 < hi) {
+      if (lo + 1 < hi && !kFp8) {
         if constexpr (kSparse)
           issue_gather<true>(p, g1, dma_off, wslice + kPageBytes);
         else
           issue_stage<true>(page_rows(m.blk[1]), wslice + kPageBytes, dma_off);
       }
-      int next_blk = m.blk[2];   // block ids are read one page ahead of their copy
+      int next_blk = kFp8 ? m.blk[1] : m.blk[2];   // block ids are read one page ahead of their copy
 
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) o[ct] = f32x4{0, 0, 0, 0};
@@ -617,14 +721,33 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
       bool restart = false;
 
       for (int j = lo; j < hi; ++j) {
-        const int stage = (j - lo) & 1;
+        const int stage = kFp8 ? 0 : (j - lo) & 1;
         LDS_PTR(unsigned char) buf = lds + stage * kPageBytes;
         // This wave's slice of page j (the next page's copy, if any, is issued
         // below, after the barrier).
-        if (j == lo && lo + 1 < hi)
+        if (j == lo && lo + 1 < hi && !kFp8)
           wait_vmcnt<kStageSlices>();
         else
           wait_vmcnt<0>();
+        if constexpr (kFp8) {
+          // Its records are in; once every wave is done with page j - 1 the
+          // bf16 stage takes page j, dequantized, and the records of page
+          // j + 1 go to the FP8 stage this wave has just read.
+          if (j > lo) lds_barrier();
+          dequant_fp8_slice(fp8s, buf + wave * kStageBytes, lane);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // its reads of the FP8 stage are done
+          if (j + 1 < hi) {
+            if constexpr (kSparse) {
+              const GatherPage gn = gather_page(p, ent_next, j + 1, L, tok0, lane);
+              issue_fp8_page(0, gn.row);
+              mk_pending = gn.mask;
+              ent_next = load_page_entries(p, req, j + 2, lane);
+            } else {
+              issue_fp8_page(next_blk, 0);
+              next_blk = ld_uniform(bt + min(j + 2, p.max_blocks - 1));
+            }
+          }
+        }
         if constexpr (kSparse) {
           const unsigned keep = (unsigned)(mk_cur >> tok0) & 0xFFFFu;
           if (keep != 0xFFFFu) zero_stage_rows(buf + wave * kStageBytes, keep, lane);
@@ -636,7 +759,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
         // Page j + 1 goes to the stage page j - 1 held (pages lo, lo + 1 were
         // issued ahead of the loop).  (A third page in flight from the start,
         // held in registers, was measured slower: every page then lands late.)
-        if (j > lo && j + 1 < hi) {
+        if (j > lo && j + 1 < hi && !kFp8) {
           if constexpr (kSparse) {
             const GatherPage gn = gather_page(p, ent_next, j + 1, L, tok0, lane);
             issue_gather<true>(p, gn, dma_off, wslice + ((j + 1 - lo) & 1) * kPageBytes);
@@ -724,7 +847,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-        if constexpr (kSparse) mk_cur = j == lo ? mk_lo1 : mk_pending;
+        if constexpr (kSparse) mk_cur = j == lo && !kFp8 ? mk_lo1 : mk_pending;
       }
       wait_vmcnt<0>();
       if (!restart) break;
@@ -1045,11 +1168,14 @@ __device__ __forceinline__ void wide_acc_settle() {
 }
 
 // kSparse: the key lists of sparse decode instead of block-table pages
-// (gathered copies, per-token key masks).
-template <bool kStream, bool kSparse>
+// (gathered copies, per-token key masks).  kFp8: an FP8 cache; one bf16
+// page stage (the dequantized page being computed) and one stage of FP8
+// records (the next page, in flight) replace the two bf16 stages.
+template <bool kStream, bool kSparse, bool kFp8>
 __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
-  // Two page stages (4 slices of 18 KiB each) and the P^T exchange buffer: 160 KiB.
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kPageBytes];
+  // Two page stages (4 slices of 18 KiB each) and the P^T exchange buffer: 160 KiB
+  // (FP8: a bf16 stage and an FP8 stage, 129 KiB).
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kFp8 ? kPageBytes + kFp8Page : 2 * kPageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char pbuf[kPFragBytes];
 
   const int lane = threadIdx.x & 63;
@@ -1070,6 +1196,9 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
   LDS_PTR(unsigned char) pb = (LDS_PTR(unsigned char))pbuf;
   const unsigned lds0 = (unsigned)(size_t)lds;
   const unsigned dma_off[2] = {stage_dma_offset(lane, 0), stage_dma_offset(lane, 1)};
+  // FP8: this wave's records in the FP8 stage (after the bf16 stage).
+  LDS_PTR(unsigned char) fp8s = lds + kPageBytes + wave * kFp8Slice;
+  const unsigned fslice = lds0 + kPageBytes + wave * kFp8Slice;
 
   // QK A fragment (32x32x16) of token tile tt, k-step ks: token m = 32 tt + n
   // = slice 2 tt + n / 16, local row n % 16; dims 16 ks + 8 h .. + 7 =
@@ -1106,6 +1235,17 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
     auto page_rows = [&](int blk) {
       return uniform_ptr(p.kv + (size_t)blk * kPageBytes + (size_t)tok0 * kRowBytes);
     };
+    // FP8: copy this wave's records of a page (block id, or gathered rows).
+    auto issue_fp8_page = [&](int blk, int entry_row) {
+      const unsigned char* rows = uniform_ptr(p.kv + (size_t)blk * kFp8Page + (size_t)tok0 * kFp8Row);
+#pragma unroll
+      for (int i = 0; i < kFp8Copies; ++i) {
+        if constexpr (kSparse)
+          issue_fp8_gather<kStream>(p, entry_row, tok0, fslice, i, lane);
+        else
+          issue_fp8_copy<kStream>(rows, fslice, i, lane);
+      }
+    };
     f32x16 o[kWideTiles][4];   // O^T tiles: row tile x this wave's 4 column tiles
     float m_ref = -INFINITY, l_run = 0.f;
     for (int attempt = 0;; ++attempt) {
@@ -1119,7 +1259,9 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
         g0 = gather_page(p, ent0, lo, L, tok0, lane);
       }
       if (lo < hi) {
-        if constexpr (kSparse)
+        if constexpr (kFp8)
+          issue_fp8_page(m.blk[0], g0.row);
+        else if constexpr (kSparse)
           issue_gather<kStream>(p, g0, dma_off, lds0 + wave * kStageBytes);
         else
           issue_stage<kStream>(page_rows(m.blk[0]), lds0 + wave * kStageBytes, dma_off);
@@ -1151,13 +1293,19 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
       unsigned long long mk_cur = g0.mask;   // sparse: key mask of page j
 
       for (int j = lo; j < hi; ++j) {
-        const int stage = (j - lo) & 1;
+        const int stage = kFp8 ? 0 : (j - lo) & 1;
         LDS_PTR(unsigned char) buf = lds + stage * kPageBytes;
         // Page j: this wave's slice has landed; zero its rows past the end of
         // the sequence, then the barrier makes all four slices visible (and
         // every wave is past the previous page's PV: P buffer and the other
         // stage are free).
         wait_vmcnt<0>();
+        if constexpr (kFp8) {
+          // Its records are in; once every wave is done with page j - 1 the
+          // bf16 stage takes page j, dequantized.
+          if (j > lo) lds_barrier();
+          dequant_fp8_slice(fp8s, buf + wave * kStageBytes, lane);
+        }
         if constexpr (kSparse) {
           const unsigned keep = (unsigned)(mk_cur >> tok0) & 0xFFFFu;
           if (keep != 0xFFFFu) zero_stage_rows(buf + wave * kStageBytes, keep, lane);
@@ -1180,9 +1328,16 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
           // budget of the QK^T loop below).
           const GatherPage gn = gather_page(p, ent_next, j + 1, L, tok0, lane);
           mk_next = gn.mask;
-          if (has_next) issue_gather<kStream>(p, gn, dma_off, nlds);
+          if (has_next) {
+            if constexpr (kFp8)
+              issue_fp8_page(0, gn.row);   // into the FP8 stage this wave dequantized from
+            else
+              issue_gather<kStream>(p, gn, dma_off, nlds);
+          }
           ent_next = load_page_entries(p, req, j + 2, lane);   // covered by the next page's wait
         } else {
+          if constexpr (kFp8)
+            if (has_next) issue_fp8_page(next_blk, 0);   // into the FP8 stage this wave dequantized from
           next_blk = ld_uniform(bt + (j + 2 < hi ? j + 2 : j));
         }
 
@@ -1298,7 +1453,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
           for (int ks = 0; ks < kQkSteps16; ++ks) {
             qk_mfma(sacc[tt], kf[ks % kWideQkLead], qf[ks], ks == 0);
             if (ks + kWideQkLead < kQkSteps16) kf[ks % kWideQkLead] = kread(ks + kWideQkLead);
-            if constexpr (!kSparse)
+            if constexpr (!kSparse && !kFp8)
               if (ks % 4 == 0 && has_next) issue_stage_slice<kStream>(nrows, nlds, dma_off, 9 * tt + ks / 4);
             // Tile 0's softmax: one piece every other step from step 1.
             if (tt == 1 && ks == 1) wide_acc_settle();
@@ -1865,25 +2020,31 @@ static hipEvent_t* profile_slot() {
 constexpr int kCombineMaxGrid = 2048;   // about one round of resident workgroups
 
 // Enqueues the split-KV kernel picked by the row count (and, for sparse
-// decode, its gather variant), then the combine kernel.
-static int launch_decode(Params& prm, const Geometry& g, bool sparse, hipStream_t st, const char* who) {
+// decode or an FP8 cache, its variant), then the combine kernel.  Sparse
+// decode and FP8 caches take the 128-row kernel above 16 rows.
+template <bool kSparse, bool kFp8>
+static const void* pick_main_kernel(const Geometry& g) {
+  if (g.R <= kSmallRows) return (const void*)mla_splitkv_small_kernel<kSparse, kFp8>;
+  // Row groups of one part share pages through L2 (cached copies); a single
+  // group streams every page once (nontemporal copies).
+  return g.row_groups == 1 ? (const void*)mla_splitkv_wide_kernel<true, kSparse, kFp8>
+                           : (const void*)mla_splitkv_wide_kernel<false, kSparse, kFp8>;
+}
+
+static int launch_decode(Params& prm, Geometry g, bool sparse, bool fp8, hipStream_t st, const char* who) {
   hipEvent_t* ev = profile_slot();
   void* args[] = {&prm};
   const void* main_fn;
+  if (g.R > kSmallRows && g.R < kWideRows && (sparse || fp8)) g.row_groups = 1;   // 128-row kernel
+  prm.row_groups = g.row_groups;
   // The XCD-aware block mapping (map_block) needs 8 * row_groups * ceil(parts / 8) workgroups.
   const int grid = 8 * g.row_groups * ((prm.num_parts + 7) / 8);
-  if (g.R <= kSmallRows) {
-    main_fn = sparse ? (const void*)mla_splitkv_small_kernel<true> : (const void*)mla_splitkv_small_kernel<false>;
-  } else if (g.R >= kWideRows || sparse) {
-    // Row groups of one part share pages through L2 (cached copies); a single
-    // group streams every page once (nontemporal copies).
-    if (g.row_groups == 1)
-      main_fn = sparse ? (const void*)mla_splitkv_wide_kernel<true, true> : (const void*)mla_splitkv_wide_kernel<true, false>;
-    else
-      main_fn = sparse ? (const void*)mla_splitkv_wide_kernel<false, true> : (const void*)mla_splitkv_wide_kernel<false, false>;
-  } else {
+  if (g.R > kSmallRows && g.R < kWideRows && !sparse && !fp8)
     main_fn = (const void*)mla_splitkv_kernel;
-  }
+  else if (sparse)
+    main_fn = fp8 ? pick_main_kernel<true, true>(g) : pick_main_kernel<true, false>(g);
+  else
+    main_fn = fp8 ? pick_main_kernel<false, true>(g) : pick_main_kernel<false, false>(g);
   // Plain launches unless profiling (these are what stream capture records).
   hipError_t e = ev ? hipExtLaunchKernel(main_fn, dim3(grid), dim3(256), args, 0, st, ev[0], ev[1], 0)
                     : hipLaunchKernel(main_fn, dim3(grid), dim3(256), args, 0, st);
@@ -1901,8 +2062,8 @@ static int launch_decode(Params& prm, const Geometry& g, bool sparse, hipStream_
 
 extern "C" int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* block_table,
                               const int32_t* cache_seqlens, int batch, int s_q, int h_q, int num_blocks,
-                              int max_blocks_per_seq, float softmax_scale, int causal, const int32_t* sched,
-                              int num_parts, const int32_t* num_splits, void* workspace,
+                              int max_blocks_per_seq, float softmax_scale, int causal, int is_fp8,
+                              const int32_t* sched, int num_parts, const int32_t* num_splits, void* workspace,
                               size_t workspace_bytes, void* out, float* lse, void* stream) {
   if (!q || !kv_cache || !block_table || !cache_seqlens || !sched || !num_splits || !out || !lse)
     return set_error(MLA_ERR_INVALID, "mla_decode_fwd: null pointer argument");
@@ -1913,6 +2074,7 @@ extern "C" int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t
   if (!std::isfinite(softmax_scale) || softmax_scale < 0.f)
     return set_error(MLA_ERR_INVALID, "mla_decode_fwd: softmax_scale must be finite and >= 0");
   if (causal != 0 && causal != 1) return set_error(MLA_ERR_INVALID, "mla_decode_fwd: causal must be 0 or 1");
+  if (is_fp8 != 0 && is_fp8 != 1) return set_error(MLA_ERR_INVALID, "mla_decode_fwd: is_fp8 must be 0 or 1");
   const Geometry g = geometry(h_q, s_q);
   const int slots = num_parts + batch - 1;
   const size_t need = mla_workspace_bytes(slots, h_q, s_q);
@@ -1946,12 +2108,12 @@ extern "C" int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t
   prm.kv_tokens = num_blocks * kPage;
   prm.fold = 1;
 
-  return launch_decode(prm, g, false, (hipStream_t)stream, "mla_decode_fwd");
+  return launch_decode(prm, g, false, is_fp8 != 0, (hipStream_t)stream, "mla_decode_fwd");
 }
 
 extern "C" int mla_decode_sparse_fwd(const void* q, const void* kv_cache, const int32_t* indices,
                                      const int32_t* topk_length, int batch, int s_q, int h_q, int num_blocks,
-                                     int topk, float softmax_scale, const int32_t* sched, int num_parts,
+                                     int topk, float softmax_scale, int is_fp8, const int32_t* sched, int num_parts,
                                      const int32_t* num_splits, void* workspace, size_t workspace_bytes, void* out,
                                      float* lse, void* stream) {
   if (!q || !kv_cache || !indices || !sched || !num_splits || !out || !lse)
@@ -1962,6 +2124,7 @@ extern "C" int mla_decode_sparse_fwd(const void* q, const void* kv_cache, const 
                      batch, s_q, h_q, num_blocks, topk, num_parts);
   if (!std::isfinite(softmax_scale) || softmax_scale < 0.f)
     return set_error(MLA_ERR_INVALID, "mla_decode_sparse_fwd: softmax_scale must be finite and >= 0");
+  if (is_fp8 != 0 && is_fp8 != 1) return set_error(MLA_ERR_INVALID, "mla_decode_sparse_fwd: is_fp8 must be 0 or 1");
   const Geometry g = geometry_sparse(h_q);
   const int n = batch * s_q;   // one split-KV "request" per (request, query token)
   const int slots = num_parts + n - 1;
@@ -1995,6 +2158,6 @@ extern "C" int mla_decode_sparse_fwd(const void* q, const void* kv_cache, const 
   prm.topk = topk;
   prm.kv_tokens = num_blocks * kPage;
   prm.fold = s_q;
-  return launch_decode(prm, g, true, (hipStream_t)stream, "mla_decode_sparse_fwd");
+  return launch_decode(prm, g, true, is_fp8 != 0, (hipStream_t)stream, "mla_decode_sparse_fwd");
 }
 

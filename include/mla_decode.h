@@ -154,6 +154,8 @@ size_t mla_workspace_bytes(int total_splits, int h_q, int s_q);
  *   cache_seqlens device int32 [batch]; must equal the lengths the plan was
  *                 made from, and L <= 64 * max_blocks_per_seq
  *   softmax_scale multiplies the q.k scores; finite and >= 0
+ *   is_fp8        0: kv_cache is bf16 as above; 1: kv_cache holds FP8
+ *                 records, uint8 [num_blocks, 64, 1, 656] (see MLA_FP8_RECORD)
  *   causal        0: every query token sees all L keys (the dense path);
  *                 1: the s_q query tokens are the last s_q positions of the
  *                 sequence (multi-token prediction), so token s sees keys
@@ -168,7 +170,8 @@ size_t mla_workspace_bytes(int total_splits, int h_q, int s_q);
  *   lse           device fp32 [batch, h_q, s_q] (written; -inf when L = 0)
  *   stream        hipStream_t to enqueue on (NULL = the null stream)
  *
- * Enqueues the split-KV kernel (one of three, by R: <= 16, < 128, >= 128),
+ * Enqueues the split-KV kernel (one of three, by R: <= 16, < 128, >= 128;
+ * with an FP8 cache every R above 16 takes the 128-row kernel),
  * then the combine kernel (which returns at once when no request is split,
  * and skips the rows of requests that are not); returns without
  * synchronising and allocates nothing.  Block-table
@@ -178,9 +181,22 @@ size_t mla_workspace_bytes(int total_splits, int h_q, int s_q);
  */
 int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* block_table,
                    const int32_t* cache_seqlens, int batch, int s_q, int h_q, int num_blocks,
-                   int max_blocks_per_seq, float softmax_scale, int causal, const int32_t* sched,
-                   int num_parts, const int32_t* num_splits, void* workspace,
+                   int max_blocks_per_seq, float softmax_scale, int causal, int is_fp8,
+                   const int32_t* sched, int num_parts, const int32_t* num_splits, void* workspace,
                    size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/*
+ * FP8 cache ("[DeepSeek-3] FlashMLA", section 12), accepted by both decode
+ * entry points when is_fp8 = 1: each token is a 656-byte record
+ *   bytes   0 .. 511  latent dims 0 .. 511 as float8 e4m3 (OCP e4m3fn)
+ *   bytes 512 .. 527  four fp32 scales, scale i for dims 128 i .. 128 i + 127
+ *   bytes 528 .. 655  RoPE dims 512 .. 575 as bf16
+ * and a 64-token page is 64 consecutive records (41,984 bytes).  The method
+ * computes with the dequantized cache: latent value =
+ * bf16_rne(fp32(e4m3 * scale)), RoPE as stored (the pages dequantize to
+ * bf16 and run bf16 matrix products with fp32 accumulation).
+ */
+#define MLA_FP8_RECORD 656
 
 /*
  * Sparse (top-k) decode ("[DeepSeek-3] FlashMLA", section 11): query token s
@@ -227,10 +243,12 @@ int mla_get_metadata_sparse(const int32_t* topk_length, int batch, int s_q, int 
  * flash_mla_with_kvcache with indices, bf16 cache, head_dim_v = 512).
  *
  *   q             device bf16 [batch, s_q, h_q, 576]
- *   kv_cache      device bf16 [num_blocks, 64, 1, 576]; num_blocks <= 2^24
+ *   kv_cache      device bf16 [num_blocks, 64, 1, 576], or with is_fp8 = 1 the
+ *                 FP8 records uint8 [num_blocks, 64, 1, 656]; num_blocks <= 2^24
  *   indices       device int32 [batch, s_q, topk]
  *   topk_length   device int32 [batch] or NULL
  *   softmax_scale finite and >= 0
+ *   is_fp8        0 or 1 (the cache format, as above)
  *   sched, num_parts, num_splits  from mla_get_metadata_sparse with the same
  *                 batch, s_q, h_q, topk and topk_length
  *   workspace     device, >= mla_workspace_bytes(num_parts + batch * s_q - 1, h_q, 1)
@@ -244,7 +262,7 @@ int mla_get_metadata_sparse(const int32_t* topk_length, int batch, int s_q, int 
  * Errors: MLA_ERR_INVALID, MLA_ERR_WORKSPACE, MLA_ERR_HIP.
  */
 int mla_decode_sparse_fwd(const void* q, const void* kv_cache, const int32_t* indices, const int32_t* topk_length,
-                          int batch, int s_q, int h_q, int num_blocks, int topk, float softmax_scale,
+                          int batch, int s_q, int h_q, int num_blocks, int topk, float softmax_scale, int is_fp8,
                           const int32_t* sched, int num_parts, const int32_t* num_splits, void* workspace,
                           size_t workspace_bytes, void* out, float* lse, void* stream);
 

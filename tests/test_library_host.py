@@ -95,21 +95,24 @@ def test_plan_errors():
 
 def test_decode_argument_errors_return_codes_without_launching():
     L = mla.lib()
-    rc = L.mla_decode_fwd(None, None, None, None, 1, 1, 16, 1, 1, 0.1, 0, None, 1, None, None, 0, None, None, None)
+    rc = L.mla_decode_fwd(None, None, None, None, 1, 1, 16, 1, 1, 0.1, 0, 0, None, 1, None, None, 0, None, None, None)
     assert rc == -1 and b"null" in L.mla_last_error()
     dummy = ctypes.c_void_p(16)   # never dereferenced: every check fails before any launch
-    rc = L.mla_decode_fwd(dummy, dummy, dummy, dummy, 0, 1, 16, 1, 1, 0.1, 0, dummy, 1, dummy, dummy, 0,
+    rc = L.mla_decode_fwd(dummy, dummy, dummy, dummy, 0, 1, 16, 1, 1, 0.1, 0, 0, dummy, 1, dummy, dummy, 0,
                           dummy, dummy, None)
     assert rc == -1 and b"batch=0" in L.mla_last_error()
-    rc = L.mla_decode_fwd(dummy, dummy, dummy, dummy, 2, 1, 16, 8, 4, float("nan"), 0, dummy, 3, dummy, dummy, 0,
+    rc = L.mla_decode_fwd(dummy, dummy, dummy, dummy, 2, 1, 16, 8, 4, float("nan"), 0, 0, dummy, 3, dummy, dummy, 0,
                           dummy, dummy, None)
     assert rc == -1 and b"softmax_scale" in L.mla_last_error()
-    rc = L.mla_decode_fwd(dummy, dummy, dummy, dummy, 2, 1, 16, 8, 4, 0.1, 2, dummy, 3, dummy, dummy, 0,
+    rc = L.mla_decode_fwd(dummy, dummy, dummy, dummy, 2, 1, 16, 8, 4, 0.1, 2, 0, dummy, 3, dummy, dummy, 0,
                           dummy, dummy, None)
     assert rc == -1 and b"causal" in L.mla_last_error()
-    rc = L.mla_decode_fwd(dummy, dummy, dummy, dummy, 2, 1, 16, 8, 4, 0.1, 0, dummy, 3, dummy, dummy, 100,
+    rc = L.mla_decode_fwd(dummy, dummy, dummy, dummy, 2, 1, 16, 8, 4, 0.1, 0, 0, dummy, 3, dummy, dummy, 100,
                           dummy, dummy, None)
     assert rc == -3 and b"workspace" in L.mla_last_error()
+    rc = L.mla_decode_fwd(dummy, dummy, dummy, dummy, 2, 1, 16, 8, 4, 0.1, 0, 2, dummy, 3, dummy, dummy, 0,
+                          dummy, dummy, None)
+    assert rc == -1 and b"is_fp8" in L.mla_last_error()
 
 
 def test_device_planner_argument_errors_return_codes_without_launching():
@@ -146,20 +149,23 @@ def test_sparse_policy_matches_reference_plan_over_token_lists(h_q, s_q, topk_le
 def test_sparse_argument_errors_return_codes_without_launching():
     L = mla.lib()
     dummy = ctypes.c_void_p(16)   # never dereferenced: every check fails before any launch
-    rc = L.mla_decode_sparse_fwd(None, dummy, dummy, None, 1, 1, 16, 1, 64, 0.1, dummy, 1, dummy, dummy, 1 << 30,
+    rc = L.mla_decode_sparse_fwd(None, dummy, dummy, None, 1, 1, 16, 1, 64, 0.1, 0, dummy, 1, dummy, dummy, 1 << 30,
                                  dummy, dummy, None)
     assert rc == -1 and b"null" in L.mla_last_error()
-    rc = L.mla_decode_sparse_fwd(dummy, dummy, dummy, None, 1, 1, 16, 1, 0, 0.1, dummy, 1, dummy, dummy, 1 << 30,
+    rc = L.mla_decode_sparse_fwd(dummy, dummy, dummy, None, 1, 1, 16, 1, 0, 0.1, 0, dummy, 1, dummy, dummy, 1 << 30,
                                  dummy, dummy, None)
     assert rc == -1 and b"topk=0" in L.mla_last_error()
-    rc = L.mla_decode_sparse_fwd(dummy, dummy, dummy, None, 1, 1, 16, (1 << 24) + 1, 64, 0.1, dummy, 1, dummy, dummy,
+    rc = L.mla_decode_sparse_fwd(dummy, dummy, dummy, None, 1, 1, 16, (1 << 24) + 1, 64, 0.1, 0, dummy, 1, dummy, dummy,
                                  1 << 30, dummy, dummy, None)
     assert rc == -1 and b"num_blocks" in L.mla_last_error()
-    rc = L.mla_decode_sparse_fwd(dummy, dummy, dummy, None, 2, 2, 16, 8, 64, -1.0, dummy, 3, dummy, dummy, 1 << 30,
+    rc = L.mla_decode_sparse_fwd(dummy, dummy, dummy, None, 2, 2, 16, 8, 64, -1.0, 0, dummy, 3, dummy, dummy, 1 << 30,
                                  dummy, dummy, None)
     assert rc == -1 and b"softmax_scale" in L.mla_last_error()
-    rc = L.mla_decode_sparse_fwd(dummy, dummy, dummy, None, 2, 2, 16, 8, 64, 0.1, dummy, 3, dummy, dummy, 100,
+    rc = L.mla_decode_sparse_fwd(dummy, dummy, dummy, None, 2, 2, 16, 8, 64, 0.1, 0, dummy, 3, dummy, dummy, 100,
                                  dummy, dummy, None)
     assert rc == -3 and b"workspace" in L.mla_last_error()
+    rc = L.mla_decode_sparse_fwd(dummy, dummy, dummy, None, 2, 2, 16, 8, 64, 0.1, 3, dummy, 3, dummy, dummy, 1 << 30,
+                                 dummy, dummy, None)
+    assert rc == -1 and b"is_fp8" in L.mla_last_error()
     with pytest.raises(mla.MlaError, match="topk"):
         mla.get_mla_metadata_sparse_host(None, 2, 1, 16, 0, num_cus=8)
