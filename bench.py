@@ -124,7 +124,8 @@ def time_steps(step, rot: int, steps: int, warmup: int):
     return ms_per_step, graph_steps, main_ms / calls, comb_ms / calls, eager_ms
 
 
-def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6, causal: bool = False):
+def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6, causal: bool = False,
+                 fp8: bool = False):
     """Times one dense workload (see time_steps), one step per rotating copy
     of q and the KV pool so that no step finds its pages in cache."""
     import torch
@@ -134,14 +135,16 @@ def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6
     t = time.perf_counter()
     inp = W.config_inputs(idx)
     log(f"[bench] config {idx} {inp.name}: inputs drawn in {time.perf_counter() - t:.1f}s")
-    flops, nbytes = W.algorithmic_work(inp.cache_seqlens, inp.s_q, inp.h_q, causal=causal)
+    flops, nbytes = W.algorithmic_work(inp.cache_seqlens, inp.s_q, inp.h_q, causal=causal,
+                                       kv_row_bytes=W.FP8_RECORD if fp8 else 2 * W.D_QK)
     dev = torch.device("cuda", 0)
 
     def bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    kv0, q0 = bf16(inp.kv_cache), bf16(inp.q)
-    kv_bytes = kv0.numel() * 2
+    kv0 = torch.from_numpy(W.to_fp8_records(inp.kv_cache)).to(dev) if fp8 else bf16(inp.kv_cache)
+    q0 = bf16(inp.q)
+    kv_bytes = kv0.numel() * kv0.element_size()
     rot = int(min(8, max(1, np.ceil(min_rot_bytes / kv_bytes))))
     kvs = [kv0] + [kv0.clone() for _ in range(rot - 1)]
     qs = [q0] + [q0.clone() for _ in range(rot - 1)]
@@ -182,12 +185,12 @@ def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6
 
     def step(i):
         mla.mla_decode_fwd(qs[i % rot], kvs[i % rot], bt, sl, inp.softmax_scale, sched, ns, out=out, lse=lse,
-                           workspace=ws, causal=causal)
+                           workspace=ws, causal=causal, fp8=fp8)
 
     ms_per_step, graph_steps, main_avg, comb_avg, eager_ms = time_steps(step, rot, steps, warmup)
 
     res = dict(
-        workload=inp.name + ("_causal" if causal else ""), batch=b, s_q=inp.s_q, h_q=inp.h_q,
+        workload=inp.name + ("_causal" if causal else "") + ("_fp8" if fp8 else ""), batch=b, s_q=inp.s_q, h_q=inp.h_q,
         sum_seqlen=int(inp.cache_seqlens.sum()),
         parts=int(sched.shape[0]), total_splits=int(total), rotating_copies=rot, graph_steps=graph_steps,
         flops=flops, bytes=nbytes, ms_per_step=ms_per_step, eager_ms_per_step=eager_ms,
@@ -195,14 +198,14 @@ def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6
         tflops=flops / (ms_per_step * 1e-3) / 1e12, gbs=nbytes / (ms_per_step * 1e-3) / 1e9,
         main_kernel_tflops=flops / (main_avg * 1e-3) / 1e12, main_kernel_gbs=nbytes / (main_avg * 1e-3) / 1e9,
     )
-    log(f"[bench] config {idx}{' causal' if causal else ''}: "
+    log(f"[bench] config {idx}{' causal' if causal else ''}{' fp8' if fp8 else ''}: "
         f"{json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()})}")
     del kvs, qs
     torch.cuda.empty_cache()
     return inp, res
 
 
-def run_sparse_workload(steps: int, warmup: int, min_rot_bytes: float = 640e6):
+def run_sparse_workload(steps: int, warmup: int, min_rot_bytes: float = 640e6, fp8: bool = False):
     """Times the sparse workload (batch 128, s_q 2, h_q 128, topk 2048; each
     query token's 2048 keys drawn from its request's 4096..8192-token
     context) the same way as the dense ones."""
@@ -213,14 +216,16 @@ def run_sparse_workload(steps: int, warmup: int, min_rot_bytes: float = 640e6):
     t = time.perf_counter()
     inp = W.sparse_config_inputs()
     log(f"[bench] sparse {inp.name}: inputs drawn in {time.perf_counter() - t:.1f}s")
-    flops, nbytes = W.sparse_algorithmic_work(inp.indices, inp.h_q, inp.topk_length)
+    flops, nbytes = W.sparse_algorithmic_work(inp.indices, inp.h_q, inp.topk_length,
+                                              kv_row_bytes=W.FP8_RECORD if fp8 else 2 * W.D_QK)
     dev = torch.device("cuda", 0)
 
     def bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    kv0, q0 = bf16(inp.kv_cache), bf16(inp.q)
-    rot = int(min(8, max(1, np.ceil(min_rot_bytes / (kv0.numel() * 2)))))
+    kv0 = torch.from_numpy(W.to_fp8_records(inp.kv_cache)).to(dev) if fp8 else bf16(inp.kv_cache)
+    q0 = bf16(inp.q)
+    rot = int(min(8, max(1, np.ceil(min_rot_bytes / (kv0.numel() * kv0.element_size())))))
     kvs = [kv0] + [kv0.clone() for _ in range(rot - 1)]
     qs = [q0] + [q0.clone() for _ in range(rot - 1)]
     idx = torch.from_numpy(inp.indices).to(dev)
@@ -233,17 +238,18 @@ def run_sparse_workload(steps: int, warmup: int, min_rot_bytes: float = 640e6):
 
     def step(i):
         mla.mla_decode_sparse_fwd(qs[i % rot], kvs[i % rot], idx, inp.softmax_scale, sched, ns, out=out, lse=lse,
-                                  workspace=ws)
+                                  workspace=ws, fp8=fp8)
 
     ms_per_step, graph_steps, main_avg, comb_avg, eager_ms = time_steps(step, rot, steps, warmup)
     res = dict(
-        workload=inp.name, batch=inp.batch, s_q=inp.s_q, h_q=inp.h_q, topk=inp.topk, parts=int(sched.shape[0]),
+        workload=inp.name + ("_fp8" if fp8 else ""), batch=inp.batch, s_q=inp.s_q, h_q=inp.h_q, topk=inp.topk,
+        parts=int(sched.shape[0]),
         total_splits=int(ns[-1].item()), rotating_copies=rot, graph_steps=graph_steps, flops=flops, bytes=nbytes,
         ms_per_step=ms_per_step, eager_ms_per_step=eager_ms, main_kernel_ms=main_avg, combine_kernel_ms=comb_avg,
         tflops=flops / (ms_per_step * 1e-3) / 1e12, gbs=nbytes / (ms_per_step * 1e-3) / 1e9,
         main_kernel_tflops=flops / (main_avg * 1e-3) / 1e12, main_kernel_gbs=nbytes / (main_avg * 1e-3) / 1e9,
     )
-    log(f"[bench] sparse: {json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()})}")
+    log(f"[bench] sparse{' fp8' if fp8 else ''}: {json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()})}")
     del kvs, qs
     torch.cuda.empty_cache()
     return inp, res
@@ -277,7 +283,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2,
-                    help="headline workload (1..5); 6 times the sparse workload alone (for profiling)")
+                    help="headline workload (1..5); 6 times the sparse workload alone, 7 workload 2 on an FP8 "
+                         "cache and 8 the sparse workload on an FP8 cache (for profiling)")
     ap.add_argument("--no-extra", action="store_true", help="skip the h_q=128 workloads")
     ap.add_argument("--extra-steps", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -292,11 +299,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     mla.lib()
-    if args.config == 6:
-        _, r = run_sparse_workload(args.steps, args.warmup)
-        print(json.dumps(dict(metric="sparse decode TFLOP/s", value=r["tflops"], unit="TFLOP/s", n_gpus=1,
-                              steps=args.steps, warmup=args.warmup, ms_per_step=r["ms_per_step"],
-                              higher_is_better=True, dtype="bf16", data="synthetic", detail=r)), flush=True)
+    if args.config in (6, 7, 8):   # profiling entry points: one workload, no headline line
+        if args.config == 7:
+            _, r = run_workload(2, args.steps, args.warmup, fp8=True)
+            metric, value, unit = "decode GB/s, FP8 cache", r["gbs"], "GB/s"
+        else:
+            _, r = run_sparse_workload(args.steps, args.warmup, fp8=args.config == 8)
+            metric, value, unit = "sparse decode TFLOP/s", r["tflops"], "TFLOP/s"
+        print(json.dumps(dict(metric=metric, value=value, unit=unit, n_gpus=1, steps=args.steps, warmup=args.warmup,
+                              ms_per_step=r["ms_per_step"], higher_is_better=True, dtype="bf16", data="synthetic",
+                              detail=r)), flush=True)
         return
 
     inp, head = run_workload(args.config, args.steps, args.warmup)
@@ -332,13 +344,20 @@ def main():
                 main_kernel_ms=r["main_kernel_ms"], combine_kernel_ms=r["combine_kernel_ms"],
                 parts=r["parts"], total_splits=r["total_splits"], plan_us=r["plan_us"],
                 plan_device_us=r["plan_device_us"])
-        _, r = run_sparse_workload(args.extra_steps, max(2, args.extra_steps // 5))
-        extra["sparse"] = dict(
-            workload=r["workload"], tflops=r["tflops"], frac_mfma_peak=r["tflops"] / MFMA_PEAK_TFLOPS,
-            gbs=r["gbs"], frac_hbm_peak=r["gbs"] / HBM_PEAK_GBS, ms_per_step=r["ms_per_step"],
-            eager_ms_per_step=r["eager_ms_per_step"], main_kernel_tflops=r["main_kernel_tflops"],
-            main_kernel_ms=r["main_kernel_ms"], combine_kernel_ms=r["combine_kernel_ms"],
-            parts=r["parts"], total_splits=r["total_splits"])
+        _, r = run_workload(2, args.extra_steps, max(2, args.extra_steps // 5), fp8=True)
+        extra["config2_fp8"] = dict(
+            workload=r["workload"], gbs=r["gbs"], frac_hbm_peak=r["gbs"] / HBM_PEAK_GBS, tflops=r["tflops"],
+            ms_per_step=r["ms_per_step"], eager_ms_per_step=r["eager_ms_per_step"],
+            main_kernel_gbs=r["main_kernel_gbs"], main_kernel_ms=r["main_kernel_ms"],
+            combine_kernel_ms=r["combine_kernel_ms"], parts=r["parts"], total_splits=r["total_splits"])
+        for fp8 in (False, True):
+            _, r = run_sparse_workload(args.extra_steps, max(2, args.extra_steps // 5), fp8=fp8)
+            extra["sparse_fp8" if fp8 else "sparse"] = dict(
+                workload=r["workload"], tflops=r["tflops"], frac_mfma_peak=r["tflops"] / MFMA_PEAK_TFLOPS,
+                gbs=r["gbs"], frac_hbm_peak=r["gbs"] / HBM_PEAK_GBS, ms_per_step=r["ms_per_step"],
+                eager_ms_per_step=r["eager_ms_per_step"], main_kernel_tflops=r["main_kernel_tflops"],
+                main_kernel_ms=r["main_kernel_ms"], combine_kernel_ms=r["combine_kernel_ms"],
+                parts=r["parts"], total_splits=r["total_splits"])
 
     line = dict(
         metric=METRIC, value=value, unit=unit, n_gpus=1, steps=args.steps, warmup=args.warmup,

@@ -249,10 +249,12 @@ def sparse_config_inputs(seed: int = 6) -> SparseInputs:
     return make_sparse_inputs(c["batch"], c["s_q"], c["h_q"], c["topk"], c["context"], seed=seed, name=c["name"])
 
 
-def sparse_algorithmic_work(indices: np.ndarray, h_q: int, topk_length=None) -> tuple[float, float]:
+def sparse_algorithmic_work(indices: np.ndarray, h_q: int, topk_length=None,
+                            kv_row_bytes: int = 2 * D_QK) -> tuple[float, float]:
     """(FLOPs, bytes) of one sparse decode call: every counted entry of every
     query token's list is one key (576 + 512 dims, 2 FLOPs each, h_q heads)
-    and one 1152-byte cache row read; plus the index list (4 B per entry),
+    and one cache row read (1152 bytes in bf16, 656 as an FP8 record);
+    plus the index list (4 B per entry),
     q read, out written (bf16) and lse written (fp32)."""
     b, s_q, topk = indices.shape
     keys = 0
@@ -261,7 +263,7 @@ def sparse_algorithmic_work(indices: np.ndarray, h_q: int, topk_length=None) -> 
         keys += int((indices[i, :, :n] >= 0).sum())
     rows = b * s_q * h_q
     flops = 2.0 * h_q * keys * (D_QK + D_V)
-    nbytes = 2.0 * D_QK * keys + 4.0 * b * s_q * topk + 2.0 * rows * (D_QK + D_V) + 4.0 * rows
+    nbytes = float(kv_row_bytes) * keys + 4.0 * b * s_q * topk + 2.0 * rows * (D_QK + D_V) + 4.0 * rows
     return flops, nbytes
 
 
@@ -292,34 +294,49 @@ def _e4m3_table() -> np.ndarray:
 E4M3 = _e4m3_table()
 
 
-def quantize_e4m3(x: np.ndarray) -> np.ndarray:
-    """Round float values to the nearest e4m3fn byte (ties to the even
-    mantissa), saturating at +-448.  Input generation only: the cache's
-    writer quantizes, the method reads the bytes."""
-    x = np.clip(np.asarray(x, np.float64), -FP8_MAX, FP8_MAX)
-    pos = E4M3[:0x7f]                 # 0x00 .. 0x7e: ascending non-negative values
-    mag = np.abs(x)
-    hi = np.clip(np.searchsorted(pos, mag, side="left"), 0, 0x7e)
-    lo = np.clip(hi - 1, 0, 0x7e)
-    dlo, dhi = mag - pos[lo], pos[hi] - mag
-    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
-    return (pick | np.where(np.signbit(x) & (pick != 0), 0x80, 0)).astype(np.uint8)
+def quantize_e4m3(x: np.ndarray, chunk: int = 1 << 20) -> np.ndarray:
+    """Round fp32 values to the nearest e4m3fn byte (ties to the even
+    mantissa), saturating at +-448, by integer arithmetic on the fp32 bits
+    (in chunks, so that the temporaries stay small).  Input generation only:
+    the cache's writer quantizes, the method reads the bytes."""
+    x = np.asarray(x, np.float32)
+    if x.size > chunk:
+        out = np.empty(x.shape, np.uint8)
+        xf, of = x.reshape(-1), out.reshape(-1)
+        for s in range(0, xf.size, chunk):
+            of[s:s + chunk] = quantize_e4m3(xf[s:s + chunk], chunk)
+        return out
+    v = np.clip(x, -FP8_MAX, FP8_MAX)
+    a = np.abs(v)
+    bits = a.view(np.uint32)
+    e0 = (bits >> 23).astype(np.int32) - 127          # unbiased fp32 exponent
+    man = bits & 0x7FFFFF
+    m3 = (man >> 20).astype(np.int32)                 # top 3 mantissa bits
+    rem = man & 0xFFFFF
+    m3 = m3 + ((rem > 0x80000) | ((rem == 0x80000) & ((m3 & 1) == 1)))   # round half to even
+    e = e0 + (m3 >> 3)                                # mantissa carry into the exponent
+    normal = ((e + 7) << 3) | (m3 & 7)
+    sub = np.rint(a * np.float32(512.0)).astype(np.int32)   # below 2^-6: multiples of 2^-9 (8 -> 2^-6)
+    byte = np.where(e0 >= -6, normal, sub)
+    sign = np.where(np.signbit(v) & (byte != 0), 0x80, 0)
+    return (byte | sign).astype(np.uint8)
 
 
-def to_fp8_records(kv_bf16: np.ndarray) -> np.ndarray:
+def to_fp8_records(kv_bf16: np.ndarray, pages_per_chunk: int = 256) -> np.ndarray:
     """FP8 records of a bf16 cache [nb, 64, 1, 576]: per token and 128-dim
-    tile, scale = max |x| / 448 (1 for an all-zero tile), bytes =
-    e4m3(x / scale); RoPE dims copied.  Returns uint8 [nb, 64, 1, 656]."""
+    tile, scale = fp32(max |x| / 448) (1 for an all-zero tile), bytes =
+    e4m3(fp32(x / scale)); RoPE dims copied.  Returns uint8 [nb, 64, 1, 656]."""
     nb = kv_bf16.shape[0]
-    x = bf16_bits_to_f32(kv_bf16.reshape(nb, PAGE, D_QK)).astype(np.float64)
-    lat = x[..., :D_V].reshape(nb, PAGE, 4, 128)
-    amax = np.abs(lat).max(axis=-1)
-    scale = np.where(amax > 0, amax / FP8_MAX, 1.0).astype(np.float32)
-    q8 = quantize_e4m3(lat / scale[..., None].astype(np.float64)).reshape(nb, PAGE, D_V)
     rec = np.empty((nb, PAGE, FP8_RECORD), np.uint8)
-    rec[..., :D_V] = q8
-    rec[..., D_V:D_V + 16] = scale.view(np.uint8).reshape(nb, PAGE, 16)
-    rec[..., D_V + 16:] = kv_bf16.reshape(nb, PAGE, D_QK)[..., D_V:].view(np.uint8).reshape(nb, PAGE, 128)
+    for p0 in range(0, nb, pages_per_chunk):
+        p1 = min(nb, p0 + pages_per_chunk)
+        bits = kv_bf16[p0:p1].reshape(p1 - p0, PAGE, D_QK)
+        lat = bf16_bits_to_f32(bits[..., :D_V]).reshape(p1 - p0, PAGE, 4, 128)
+        amax = np.abs(lat).max(axis=-1)
+        scale = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
+        rec[p0:p1, :, :D_V] = quantize_e4m3(lat / scale[..., None]).reshape(p1 - p0, PAGE, D_V)   # fp32 division
+        rec[p0:p1, :, D_V:D_V + 16] = scale.view(np.uint8).reshape(p1 - p0, PAGE, 16)
+        rec[p0:p1, :, D_V + 16:] = np.ascontiguousarray(bits[..., D_V:]).view(np.uint8).reshape(p1 - p0, PAGE, 128)
     return rec.reshape(nb, PAGE, 1, FP8_RECORD)
 
 
@@ -330,13 +347,14 @@ def config_inputs(index: int) -> MlaInputs:
                        c["max_blocks"], seed=index, name=c["name"])
 
 
-def algorithmic_work(seqlens, s_q: int, h_q: int, causal: bool = False) -> tuple[float, float]:
+def algorithmic_work(seqlens, s_q: int, h_q: int, causal: bool = False, kv_row_bytes: int = 2 * D_QK) -> tuple[float, float]:
     """(FLOPs, bytes) the method must do for one decode call.
 
     FLOPs = 2 * h_q * sum over (request, query token) of the keys it sees *
     (576 + 512): the QK^T and PV products (all L keys, or with the causal
     mask L - (s_q - 1 - s) for query token s).  Bytes = bf16 KV read once per
-    request, q read, out written (bf16), lse written (fp32).  Masked tail
+    request (1152 bytes a token in bf16, 656 as an FP8 record), q read,
+    out written (bf16), lse written (fp32).  Masked tail
     tokens, split partials and the block table are overhead and are not
     counted.
     """
@@ -346,7 +364,7 @@ def algorithmic_work(seqlens, s_q: int, h_q: int, causal: bool = False) -> tuple
     b = int(sl.shape[0])
     seen = s_q * total if not causal else int(sum(np.maximum(sl - (s_q - 1 - s), 0).sum() for s in range(s_q)))
     flops = 2.0 * h_q * seen * (D_QK + D_V)
-    nbytes = 2.0 * (total * D_QK + b * R * D_QK + b * R * D_V) + 4.0 * b * R
+    nbytes = float(kv_row_bytes) * total + 2.0 * (b * R * D_QK + b * R * D_V) + 4.0 * b * R
     return flops, nbytes
 
 
