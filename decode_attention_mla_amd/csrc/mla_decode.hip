@@ -328,35 +328,37 @@ __device__ __forceinline__ void issue_fp8_gather(const Params& p, int entry_row,
 }
 
 // Dequantize this wave's 16 records (fp8 slice) into its bf16 stage slice
-// (the 16-token layout above).  Lane (t = lane / 4, q = lane % 4) converts
-// dims 128 q .. 128 q + 127 of token t with scale q, and copies RoPE bytes
-// 32 q .. 32 q + 31 of the token.
+// (the 16-token layout above).  Block b (dims 64 b .. 64 b + 63) of local
+// token t = lane / 8 + 8 r, chunk c = lane % 8 (dims 64 b + 8 c .. + 7): a
+// 16-lane pass then reads 8-byte chunks of two records and writes 16-byte
+// chunks of two rows, each on distinct LDS banks.  Blocks 0..7 hold the
+// e4m3 latent (scale b / 2), block 8 the bf16 RoPE, copied.
 __device__ __forceinline__ void dequant_fp8_slice(LDS_PTR(unsigned char) fp8, LDS_PTR(unsigned char) bf, int lane) {
-  const int t = lane >> 2, q = lane & 3;
-  LDS_PTR(unsigned char) rec = fp8 + t * kFp8Row;
-  const float sc = *(LDS_PTR(float))(rec + kDv + 4 * q);
-  const int swz = stage_swizzle(t);
+  const int c = lane & 7;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const u32x4 v = *(LDS_PTR(u32x4))(rec + 128 * q + 16 * k);
-    u32x4 w[2];
+  for (int r = 0; r < 2; ++r) {
+    const int t = (lane >> 3) + 8 * r;
+    LDS_PTR(unsigned char) rec = fp8 + t * kFp8Row;
+    LDS_PTR(unsigned char) row = bf + t * 128 + ((c ^ stage_swizzle(t)) << 4);
+    float sc[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[e], false);   // bytes 0, 1
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[e], true);    // bytes 2, 3
-      w[e >> 1][2 * (e & 1)] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)(lo[0] * sc), (__bf16)(lo[1] * sc)});
-      w[e >> 1][2 * (e & 1) + 1] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)(hi[0] * sc), (__bf16)(hi[1] * sc)});
+    for (int q = 0; q < 4; ++q) sc[q] = *(LDS_PTR(float))(rec + kDv + 4 * q);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const u32x2 v = *(LDS_PTR(u32x2))(rec + 64 * b + 8 * c);
+      const float s = sc[b >> 1];
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[e], false);   // bytes 0, 1
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[e], true);    // bytes 2, 3
+        w[2 * e] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)(lo[0] * s), (__bf16)(lo[1] * s)});
+        w[2 * e + 1] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)(hi[0] * s), (__bf16)(hi[1] * s)});
+      }
+      *(LDS_PTR(u32x4))(row + b * kStageBlock) = w;
     }
-    // dims d0 = 128 q + 16 k: block d0 / 64, in-block chunks c0, c0 + 1
-    const int b = 2 * q + (k >> 2), c0 = 2 * (k & 3);
-    LDS_PTR(unsigned char) row = bf + b * kStageBlock + t * 128;
-    *(LDS_PTR(u32x4))(row + ((c0 ^ swz) << 4)) = w[0];
-    *(LDS_PTR(u32x4))(row + (((c0 + 1) ^ swz) << 4)) = w[1];
-  }
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {   // RoPE dims 512 + 8 (2 q + k) .. + 7: block 8, chunk 2 q + k
-    const u32x4 v = *(LDS_PTR(u32x4))(rec + kDv + 16 + 32 * q + 16 * k);
-    *(LDS_PTR(u32x4))(bf + 8 * kStageBlock + t * 128 + (((2 * q + k) ^ swz) << 4)) = v;
+    // RoPE dims 512 + 8 c .. + 7 (record bytes 528 + 16 c): block 8, chunk c
+    *(LDS_PTR(u32x4))(row + 8 * kStageBlock) = *(LDS_PTR(u32x4))(rec + kDv + 16 + 16 * c);
   }
 }
 
@@ -558,11 +560,15 @@ __device__ __forceinline__ float row_sum4(float v) {
 
 // kSparse: the key lists of sparse decode instead of block-table pages
 // (gathered copies, per-token key masks).  kFp8: an FP8 cache; one bf16
-// page stage (the dequantized page being computed) and one stage of FP8
-// records (the next page, in flight) replace the two bf16 stages.
+// page stage (the dequantized page being computed) and stages of FP8
+// records replace the two bf16 stages: two for block-table pages (pages
+// j + 1 and j + 2 in flight while page j is computed), one for sparse
+// lists (whose entries are loaded by the compiler, whose waits would
+// otherwise wait for every copy in flight).
 template <bool kSparse, bool kFp8>
 __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kFp8 ? kPageBytes + kFp8Page : 2 * kPageBytes];
+  constexpr int kF8Stages = kFp8 ? (kSparse ? 1 : 2) : 0;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kFp8 ? kPageBytes + kF8Stages * kFp8Page : 2 * kPageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char pbuf[kSmallPBytes];
   __shared__ float red[4][kSmallRows];   // per-wave row maxima, then row sums
   __shared__ int vote[4];                // per-wave restart votes
@@ -641,15 +647,16 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
     auto page_rows = [&](int blk) {
       return uniform_ptr(p.kv + (size_t)blk * kPageBytes + (size_t)tok0 * kRowBytes);
     };
-    // FP8: copy this wave's records of a page (block id, or gathered rows).
-    auto issue_fp8_page = [&](int blk, int entry_row) {
+    // FP8: copy this wave's records of a page (block id, or gathered rows) to FP8 stage f.
+    auto issue_fp8_page = [&](int blk, int entry_row, int f) {
       const unsigned char* rows = uniform_ptr(p.kv + (size_t)blk * kFp8Page + (size_t)tok0 * kFp8Row);
+      const unsigned dst = fslice + (unsigned)(f * kFp8Page);
 #pragma unroll
       for (int i = 0; i < kFp8Copies; ++i) {
         if constexpr (kSparse)
-          issue_fp8_gather<true>(p, entry_row, tok0, fslice, i, lane);
+          issue_fp8_gather<true>(p, entry_row, tok0, dst, i, lane);
         else
-          issue_fp8_copy<true>(rows, fslice, i, lane);
+          issue_fp8_copy<true>(rows, dst, i, lane);
       }
     };
 
@@ -684,15 +691,21 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
       unsigned long long mk_cur = g0.mask, mk_lo1 = g1.mask, mk_pending = 0;
       int ent_next = kFp8 ? ent[1] : ent[2];
       if constexpr (kFp8) {
-        if (lo < hi) issue_fp8_page(m.blk[0], g0.row);
+        if (lo < hi) issue_fp8_page(m.blk[0], g0.row, 0);
+        if (kF8Stages == 2 && lo + 1 < hi) issue_fp8_page(m.blk[1], 0, 1);
       } else if constexpr (kSparse) {
         if (lo < hi) issue_gather<true>(p, g0, dma_off, wslice);
       } else {
         if (lo < hi) issue_stage<true>(page_rows(m.blk[0]), wslice, dma_off);
       }
       if (attempt == 0) {
-        if (lo < hi && !kFp8)
-          wait_vmcnt<kStageSlices>();   // this wave's pieces of Q (the first page may still be in flight)
+        // this wave's pieces of Q (the first pages may still be in flight)
+        if (kF8Stages == 2 && lo + 1 < hi)
+          wait_vmcnt<2 * kFp8Copies>();
+        else if (kFp8 && lo < hi)
+          wait_vmcnt<kFp8Copies>();
+        else if (!kFp8 && lo < hi)
+          wait_vmcnt<kStageSlices>();
         else
           wait_vmcnt<0>();
         lds_barrier();                  // all of Q has landed
@@ -712,7 +725,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
         else
           issue_stage<true>(page_rows(m.blk[1]), wslice + kPageBytes, dma_off);
       }
-      int next_blk = kFp8 ? m.blk[1] : m.blk[2];   // block ids are read one page ahead of their copy
+      int next_blk = kF8Stages == 1 ? m.blk[1] : m.blk[2];   // block ids are read one page ahead of their copy
 
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) o[ct] = f32x4{0, 0, 0, 0};
@@ -725,26 +738,32 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
         LDS_PTR(unsigned char) buf = lds + stage * kPageBytes;
         // This wave's slice of page j (the next page's copy, if any, is issued
         // below, after the barrier).
-        if (j == lo && lo + 1 < hi && !kFp8)
+        if (kF8Stages == 2 && j + 1 < hi)
+          wait_vmcnt<kFp8Copies>();      // page j + 1's records may still be in flight
+        else if (j == lo && lo + 1 < hi && !kFp8)
           wait_vmcnt<kStageSlices>();
         else
           wait_vmcnt<0>();
         if constexpr (kFp8) {
           // Its records are in; once every wave is done with page j - 1 the
-          // bf16 stage takes page j, dequantized, and the records of page
-          // j + 1 go to the FP8 stage this wave has just read.
+          // bf16 stage takes page j, dequantized, and the FP8 stage this wave
+          // has just read takes the records of page j + 2 (one FP8 stage:
+          // j + 1).
           if (j > lo) lds_barrier();
-          dequant_fp8_slice(fp8s, buf + wave * kStageBytes, lane);
+          const int f = kF8Stages == 2 ? (j - lo) & 1 : 0;
+          dequant_fp8_slice(fp8s + f * kFp8Page, buf + wave * kStageBytes, lane);
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // its reads of the FP8 stage are done
-          if (j + 1 < hi) {
-            if constexpr (kSparse) {
+          if constexpr (kSparse) {
+            if (j + 1 < hi) {
               const GatherPage gn = gather_page(p, ent_next, j + 1, L, tok0, lane);
-              issue_fp8_page(0, gn.row);
+              issue_fp8_page(0, gn.row, 0);
               mk_pending = gn.mask;
               ent_next = load_page_entries(p, req, j + 2, lane);
-            } else {
-              issue_fp8_page(next_blk, 0);
-              next_blk = ld_uniform(bt + min(j + 2, p.max_blocks - 1));
+            }
+          } else {
+            if (j + 2 < hi) {
+              issue_fp8_page(next_blk, 0, f);
+              next_blk = ld_uniform(bt + min(j + 3, p.max_blocks - 1));
             }
           }
         }
