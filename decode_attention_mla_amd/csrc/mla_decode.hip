@@ -333,20 +333,31 @@ __device__ __forceinline__ void issue_fp8_gather(const Params& p, int entry_row,
 // 16-lane pass then reads 8-byte chunks of two records and writes 16-byte
 // chunks of two rows, each on distinct LDS banks.  Blocks 0..7 hold the
 // e4m3 latent (scale b / 2), block 8 the bf16 RoPE, copied.
+//   Every read of the slice is issued before the first write: the compiler
+// cannot tell the two stages apart, so a read placed after a write would
+// wait for it, and each block would pay a full LDS round trip in turn.
 __device__ __forceinline__ void dequant_fp8_slice(LDS_PTR(unsigned char) fp8, LDS_PTR(unsigned char) bf, int lane) {
   const int c = lane & 7;
+  u32x2 lat[2][8];
+  f32x4 sc[2];
+  u32x4 rope[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    LDS_PTR(unsigned char) rec = fp8 + ((lane >> 3) + 8 * r) * kFp8Row;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) lat[r][b] = *(LDS_PTR(u32x2))(rec + 64 * b + 8 * c);
+    sc[r] = *(LDS_PTR(f32x4))(rec + kDv);
+    // RoPE dims 512 + 8 c .. + 7 (record bytes 528 + 16 c): block 8, chunk c
+    rope[r] = *(LDS_PTR(u32x4))(rec + kDv + 16 + 16 * c);
+  }
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int t = (lane >> 3) + 8 * r;
-    LDS_PTR(unsigned char) rec = fp8 + t * kFp8Row;
     LDS_PTR(unsigned char) row = bf + t * 128 + ((c ^ stage_swizzle(t)) << 4);
-    float sc[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) sc[q] = *(LDS_PTR(float))(rec + kDv + 4 * q);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const u32x2 v = *(LDS_PTR(u32x2))(rec + 64 * b + 8 * c);
-      const float s = sc[b >> 1];
+      const u32x2 v = lat[r][b];
+      const float s = sc[r][b >> 1];
       u32x4 w;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
@@ -357,8 +368,7 @@ __device__ __forceinline__ void dequant_fp8_slice(LDS_PTR(unsigned char) fp8, LD
       }
       *(LDS_PTR(u32x4))(row + b * kStageBlock) = w;
     }
-    // RoPE dims 512 + 8 c .. + 7 (record bytes 528 + 16 c): block 8, chunk c
-    *(LDS_PTR(u32x4))(row + 8 * kStageBlock) = *(LDS_PTR(u32x4))(rec + kDv + 16 + 16 * c);
+    *(LDS_PTR(u32x4))(row + 8 * kStageBlock) = rope[r];
   }
 }
 
