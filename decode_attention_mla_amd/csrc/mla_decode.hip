@@ -372,6 +372,48 @@ __device__ __forceinline__ void dequant_fp8_slice(LDS_PTR(unsigned char) fp8, LD
   }
 }
 
+// The FP8 records of a wave's 16 tokens read straight into the K operand
+// of S^T = K Q^T in the small kernel's order of the contraction (k-step
+// ks, lane (g, c16): token c16, dims 64 (ks / 2) + 16 g + 8 (ks % 2) .. + 7):
+// lane (g, c16) holds token c16's latent bytes 64 m + 16 g .. + 15 (k-steps
+// 2 m, 2 m + 1), its four tile scales and its RoPE dims 512 + 16 g + 8 i ..
+// + 7 (k-step 16 + i).  Sixteen records lie 656 bytes apart, so each
+// 16-lane pass reads distinct LDS banks.
+struct Fp8Frags {
+  u32x4 lat[kDv / 64];
+  f32x4 sc;
+  u32x4 rope[2];
+};
+
+__device__ __forceinline__ Fp8Frags read_fp8_frags(LDS_PTR(unsigned char) slice, int c16, int g) {
+  Fp8Frags fr;
+  LDS_PTR(unsigned char) rec = slice + c16 * kFp8Row;
+#pragma unroll
+  for (int m = 0; m < kDv / 64; ++m) fr.lat[m] = *(LDS_PTR(u32x4))(rec + 64 * m + 16 * g);
+  fr.sc = *(LDS_PTR(f32x4))(rec + kDv);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) fr.rope[i] = *(LDS_PTR(u32x4))(rec + kDv + 16 + 32 * g + 16 * i);
+  return fr;
+}
+
+// K fragment ks in bf16: bf16_rne(fp32(e4m3 * tile scale)) for the latent,
+// the stored RoPE; zero for a token that is not a key (keep = 0).
+__device__ __forceinline__ u32x4 fp8_k_fragment(const Fp8Frags& fr, int ks, unsigned keep) {
+  if (ks >= kDv / 32) return fr.rope[ks - kDv / 32] & keep;
+  const u32x4 l = fr.lat[ks >> 1];
+  const u32x2 v = (ks & 1) ? u32x2{l[2], l[3]} : u32x2{l[0], l[1]};
+  const float s = fr.sc[ks >> 2];
+  u32x4 w;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[e], false);   // bytes 0, 1
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[e], true);    // bytes 2, 3
+    w[2 * e] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)(lo[0] * s), (__bf16)(lo[1] * s)});
+    w[2 * e + 1] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)(hi[0] * s), (__bf16)(hi[1] * s)});
+  }
+  return w & keep;
+}
+
 // Q^T fragments (B operand of 16x16x32): query row `row` (masked to zero when
 // >= R), dims 32 ks + 8 g .. + 7.
 __device__ __forceinline__ void load_q(bf16x8 (&qf)[kQkSteps], const Params& p, int req, int row, int g) {
@@ -578,6 +620,10 @@ __device__ __forceinline__ float row_sum4(float v) {
 template <bool kSparse, bool kFp8>
 __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
   constexpr int kF8Stages = kFp8 ? (kSparse ? 1 : 2) : 0;
+  // FP8 block-table pages are read one page ahead: page j + 1's records are
+  // read into registers (and the next copy issued) while page j's PV runs,
+  // then dequantized next to page j + 1's QK^T MFMAs.
+  constexpr bool kPipe = kFp8 && !kSparse;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kFp8 ? kPageBytes + kF8Stages * kFp8Page : 2 * kPageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char pbuf[kSmallPBytes];
   __shared__ float red[4][kSmallRows];   // per-wave row maxima, then row sums
@@ -612,11 +658,12 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
     q_dma_off[par] = t < p.R ? dma_off[par] : (unsigned)(((lane & 7) ^ stage_swizzle(t)) << 4);
   }
 
-  // QK A fragment of k-step ks: local token c16, logical chunk 4 ks + g =
-  // block ks / 2, in-block chunk 4 (ks % 2) + g.
+  // QK A fragment of k-step ks (and the Q^T B fragment, in the same order
+  // of the contraction): local token c16, block ks / 2, in-block chunk
+  // 2 g + ks % 2, so a lane's two k-steps of a block are 16 adjacent dims.
   int qk_off[2];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) qk_off[b] = c16 * 128 + (((4 * b + g) ^ stage_swizzle(c16)) << 4);
+  for (int b = 0; b < 2; ++b) qk_off[b] = c16 * 128 + (((2 * g + b) ^ stage_swizzle(c16)) << 4);
   // PV A fragment (V^T: 16 columns x 32 tokens of a 32-token step): lane
   // (g, c16) needs column c16 of the tile and step tokens 8 g .. 8 g + 7,
   // from two transposing reads r = 0, 1: the group's 16 lanes read tokens
@@ -743,74 +790,119 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
       l_run = 0.f;
       bool restart = false;
 
+      // FP8 block-table pages: the records of the page being computed, in
+      // the K operand layout (page lo's read here, the others during the
+      // previous page's PV).
+      Fp8Frags frn;
+      if constexpr (kPipe) {
+        if (lo < hi) {
+          if (lo + 1 < hi)
+            wait_vmcnt<kFp8Copies>();   // page lo + 1's records may still be in flight
+          else
+            wait_vmcnt<0>();
+          frn = read_fp8_frags(fp8s, c16, g);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // FP8 stage 0 has been read
+          if (lo + 2 < hi) {
+            issue_fp8_page(next_blk, 0, 0);
+            next_blk = ld_uniform(bt + min(lo + 3, p.max_blocks - 1));
+          }
+        }
+      }
+
       for (int j = lo; j < hi; ++j) {
         const int stage = kFp8 ? 0 : (j - lo) & 1;
         LDS_PTR(unsigned char) buf = lds + stage * kPageBytes;
         // This wave's slice of page j (the next page's copy, if any, is issued
         // below, after the barrier).
-        if (kF8Stages == 2 && j + 1 < hi)
-          wait_vmcnt<kFp8Copies>();      // page j + 1's records may still be in flight
-        else if (j == lo && lo + 1 < hi && !kFp8)
+        if constexpr (kPipe) {
+          // (page j's records were waited for and dequantized during page j - 1)
+        } else if (j == lo && lo + 1 < hi && !kFp8) {
           wait_vmcnt<kStageSlices>();
-        else
-          wait_vmcnt<0>();
-        if constexpr (kFp8) {
-          // Its records are in; once every wave is done with page j - 1 the
-          // bf16 stage takes page j, dequantized, and the FP8 stage this wave
-          // has just read takes the records of page j + 2 (one FP8 stage:
-          // j + 1).
-          if (j > lo) lds_barrier();
-          const int f = kF8Stages == 2 ? (j - lo) & 1 : 0;
-          dequant_fp8_slice(fp8s + f * kFp8Page, buf + wave * kStageBytes, lane);
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // its reads of the FP8 stage are done
-          if constexpr (kSparse) {
-            if (j + 1 < hi) {
-              const GatherPage gn = gather_page(p, ent_next, j + 1, L, tok0, lane);
-              issue_fp8_page(0, gn.row, 0);
-              mk_pending = gn.mask;
-              ent_next = load_page_entries(p, req, j + 2, lane);
-            }
-          } else {
-            if (j + 2 < hi) {
-              issue_fp8_page(next_blk, 0, f);
-              next_blk = ld_uniform(bt + min(j + 3, p.max_blocks - 1));
-            }
-          }
-        }
-        if constexpr (kSparse) {
-          const unsigned keep = (unsigned)(mk_cur >> tok0) & 0xFFFFu;
-          if (keep != 0xFFFFu) zero_stage_rows(buf + wave * kStageBytes, keep, lane);
         } else {
-          const int valid = min(kPage, L - j * kPage);
-          if (valid - tok0 < kWaveTokens) zero_stage_tail(buf + wave * kStageBytes, valid - tok0, lane);
+          wait_vmcnt<0>();
         }
-        lds_barrier();   // page j is visible; every wave is past page j - 1
-        // Page j + 1 goes to the stage page j - 1 held (pages lo, lo + 1 were
-        // issued ahead of the loop).  (A third page in flight from the start,
-        // held in registers, was measured slower: every page then lands late.)
-        if (j > lo && j + 1 < hi && !kFp8) {
-          if constexpr (kSparse) {
+        LDS_PTR(unsigned char) own = buf + wave * kStageBytes;
+        u32x4 kf[kQkSteps];
+        if constexpr (kPipe) {
+          if (j > lo) lds_barrier();   // every wave is done with page j - 1: the bf16 stage and P buffer are free
+        } else if constexpr (kFp8) {
+          // Sparse lists (one FP8 stage): its records are in; once every wave
+          // is done with page j - 1 (the bf16 stage and the P buffer are free)
+          // each lane reads its token's records in the K operand layout, and
+          // the FP8 stage takes the records of page j + 1.  The K fragments
+          // are dequantized in registers and written to the bf16 stage for PV
+          // (latent only; PV reads it after the barrier that publishes P).
+          if (j > lo) lds_barrier();
+          const Fp8Frags fr = read_fp8_frags(fp8s, c16, g);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // its reads of the FP8 stage are done
+          if (j + 1 < hi) {
             const GatherPage gn = gather_page(p, ent_next, j + 1, L, tok0, lane);
-            issue_gather<true>(p, gn, dma_off, wslice + ((j + 1 - lo) & 1) * kPageBytes);
+            issue_fp8_page(0, gn.row, 0);
             mk_pending = gn.mask;
             ent_next = load_page_entries(p, req, j + 2, lane);
-          } else {
-            issue_stage<true>(page_rows(next_blk), wslice + ((j + 1 - lo) & 1) * kPageBytes, dma_off);
-            next_blk = ld_uniform(bt + min(j + 2, p.max_blocks - 1));
           }
+          const unsigned keep = ((mk_cur >> (tok0 + c16)) & 1ull) != 0 ? ~0u : 0u;
+#pragma unroll
+          for (int ks = 0; ks < kQkSteps; ++ks) {
+            kf[ks] = fp8_k_fragment(fr, ks, keep);
+            if (ks < kDv / 32) *(LDS_PTR(u32x4))(own + (ks >> 1) * kStageBlock + qk_off[ks & 1]) = kf[ks];
+          }
+        }
+        if constexpr (!kFp8) {
+          if constexpr (kSparse) {
+            const unsigned keep = (unsigned)(mk_cur >> tok0) & 0xFFFFu;
+            if (keep != 0xFFFFu) zero_stage_rows(own, keep, lane);
+          } else {
+            const int valid = min(kPage, L - j * kPage);
+            if (valid - tok0 < kWaveTokens) zero_stage_tail(own, valid - tok0, lane);
+          }
+          lds_barrier();   // page j is visible; every wave is past page j - 1
+          // Page j + 1 goes to the stage page j - 1 held (pages lo, lo + 1 were
+          // issued ahead of the loop).  (A third page in flight from the start,
+          // held in registers, was measured slower: every page then lands late.)
+          if (j > lo && j + 1 < hi) {
+            if constexpr (kSparse) {
+              const GatherPage gn = gather_page(p, ent_next, j + 1, L, tok0, lane);
+              issue_gather<true>(p, gn, dma_off, wslice + ((j + 1 - lo) & 1) * kPageBytes);
+              mk_pending = gn.mask;
+              ent_next = load_page_entries(p, req, j + 2, lane);
+            } else {
+              issue_stage<true>(page_rows(next_blk), wslice + ((j + 1 - lo) & 1) * kPageBytes, dma_off);
+              next_blk = ld_uniform(bt + min(j + 2, p.max_blocks - 1));
+            }
+          }
+#pragma unroll
+          for (int ks = 0; ks < kQkSteps; ++ks)
+            kf[ks] = *(LDS_PTR(u32x4))(own + (ks >> 1) * kStageBlock + qk_off[ks & 1]);
         }
 
         // ---- S^T (this wave's 16 tokens x 16 rows) = K Q^T, three chains.
-        LDS_PTR(unsigned char) own = buf + wave * kStageBytes;
-        u32x4 kf[kQkSteps];
-#pragma unroll
-        for (int ks = 0; ks < kQkSteps; ++ks)
-          kf[ks] = *(LDS_PTR(u32x4))(own + (ks >> 1) * kStageBlock + qk_off[ks & 1]);
         f32x4 sacc[3] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+        if constexpr (kPipe) {
+          // FP8 block-table pages: K fragment ks is dequantized right before
+          // its MFMA (in the shadow of the previous ones) and its latent part
+          // written to the bf16 stage for PV.
+          auto qk = [&](unsigned keep) {
 #pragma unroll
-        for (int ks = 0; ks < kQkSteps; ++ks)
-          sacc[ks % 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[ks]), qf[ks],
-                                                                  sacc[ks % 3], 0, 0, 0);
+            for (int ks = 0; ks < kQkSteps; ++ks) {
+              const u32x4 k = fp8_k_fragment(frn, ks, keep);
+              if (ks < kDv / 32) *(LDS_PTR(u32x4))(own + (ks >> 1) * kStageBlock + qk_off[ks & 1]) = k;
+              sacc[ks % 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k), qf[ks],
+                                                                      sacc[ks % 3], 0, 0, 0);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          };
+          // (uniform: a page whose 16 tokens of this wave are all keys needs no mask)
+          if (L - j * kPage - tok0 >= kWaveTokens)
+            qk(~0u);
+          else
+            qk(tok0 + c16 < L - j * kPage ? ~0u : 0u);
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < kQkSteps; ++ks)
+            sacc[ks % 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[ks]), qf[ks],
+                                                                    sacc[ks % 3], 0, 0, 0);
+        }
         const f32x4 sv = sacc[0] + sacc[1] + sacc[2];
 
         // ---- softmax against the common reference (base 2).
@@ -863,6 +955,19 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
             const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv_off[1][i & 3]));
             return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
           };
+          // FP8 block-table pages: page j + 1's records (landed; page j + 2's
+          // copies may still be in flight) are read with the first V^T
+          // fragments, and its FP8 stage takes page j + 3 after the MFMAs.
+          const bool next = kPipe && j + 1 < hi;
+          if constexpr (kPipe) {
+            if (next) {
+              if (j + 2 < hi)
+                wait_vmcnt<kFp8Copies>();
+              else
+                wait_vmcnt<0>();
+              frn = read_fp8_frags(fp8s + ((j + 1 - lo) & 1) * kFp8Page, c16, g);
+            }
+          }
           const bf16x8 pB0 = *(LDS_PTR(bf16x8))(pb + lane * 16);
           const bf16x8 pB1 = *(LDS_PTR(bf16x8))(pb + (64 + lane) * 16);
           bf16x8 vf[kSmallPvLead];
@@ -874,6 +979,15 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
             o[i & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[i % kSmallPvLead], i < 8 ? pB0 : pB1, o[i & 7], 0, 0, 0);
             if (i + kSmallPvLead < 16) vf[i % kSmallPvLead] = vread(i + kSmallPvLead);
             __builtin_amdgcn_sched_barrier(0);
+          }
+          if constexpr (kPipe) {
+            if (next) {
+              asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this FP8 stage has been read
+              if (j + 3 < hi) {
+                issue_fp8_page(next_blk, 0, (j + 1 - lo) & 1);
+                next_blk = ld_uniform(bt + min(j + 4, p.max_blocks - 1));
+              }
+            }
           }
         }
         if constexpr (kSparse) mk_cur = j == lo && !kFp8 ? mk_lo1 : mk_pending;
