@@ -4,7 +4,9 @@ the oracle on the dequantized cache: a single key per request (the output is
 then the dequantized V row itself, so the in-kernel dequantization is checked
 bit for bit), every kernel (16 rows; 128-row groups, one or two; 32 and 64
 rows on the 128-row kernel), ragged lengths, forced splits, the causal mask,
-NaN records past the sequence end, and the memory-bound workload in full."""
+NaN records past the sequence end, the restart path, sparse identity lists
+against the dense path bit for bit, graph replay, and the memory-bound
+workload in full."""
 import numpy as np
 import pytest
 
@@ -139,3 +141,100 @@ def test_fp8_sparse_parity(case):
     out, lse = run_sparse_fp8(inp, rec, num_cus=cus)
     deq = W.SparseInputs(inp.name, inp.q, kv, inp.indices, inp.topk_length, inp.softmax_scale)
     assert_parity(out, lse, ref_out, ref_lse, f"fp8 sparse case {case}", out_tol=sparse_out_tol(deq))
+
+
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_fp8_restart_when_later_page_outgrows_first_max(h_q):
+    """First page scores ~0, a later page's ~+150 (far beyond the 2^64
+    headroom of the first page's reference): the restart path of the FP8
+    kernels (records read a page ahead on the small kernel) must match."""
+    rng = np.random.default_rng(3)
+    L = 64 * 5 + 7
+    keys = (0.01 * rng.standard_normal((L, W.D_QK))).astype(np.float32)
+    keys[64 * 3 + 5, :] = 0.5
+    keys[64 * 4 + 1, :] = -0.5
+    q = np.abs(rng.standard_normal((1, 1, h_q, W.D_QK))).astype(np.float32)
+    if h_q >= 128:
+        keep = np.zeros(h_q, dtype=bool)
+        keep[32:64] = True
+        q[0, 0, ~keep] *= 1e-3
+    inp = W.make_inputs(1, 1, h_q, [L], pool=8, max_blocks=6, seed=5)
+    kv = inp.kv_cache.copy()
+    for t in range(L):
+        kv[inp.block_table[0, t // 64], t % 64, 0] = W.f32_to_bf16_bits(keys[t])
+    inp.kv_cache = kv
+    inp.q = W.f32_to_bf16_bits(q)
+    inp.softmax_scale = 1.0
+    rec = W.to_fp8_records(inp.kv_cache)
+    ref_out, ref_lse = ref_dense_fp8(inp, rec)
+    assert ref_lse.max() > 100
+    for force in (0, 1):
+        out, lse = run_dense_fp8(inp, rec, force_splits=force)
+        assert_parity(out, lse, ref_out, ref_lse, f"fp8 restart h_q={h_q} force={force}", out_tol=out_tol_bound(inp))
+
+
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_fp8_sparse_identity_gather_equals_dense_bitwise(h_q):
+    """Index lists naming each request's dense keys in order, on FP8
+    records: the sparse kernels (gathered records, key masks) and the dense
+    ones (block-table records, read a page ahead on the small kernel) run
+    the same plan and the same arithmetic, so they agree bit for bit."""
+    import torch
+    inp = W.make_inputs(4, 1, h_q, [70, 640, 1, 3000], pool=70, max_blocks=48, seed=9)
+    rec = W.to_fp8_records(inp.kv_cache)
+    topk = 3008
+    idx = np.full((4, 1, topk), -1, dtype=np.int32)
+    for i in range(4):
+        L = int(inp.cache_seqlens[i])
+        t = np.arange(L)
+        idx[i, 0, :L] = inp.block_table[i, t // 64] * 64 + t % 64
+    q, kv = _bf16(inp.q), _dev(rec)
+    bt, sl = _dev(inp.block_table), _dev(inp.cache_seqlens)
+    for cus in (0, 256):
+        print(f"[fp8] identity gather h_q={h_q} cus={cus}", flush=True)
+        hs, hn = mla.get_mla_metadata(inp.cache_seqlens, h_q, 1, num_cus=cus)
+        dense_o, dense_l = mla.mla_decode_fwd(q, kv, bt, sl, inp.softmax_scale, hs, hn, fp8=True)
+        ss, sn = mla.get_mla_metadata_sparse(inp.cache_seqlens, 4, 1, h_q, topk, num_cus=cus)
+        assert torch.equal(ss.cpu(), hs.cpu()) and torch.equal(sn.cpu(), hn.cpu())
+        sp_o, sp_l = mla.mla_decode_sparse_fwd(q, kv, _dev(idx), inp.softmax_scale, ss, sn, topk_length=sl, fp8=True)
+        torch.cuda.synchronize()
+        assert torch.equal(sp_o, dense_o) and torch.equal(sp_l, dense_l)
+
+
+def test_fp8_graph_replay_matches_eager():
+    """The memory-bound workload on FP8 records, one decode call captured in
+    a HIP graph and replayed with eager work between replays: every replay
+    reproduces the eager result bit for bit."""
+    import torch
+    inp = W.config_inputs(2)
+    rec = W.to_fp8_records(inp.kv_cache)
+    q, kv = _bf16(inp.q), _dev(rec)
+    bt, sl = _dev(inp.block_table), _dev(inp.cache_seqlens)
+    sched, ns = mla.get_mla_metadata(inp.cache_seqlens, inp.h_q, inp.s_q)
+    ref_out, ref_lse = mla.mla_decode_fwd(q, kv, bt, sl, inp.softmax_scale, sched, ns, fp8=True)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = ref_out.clone(), ref_lse.clone()
+    out, lse = torch.empty_like(ref_out), torch.empty_like(ref_lse)
+    ws = torch.empty(mla.mla_workspace_bytes(sched.shape[0] + inp.batch - 1, inp.h_q, inp.s_q),
+                     dtype=torch.uint8, device=out.device)
+
+    def call():
+        mla.mla_decode_fwd(q, kv, bt, sl, inp.softmax_scale, sched, ns, out=out, lse=lse, workspace=ws, fp8=True)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        call()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.synchronize()
+    print("[fp8] graph replay", flush=True)
+    for _ in range(4):
+        out.zero_()
+        lse.fill_(1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
