@@ -32,15 +32,29 @@ METRIC = "MLA decode TFLOPs (h_q=128) and effective HBM GB/s (h_q=16), 1 MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SRC = os.path.join(ROOT, "decode_attention_mla_amd", "csrc", "mla_decode.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "decode_attention_mla_amd", "csrc", f) for f in ("mla_decode.hip", "mla_internal.h")]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace collapsed."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """First 16 hex digits of the sha256 of the kernels' code (comments and
+    whitespace dropped, so that rewording a comment keeps the committed
+    counter measurements valid)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        h.update(_code_only(open(path).read()).encode())
+    return h.hexdigest()[:16]
 
 
 def main_kernel_name(rows: int) -> str:

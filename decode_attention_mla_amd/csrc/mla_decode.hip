@@ -591,6 +591,10 @@ __device__ __forceinline__ void map_block(const Params& p, int& part, int& rg) {
 //   * Two barriers per page: the page's slices landed (and every wave is past
 //     the previous page: its stage and the P buffer are free), and the P
 //     fragments are written.
+//   * An FP8 cache: each lane reads its own token's records in the K operand
+//     layout and dequantizes them in registers next to the QK^T MFMAs; the
+//     latent part also goes to the bf16 stage for PV, which reads it after
+//     the P barrier (so the first barrier only frees the stage).
 constexpr int kSmallPBytes = 2 * 64 * 16;   // two 32-token P^T fragments
 constexpr int kSmallPvLead = 6;             // V^T fragments in flight
 
