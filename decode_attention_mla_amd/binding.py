@@ -40,6 +40,10 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                            "or python -m decode_attention_mla_amd.build")
+    # PyTorch's ROCm build ships its own HIP runtime: load it first, so that the
+    # library binds to the runtime the tensors live in (a library loaded first
+    # binds to another copy, whose device queries then fail once torch loads).
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     i32p = ctypes.POINTER(ctypes.c_int32)
     ip = ctypes.POINTER(ctypes.c_int)
