@@ -169,3 +169,29 @@ def test_sparse_argument_errors_return_codes_without_launching():
     assert rc == -1 and b"is_fp8" in L.mla_last_error()
     with pytest.raises(mla.MlaError, match="topk"):
         mla.get_mla_metadata_sparse_host(None, 2, 1, 16, 0, num_cus=8)
+
+
+def test_entry_points_raise_without_the_library():
+    """No CPU fallback: with the library missing, every entry point raises
+    (checked in a fresh interpreter, so the loaded library does not leak)."""
+    import subprocess
+    import sys
+    code = (
+        "import numpy as np\n"
+        "from decode_attention_mla_amd import binding\n"
+        "binding.LIB_PATH = '/nonexistent/libmla_decode.so'\n"
+        "calls = [lambda: binding.get_mla_metadata_host(np.array([100], np.int32), 16, 1),\n"
+        "         lambda: binding.mla_plan(np.array([100], np.int32), 4),\n"
+        "         lambda: binding.mla_workspace_bytes(4, 16, 1),\n"
+        "         lambda: binding.get_mla_metadata_sparse_host(None, 1, 1, 16, 64)]\n"
+        "for c in calls:\n"
+        "    try:\n"
+        "        c()\n"
+        "    except RuntimeError as e:\n"
+        "        assert 'missing' in str(e), e\n"
+        "    else:\n"
+        "        raise SystemExit('an entry point ran without the library')\n"
+        "print('raised')\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0 and "raised" in res.stdout, res.stdout + res.stderr
