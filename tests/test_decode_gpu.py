@@ -59,6 +59,28 @@ def test_mtp_config_sampled_requests():
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
 
 
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_longest_request_sampled(h_q):
+    """One request of 2^19 tokens (8192 pages, 604 MB of KV) beside a short
+    one: the plan cuts it into about 256 pieces, whose partials the combine
+    merges 64 to a wave; sampled heads match the oracle."""
+    import decode_attention_mla_amd as mla
+    L = 1 << 19
+    inp = W.make_inputs(2, 1, h_q, [L, 100], pool=None, max_blocks=L // 64, seed=77)
+    sched, ns = mla.get_mla_metadata(inp.cache_seqlens, h_q, 1)
+    pieces = int(ns[1].item() - ns[0].item())
+    print(f"[longest] h_q={h_q} L={L} pieces={pieces}", flush=True)
+    assert pieces >= 128
+    out, lse = run_gpu(inp)
+    picks = [(0, 0, h) for h in sorted({0, h_q // 2, h_q - 1})] + [(1, 0, 0)]
+    ref_o, ref_l = oracle.mla_decode_rows(inp.q, inp.kv_cache, inp.block_table, inp.cache_seqlens,
+                                          inp.softmax_scale, picks)
+    got_o = np.array([out[i, s, h] for i, s, h in picks])
+    got_l = np.array([lse[i, h, s] for i, s, h in picks])
+    assert_parity(got_o, got_l, ref_o, ref_l, f"longest request h_q={h_q}")
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+
 EDGE_LENS = [0, 1, 2, 63, 64, 65, 127, 128, 129, 200, 1000]
 
 
