@@ -81,6 +81,21 @@ def test_longest_request_sampled(h_q):
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
 
 
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_large_batch_of_short_requests(h_q):
+    """2048 requests of 0..300 tokens: parts span many requests (most pieces
+    are whole requests, written straight to the output), some zero-length."""
+    rng = np.random.default_rng(91)
+    lens = rng.integers(0, 301, size=2048).astype(np.int32)
+    lens[::97] = 0
+    inp = W.make_inputs(len(lens), 1, h_q, lens, pool=None, max_blocks=6, seed=91)
+    print(f"[large batch] h_q={h_q} batch={len(lens)}", flush=True)
+    ref_out, ref_lse = _ref(inp)
+    out, lse = run_gpu(inp)
+    assert_parity(out, lse, ref_out, ref_lse, f"large batch h_q={h_q}", out_tol=out_tol_bound(inp))
+    assert np.all(out[lens == 0] == 0) and np.all(np.isneginf(lse[lens == 0]))
+
+
 EDGE_LENS = [0, 1, 2, 63, 64, 65, 127, 128, 129, 200, 1000]
 
 
