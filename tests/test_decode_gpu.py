@@ -96,6 +96,47 @@ def test_large_batch_of_short_requests(h_q):
     assert np.all(out[lens == 0] == 0) and np.all(np.isneginf(lse[lens == 0]))
 
 
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_pages_beyond_4_gib_of_pool(h_q):
+    """Pages at byte offsets past 2^32 of the KV pool (a 60000-page, 4.4 GB
+    pool whose used pages sit at its end), through the block table and
+    through sparse index lists: the 64-bit address arithmetic of both copy
+    paths.  The oracle sees the same pages in a compact pool."""
+    import torch
+    import decode_attention_mla_amd as mla
+    dev = torch.device("cuda", 0)
+    inp = W.make_inputs(3, 1, h_q, [700, 64, 1], pool=16, max_blocks=11, seed=23)
+    n_pool, compact = 60000, inp.kv_cache.shape[0]
+    high = n_pool - compact + np.arange(compact, dtype=np.int64)      # compact page i -> pool page high[i]
+    assert high[0] * 64 * 1152 > 2 ** 32
+    big = torch.zeros((n_pool, 64, 1, W.D_QK), dtype=torch.bfloat16, device=dev)
+    big[torch.from_numpy(high).to(dev)] = torch.from_numpy(inp.kv_cache.view(np.int16)).view(torch.bfloat16).to(dev)
+    bt_high = high[inp.block_table].astype(np.int32)
+    q = torch.from_numpy(inp.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    sl = torch.from_numpy(inp.cache_seqlens).to(dev)
+    ref_out, ref_lse = _ref(inp)
+    print(f"[4 GiB] dense h_q={h_q}", flush=True)
+    sched, ns = mla.get_mla_metadata(inp.cache_seqlens, h_q, 1)
+    out, lse = mla.mla_decode_fwd(q, big, torch.from_numpy(bt_high).to(dev), sl, inp.softmax_scale, sched, ns)
+    torch.cuda.synchronize()
+    assert_parity(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_out,
+                  ref_lse, f"pool past 4 GiB, dense h_q={h_q}", out_tol=out_tol_bound(inp))
+    # the same keys as sparse lists: entry = pool page * 64 + slot
+    topk = 704
+    idx = np.full((3, 1, topk), -1, dtype=np.int32)
+    for i, L in enumerate(inp.cache_seqlens):
+        t = np.arange(int(L))
+        idx[i, 0, :L] = bt_high[i, t // 64] * 64 + t % 64
+    print(f"[4 GiB] sparse h_q={h_q}", flush=True)
+    ss, sn = mla.get_mla_metadata_sparse(None, 3, 1, h_q, topk)
+    out2, lse2 = mla.mla_decode_sparse_fwd(q, big, torch.from_numpy(idx).to(dev), inp.softmax_scale, ss, sn)
+    torch.cuda.synchronize()
+    assert_parity(out2.float().cpu().numpy().astype(np.float64), lse2.cpu().numpy().astype(np.float64), ref_out,
+                  ref_lse, f"pool past 4 GiB, sparse h_q={h_q}", out_tol=out_tol_bound(inp))
+    del big
+    torch.cuda.empty_cache()
+
+
 EDGE_LENS = [0, 1, 2, 63, 64, 65, 127, 128, 129, 200, 1000]
 
 

@@ -238,3 +238,41 @@ def test_fp8_graph_replay_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+
+
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_fp8_records_beyond_4_gib_of_pool(h_q):
+    """FP8 records at byte offsets past 2^32 (a 110000-page, 4.6 GB pool whose
+    used pages sit at its end), through the block table and through sparse
+    index lists; the oracle sees the same records in a compact pool."""
+    import torch
+    inp = W.make_inputs(3, 1, h_q, [700, 64, 1], pool=16, max_blocks=11, seed=29)
+    rec = W.to_fp8_records(inp.kv_cache)
+    n_pool, compact = 110000, rec.shape[0]
+    high = n_pool - compact + np.arange(compact, dtype=np.int64)
+    assert high[0] * 64 * W.FP8_RECORD > 2 ** 32
+    dev = torch.device("cuda", 0)
+    big = torch.zeros((n_pool, 64, 1, W.FP8_RECORD), dtype=torch.uint8, device=dev)
+    big[torch.from_numpy(high).to(dev)] = torch.from_numpy(rec).to(dev)
+    bt_high = high[inp.block_table].astype(np.int32)
+    ref_out, ref_lse = ref_dense_fp8(inp, rec)
+    print(f"[fp8 4 GiB] dense h_q={h_q}", flush=True)
+    sched, ns = mla.get_mla_metadata(inp.cache_seqlens, h_q, 1)
+    out, lse = mla.mla_decode_fwd(_bf16(inp.q), big, _dev(bt_high), _dev(inp.cache_seqlens), inp.softmax_scale,
+                                  sched, ns, fp8=True)
+    torch.cuda.synchronize()
+    assert_parity(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_out,
+                  ref_lse, f"fp8 pool past 4 GiB, dense h_q={h_q}", out_tol=out_tol_bound(inp))
+    topk = 704
+    idx = np.full((3, 1, topk), -1, dtype=np.int32)
+    for i, L in enumerate(inp.cache_seqlens):
+        t = np.arange(int(L))
+        idx[i, 0, :L] = bt_high[i, t // 64] * 64 + t % 64
+    print(f"[fp8 4 GiB] sparse h_q={h_q}", flush=True)
+    ss, sn = mla.get_mla_metadata_sparse(None, 3, 1, h_q, topk)
+    out2, lse2 = mla.mla_decode_sparse_fwd(_bf16(inp.q), big, _dev(idx), inp.softmax_scale, ss, sn, fp8=True)
+    torch.cuda.synchronize()
+    assert_parity(out2.float().cpu().numpy().astype(np.float64), lse2.cpu().numpy().astype(np.float64), ref_out,
+                  ref_lse, f"fp8 pool past 4 GiB, sparse h_q={h_q}", out_tol=out_tol_bound(inp))
+    del big
+    torch.cuda.empty_cache()
