@@ -14,10 +14,10 @@
 //     has four waves, one per SIMD.  Wave w owns tokens 16 w .. 16 w + 15 of
 //     every page: it copies just those 16 token rows (18 KiB) into its own
 //     pair of LDS stages with global_load_lds_dwordx4 (16 B per lane straight
-//     into LDS, nontemporal: each page is streamed once per workgroup, and on
-//     MI355X the hinted copies sustain about twice the bandwidth of plain
-//     ones), so every LDS byte is read by one wave only and the page loop
-//     has no workgroup barrier.  Each wave keeps its own softmax state; the
+//     into LDS; the nontemporal hint is a per-kernel choice, measured: the
+//     128-row kernel is faster with it, the small-row kernel without), so
+//     every LDS byte is read by one wave only and the page loop has no
+//     workgroup barrier.  Each wave keeps its own softmax state; the
 //     four states are merged through LDS when a piece ends.
 //   * In LDS a stage holds 16 token rows as nine 64-dim column blocks; block
 //     b has one 128-byte row per token whose eight 16-byte chunks are
@@ -715,9 +715,9 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
 #pragma unroll
       for (int i = 0; i < kFp8Copies; ++i) {
         if constexpr (kSparse)
-          issue_fp8_gather<true>(p, entry_row, tok0, dst, i, lane);
+          issue_fp8_gather<false>(p, entry_row, tok0, dst, i, lane);
         else
-          issue_fp8_copy<true>(rows, dst, i, lane);
+          issue_fp8_copy<false>(rows, dst, i, lane);
       }
     };
 
@@ -755,9 +755,9 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
         if (lo < hi) issue_fp8_page(m.blk[0], g0.row, 0);
         if (kF8Stages == 2 && lo + 1 < hi) issue_fp8_page(m.blk[1], 0, 1);
       } else if constexpr (kSparse) {
-        if (lo < hi) issue_gather<true>(p, g0, dma_off, wslice);
+        if (lo < hi) issue_gather<false>(p, g0, dma_off, wslice);
       } else {
-        if (lo < hi) issue_stage<true>(page_rows(m.blk[0]), wslice, dma_off);
+        if (lo < hi) issue_stage<false>(page_rows(m.blk[0]), wslice, dma_off);
       }
       if (attempt == 0) {
         // this wave's pieces of Q (the first pages may still be in flight)
@@ -782,9 +782,9 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
       }
       if (lo + 1 < hi && !kFp8) {
         if constexpr (kSparse)
-          issue_gather<true>(p, g1, dma_off, wslice + kPageBytes);
+          issue_gather<false>(p, g1, dma_off, wslice + kPageBytes);
         else
-          issue_stage<true>(page_rows(m.blk[1]), wslice + kPageBytes, dma_off);
+          issue_stage<false>(page_rows(m.blk[1]), wslice + kPageBytes, dma_off);
       }
       int next_blk = kF8Stages == 1 ? m.blk[1] : m.blk[2];   // block ids are read one page ahead of their copy
 
@@ -867,11 +867,11 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
           if (j > lo && j + 1 < hi) {
             if constexpr (kSparse) {
               const GatherPage gn = gather_page(p, ent_next, j + 1, L, tok0, lane);
-              issue_gather<true>(p, gn, dma_off, wslice + ((j + 1 - lo) & 1) * kPageBytes);
+              issue_gather<false>(p, gn, dma_off, wslice + ((j + 1 - lo) & 1) * kPageBytes);
               mk_pending = gn.mask;
               ent_next = load_page_entries(p, req, j + 2, lane);
             } else {
-              issue_stage<true>(page_rows(next_blk), wslice + ((j + 1 - lo) & 1) * kPageBytes, dma_off);
+              issue_stage<false>(page_rows(next_blk), wslice + ((j + 1 - lo) & 1) * kPageBytes, dma_off);
               next_blk = ld_uniform(bt + min(j + 2, p.max_blocks - 1));
             }
           }
