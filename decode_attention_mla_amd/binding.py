@@ -51,15 +51,16 @@ def lib() -> ctypes.CDLL:
     L.mla_plan.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, i32p,
                            ctypes.c_int, i32p, ip]
     L.mla_plan.restype = ctypes.c_int
-    L.mla_get_metadata.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+    L.mla_get_metadata.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, i32p, ctypes.c_int, i32p, ip, ip]
     L.mla_get_metadata.restype = ctypes.c_int
-    L.mla_max_parts.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.mla_max_parts.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_int]
     L.mla_max_parts.restype = ctypes.c_int
     L.mla_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     L.mla_workspace_bytes.restype = ctypes.c_size_t
-    L.mla_get_metadata_device.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
-                                          ctypes.c_int, vp, ip, vp]
+    L.mla_get_metadata_device.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          vp, ctypes.c_int, vp, ip, vp]
     L.mla_get_metadata_device.restype = ctypes.c_int
     L.mla_decode_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, vp, vp,
@@ -117,39 +118,43 @@ def mla_plan(cache_seqlens, num_parts: int, fixed_overhead: int = 0, force_split
     return sched[:nparts.value].copy(), ns
 
 
-def get_mla_metadata_host(cache_seqlens, h_q: int, s_q: int, num_cus: int = 0, force_splits: int = 0):
-    """mla_get_metadata on host arrays: (sched [P, 8], num_splits [b + 1], total_splits)."""
+def get_mla_metadata_host(cache_seqlens, h_q: int, s_q: int, num_cus: int = 0, force_splits: int = 0,
+                          fp8: bool = False):
+    """mla_get_metadata on host arrays: (sched [P, 8], num_splits [b + 1], total_splits).
+    ``fp8``: the plan serves decode calls on an FP8 cache."""
     sl = _i32_host(cache_seqlens)
     b = int(sl.shape[0])
     L = lib()
-    cap = L.mla_max_parts(_ptr(sl), b, int(h_q), int(s_q), int(num_cus), int(force_splits))
+    f8 = 1 if fp8 else 0
+    cap = L.mla_max_parts(_ptr(sl), b, int(h_q), int(s_q), f8, int(num_cus), int(force_splits))
     _check(cap if cap < 0 else 0, "mla_max_parts")
     sched = np.zeros((max(cap, 1), SCHED_INTS), dtype=np.int32)
     ns = np.zeros(b + 1, dtype=np.int32)
     nparts = ctypes.c_int(0)
     total = ctypes.c_int(0)
-    _check(L.mla_get_metadata(_ptr(sl), b, int(h_q), int(s_q), int(num_cus), int(force_splits), _ptr(sched),
+    _check(L.mla_get_metadata(_ptr(sl), b, int(h_q), int(s_q), f8, int(num_cus), int(force_splits), _ptr(sched),
                               sched.shape[0], _ptr(ns), ctypes.byref(nparts), ctypes.byref(total)),
            "mla_get_metadata")
     return sched[:nparts.value].copy(), ns, int(total.value)
 
 
 def get_mla_metadata(cache_seqlens, h_q: int, s_q: int, num_cus: int = 0, force_splits: int = 0,
-                     device=None):
+                     device=None, fp8: bool = False):
     """Plan one decode step; returns (sched, num_splits) as int32 device tensors.
 
-    The plan is reusable for every call with the same batch, s_q, h_q and
-    cache_seqlens (e.g. every layer of one decode step).  ``cache_seqlens``
-    may be a host array or a tensor; the planner reads it on the host.
+    The plan is reusable for every call with the same batch, s_q, h_q, cache
+    format (``fp8``) and cache_seqlens (e.g. every layer of one decode step).
+    ``cache_seqlens`` may be a host array or a tensor; the planner reads it on
+    the host.
     """
     import torch
-    sched, ns, _ = get_mla_metadata_host(cache_seqlens, h_q, s_q, num_cus, force_splits)
+    sched, ns, _ = get_mla_metadata_host(cache_seqlens, h_q, s_q, num_cus, force_splits, fp8)
     dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
     return (torch.from_numpy(sched).to(dev, non_blocking=False),
             torch.from_numpy(ns).to(dev, non_blocking=False))
 
 
-def get_mla_metadata_device(cache_seqlens, h_q: int, s_q: int, num_cus: int = 0):
+def get_mla_metadata_device(cache_seqlens, h_q: int, s_q: int, num_cus: int = 0, fp8: bool = False):
     """The split plan computed on the GPU from device lengths (int32 [b]),
     enqueued on the current stream: returns (sched int32 [P, 8],
     num_splits int32 [b + 1]) device tensors, P = the policy's part count
@@ -159,14 +164,15 @@ def get_mla_metadata_device(cache_seqlens, h_q: int, s_q: int, num_cus: int = 0)
           and cache_seqlens.is_contiguous(), "cache_seqlens must be a contiguous int32 [b] GPU tensor")
     b = int(cache_seqlens.shape[0])
     dummy = np.zeros(b, dtype=np.int32)   # the part count depends on sizes only
-    cap = lib().mla_max_parts(_ptr(dummy), b, int(h_q), int(s_q), int(num_cus), 0)
+    f8 = 1 if fp8 else 0
+    cap = lib().mla_max_parts(_ptr(dummy), b, int(h_q), int(s_q), f8, int(num_cus), 0)
     _check(cap if cap < 0 else 0, "mla_max_parts")
     dev = cache_seqlens.device
     sched = torch.empty((cap, SCHED_INTS), dtype=torch.int32, device=dev)
     ns = torch.empty(b + 1, dtype=torch.int32, device=dev)
     parts = ctypes.c_int(0)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    _check(lib().mla_get_metadata_device(cache_seqlens.data_ptr(), b, int(h_q), int(s_q), int(num_cus),
+    _check(lib().mla_get_metadata_device(cache_seqlens.data_ptr(), b, int(h_q), int(s_q), f8, int(num_cus),
                                          sched.data_ptr(), cap, ns.data_ptr(), ctypes.byref(parts), stream),
            "mla_get_metadata_device")
     return sched[:parts.value], ns

@@ -700,7 +700,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
       for (int i = 0; i < 3; ++i) ent[i] = load_page_entries(p, req, lo + i, lane);
     }
     const int L = m.L;
-    const int nblk = (L + kPage - 1) / kPage;
+    const int nblk = pages_of(L);
     const int hi = (req == pr.end_req) ? pr.end_blk : nblk;
     const int slot = m.slot0 + ((req == pr.begin_req) ? pr.begin_piece : 0);
     const bool split = m.slot1 - m.slot0 > 1;
@@ -1088,7 +1088,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_kernel(Params p) {
     const int lo = (req == pr.begin_req) ? pr.begin_blk : 0;
     const RequestMeta m = load_request(p, req, lo);
     const int L = m.L;
-    const int nblk = (L + kPage - 1) / kPage;
+    const int nblk = pages_of(L);
     const int hi = (req == pr.end_req) ? pr.end_blk : nblk;
     const int slot = m.slot0 + ((req == pr.begin_req) ? pr.begin_piece : 0);
     const bool split = m.slot1 - m.slot0 > 1;
@@ -1374,7 +1374,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
     const int lo = (req == pr.begin_req) ? pr.begin_blk : 0;
     const RequestMeta m = kSparse ? load_request_sparse(p, req) : load_request(p, req, lo);
     const int L = m.L;
-    const int nblk = (L + kPage - 1) / kPage;
+    const int nblk = pages_of(L);
     const int hi = (req == pr.end_req) ? pr.end_blk : nblk;
     const int slot = m.slot0 + ((req == pr.begin_req) ? pr.begin_piece : 0);
     const bool split = m.slot1 - m.slot0 > 1;
@@ -1550,8 +1550,10 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
           } else if (k == 2) {
             // The other half of the row's tokens sits in lane l ^ 32
             // (softmax_scale >= 0: the max commutes with the scaling).
+            // A tile with no key has max -inf, and -inf * 0 (softmax_scale = 0)
+            // is NaN: the clamp keeps it -inf, so such a tile sets no reference.
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t.mloc), __float_as_uint(t.mloc), false, false);
-            t.mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2;
+            t.mloc = fmaxf(fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2, -INFINITY);
           } else if (k == 3) {
             if (m_ref == -INFINITY) m_ref = t.mloc;   // the first tile in which the row sees a key
             m_seen = fmaxf(m_seen, t.mloc);
@@ -1874,7 +1876,7 @@ __global__ void __launch_bounds__(64) mla_plan_kernel(const int32_t* seqlens, in
                                                     int32_t* sched, int32_t* num_splits) {
   __shared__ int pb_req[kPlanMaxParts], pb_blk[kPlanMaxParts], pb_piece[kPlanMaxParts];
   const int lane = threadIdx.x;
-  auto blocks_of = [](int L) { return L > 0 ? (L + kPage - 1) / kPage : 0; };   // negative lengths count as 0
+  auto blocks_of = [](int L) { return pages_of(L); };   // negative lengths count as 0
   // total = sum (n_b + F); payload = ceil(total / parts) + F
   long long part_sum = 0;
   for (int b = lane; b < batch; b += 64) part_sum += blocks_of(seqlens[b]) + F;
@@ -2005,33 +2007,34 @@ static int policy_for(const Geometry& g, bool wide, int* num_cus, int* parts, in
   return MLA_OK;
 }
 
-static int policy(const int32_t* seqlens, int batch, int h_q, int s_q, int* num_cus, int* parts, int* F) {
-  if (batch <= 0 || h_q <= 0 || s_q <= 0 || !seqlens)
-    return set_error(MLA_ERR_INVALID, "mla_get_metadata: batch=%d h_q=%d s_q=%d seqlens=%p", batch, h_q, s_q,
-                     (const void*)seqlens);
-  const Geometry g = geometry(h_q, s_q);
-  return policy_for(g, g.R >= kWideRows, num_cus, parts, F);
+static int policy(const int32_t* seqlens, int batch, int h_q, int s_q, int is_fp8, int* num_cus, int* parts,
+                  int* F) {
+  if (batch <= 0 || h_q <= 0 || s_q <= 0 || !seqlens || (is_fp8 != 0 && is_fp8 != 1))
+    return set_error(MLA_ERR_INVALID, "mla_get_metadata: batch=%d h_q=%d s_q=%d is_fp8=%d seqlens=%p", batch, h_q,
+                     s_q, is_fp8, (const void*)seqlens);
+  const Geometry g = geometry(h_q, s_q, is_fp8 != 0);
+  return policy_for(g, g.R >= kWideRows || (is_fp8 && g.R > kSmallRows), num_cus, parts, F);
 }
 
-extern "C" int mla_max_parts(const int32_t* cache_seqlens, int batch, int h_q, int s_q, int num_cus,
+extern "C" int mla_max_parts(const int32_t* cache_seqlens, int batch, int h_q, int s_q, int is_fp8, int num_cus,
                              int force_splits) {
   int parts, F;
-  int rc = policy(cache_seqlens, batch, h_q, s_q, &num_cus, &parts, &F);
+  int rc = policy(cache_seqlens, batch, h_q, s_q, is_fp8, &num_cus, &parts, &F);
   if (rc) return rc;
   if (force_splits <= 0) return parts;
   long long total = 0;
   for (int b = 0; b < batch; ++b) {
-    const int n = (cache_seqlens[b] + kPage - 1) / kPage;
+    const int n = pages_of(cache_seqlens[b]);
     total += n < 1 ? 1 : (n < force_splits ? n : force_splits);
   }
   return (int)total;
 }
 
-extern "C" int mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q, int s_q, int num_cus,
+extern "C" int mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q, int s_q, int is_fp8, int num_cus,
                                 int force_splits, int32_t* sched_out, int max_parts,
                                 int32_t* num_splits_out, int* num_parts_out, int* total_splits_out) {
   int parts, F;
-  int rc = policy(cache_seqlens, batch, h_q, s_q, &num_cus, &parts, &F);
+  int rc = policy(cache_seqlens, batch, h_q, s_q, is_fp8, &num_cus, &parts, &F);
   if (rc) return rc;
   if (!total_splits_out) return set_error(MLA_ERR_INVALID, "mla_get_metadata: null total_splits_out");
   rc = plan(cache_seqlens, batch, parts, F, force_splits, sched_out, max_parts, num_splits_out, num_parts_out);
@@ -2040,15 +2043,15 @@ extern "C" int mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q
   return MLA_OK;
 }
 
-extern "C" int mla_get_metadata_device(const int32_t* cache_seqlens_dev, int batch, int h_q, int s_q, int num_cus,
-                                       int32_t* sched_dev, int max_parts, int32_t* num_splits_dev,
+extern "C" int mla_get_metadata_device(const int32_t* cache_seqlens_dev, int batch, int h_q, int s_q, int is_fp8,
+                                       int num_cus, int32_t* sched_dev, int max_parts, int32_t* num_splits_dev,
                                        int* num_parts_out, void* stream) {
   if (!sched_dev || !num_splits_dev || !num_parts_out)
     return set_error(MLA_ERR_INVALID, "mla_get_metadata_device: null pointer argument");
   if (batch > kPlanMaxBatch)
     return set_error(MLA_ERR_INVALID, "mla_get_metadata_device: batch=%d > %d", batch, kPlanMaxBatch);
   int parts, F;
-  int rc = policy(cache_seqlens_dev, batch, h_q, s_q, &num_cus, &parts, &F);
+  int rc = policy(cache_seqlens_dev, batch, h_q, s_q, is_fp8, &num_cus, &parts, &F);
   if (rc) return rc;
   if (max_parts < parts)
     return set_error(MLA_ERR_CAPACITY, "mla_get_metadata_device: max_parts=%d < %d parts", max_parts, parts);
@@ -2183,7 +2186,6 @@ static int launch_decode(Params& prm, Geometry g, bool sparse, bool fp8, hipStre
   hipEvent_t* ev = profile_slot();
   void* args[] = {&prm};
   const void* main_fn;
-  if (g.R > kSmallRows && g.R < kWideRows && (sparse || fp8)) g.row_groups = 1;   // 128-row kernel
   prm.row_groups = g.row_groups;
   // The XCD-aware block mapping (map_block) needs 8 * row_groups * ceil(parts / 8) workgroups.
   const int grid = 8 * g.row_groups * ((prm.num_parts + 7) / 8);
@@ -2223,7 +2225,7 @@ extern "C" int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t
     return set_error(MLA_ERR_INVALID, "mla_decode_fwd: softmax_scale must be finite and >= 0");
   if (causal != 0 && causal != 1) return set_error(MLA_ERR_INVALID, "mla_decode_fwd: causal must be 0 or 1");
   if (is_fp8 != 0 && is_fp8 != 1) return set_error(MLA_ERR_INVALID, "mla_decode_fwd: is_fp8 must be 0 or 1");
-  const Geometry g = geometry(h_q, s_q);
+  const Geometry g = geometry(h_q, s_q, is_fp8 != 0);
   const int slots = num_parts + batch - 1;
   const size_t need = mla_workspace_bytes(slots, h_q, s_q);
   if (!workspace || workspace_bytes < need)

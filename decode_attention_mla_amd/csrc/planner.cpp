@@ -14,8 +14,6 @@
 
 namespace mla {
 
-static inline int blocks_of(int32_t L) { return (L + kPage - 1) / kPage; }
-
 int plan(const int32_t* seqlens, int batch, int num_parts, int fixed_overhead, int force_splits,
          int32_t* sched, int max_parts, int32_t* num_splits, int* parts_out) {
   if (!seqlens || !sched || !num_splits || !parts_out)
@@ -26,7 +24,7 @@ int plan(const int32_t* seqlens, int batch, int num_parts, int fixed_overhead, i
   std::vector<int> n(batch);
   for (int b = 0; b < batch; ++b) {
     if (seqlens[b] < 0) return set_error(MLA_ERR_INVALID, "mla_plan: cache_seqlens[%d] = %d < 0", b, seqlens[b]);
-    n[b] = blocks_of(seqlens[b]);
+    n[b] = pages_of(seqlens[b]);
   }
   std::vector<int> pieces(batch, 0);
   int np = 0;

@@ -276,24 +276,6 @@ FP8_RECORD = 656
 FP8_MAX = 448.0
 
 
-def _e4m3_table() -> np.ndarray:
-    """The 256 e4m3fn values (byte -> float64; 0x7f / 0xff are NaN)."""
-    v = np.empty(256, np.float64)
-    for b in range(256):
-        s = -1.0 if b & 0x80 else 1.0
-        e, m = (b >> 3) & 0xF, b & 7
-        if e == 0xF and m == 7:
-            v[b] = np.nan
-        elif e == 0:
-            v[b] = s * m / 8.0 * 2.0 ** -6
-        else:
-            v[b] = s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
-    return v
-
-
-E4M3 = _e4m3_table()
-
-
 def quantize_e4m3(x: np.ndarray, chunk: int = 1 << 20) -> np.ndarray:
     """Round fp32 values to the nearest e4m3fn byte (ties to the even
     mantissa), saturating at +-448, by integer arithmetic on the fp32 bits

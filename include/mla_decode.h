@@ -81,12 +81,17 @@ int mla_plan(const int32_t* cache_seqlens, int batch, int num_parts, int fixed_o
 /*
  * mla_get_metadata — plan one decode step (the pages' get_mla_metadata).
  *
- * Chooses num_parts and the fixed overhead from the CU count and the
- * query-row count R = s_q * h_q, then calls mla_plan.  The plan stays valid
- * for every call (e.g. every layer of one decode step) with the same batch,
- * s_q, h_q and cache_seqlens ("[DeepSeek-3] FlashMLA", section 5).
+ * Chooses num_parts and the fixed overhead from the CU count, the
+ * query-row count R = s_q * h_q and the cache format, then calls mla_plan.
+ * The plan stays valid for every call (e.g. every layer of one decode step)
+ * with the same batch, s_q, h_q, cache format and cache_seqlens
+ * ("[DeepSeek-3] FlashMLA", section 5, whose get_mla_metadata also takes the
+ * FP8 flag: the launch geometry depends on it).
  *
  *   cache_seqlens  host int32 [batch]
+ *   is_fp8         0: bf16 cache, 1: FP8 records (see MLA_FP8_RECORD); must
+ *                  match the is_fp8 of the mla_decode_fwd calls the plan
+ *                  serves (another plan is still correct, only slower)
  *   num_cus        CUs to fill; 0 = query the current HIP device
  *   force_splits   0 = greedy planner, k > 0 = k pieces per request (testing)
  *   sched_out      host int32 [max_parts * 8]; max_parts >= mla_max_parts(...)
@@ -94,7 +99,7 @@ int mla_plan(const int32_t* cache_seqlens, int batch, int num_parts, int fixed_o
  *   num_parts_out, total_splits_out  parts written, partial slots needed
  * Errors: MLA_ERR_INVALID, MLA_ERR_CAPACITY, MLA_ERR_HIP (device query).
  */
-int mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q, int s_q, int num_cus,
+int mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q, int s_q, int is_fp8, int num_cus,
                      int force_splits, int32_t* sched_out, int max_parts,
                      int32_t* num_splits_out, int* num_parts_out, int* total_splits_out);
 
@@ -108,6 +113,7 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q, int s_q, 
  *
  *   cache_seqlens_dev device int32 [batch] (read when the kernel runs;
  *                     negative lengths count as 0)
+ *   is_fp8            the cache format, as for mla_get_metadata
  *   num_cus           CUs to fill; 0 = query the current HIP device
  *   sched_dev         device int32 [max_parts * 8]; max_parts >= the policy's
  *                     part count (mla_max_parts(..., force_splits = 0))
@@ -123,12 +129,12 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q, int s_q, 
  * Errors: MLA_ERR_INVALID (also for the limits above), MLA_ERR_CAPACITY,
  *         MLA_ERR_HIP.
  */
-int mla_get_metadata_device(const int32_t* cache_seqlens_dev, int batch, int h_q, int s_q, int num_cus,
-                            int32_t* sched_dev, int max_parts, int32_t* num_splits_dev,
+int mla_get_metadata_device(const int32_t* cache_seqlens_dev, int batch, int h_q, int s_q, int is_fp8,
+                            int num_cus, int32_t* sched_dev, int max_parts, int32_t* num_splits_dev,
                             int* num_parts_out, void* stream);
 
 /* Upper bound on the parts mla_get_metadata can emit for these sizes. */
-int mla_max_parts(const int32_t* cache_seqlens, int batch, int h_q, int s_q, int num_cus,
+int mla_max_parts(const int32_t* cache_seqlens, int batch, int h_q, int s_q, int is_fp8, int num_cus,
                   int force_splits);
 
 /*

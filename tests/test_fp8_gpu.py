@@ -13,7 +13,7 @@ import pytest
 import decode_attention_mla_amd as mla
 from decode_attention_mla_amd import workloads as W
 import oracle
-from gpu_util import assert_parity, out_tol_bound
+from gpu_util import assert_parity, dense_out_bound, sparse_out_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,8 @@ def _bf16(a):
 def run_dense_fp8(inp, rec, force_splits=0, num_cus=0, causal=False):
     import torch
     print(f"[fp8] dense b={inp.batch} s_q={inp.s_q} h_q={inp.h_q} force={force_splits} causal={causal}", flush=True)
-    sched, ns = mla.get_mla_metadata(inp.cache_seqlens, inp.h_q, inp.s_q, num_cus=num_cus, force_splits=force_splits)
+    sched, ns = mla.get_mla_metadata(inp.cache_seqlens, inp.h_q, inp.s_q, num_cus=num_cus, force_splits=force_splits,
+                                      fp8=True)
     out, lse = mla.mla_decode_fwd(_bf16(inp.q), _dev(rec), _dev(inp.block_table), _dev(inp.cache_seqlens),
                                   inp.softmax_scale, sched, ns, causal=causal, fp8=True)
     torch.cuda.synchronize()
@@ -77,7 +78,8 @@ def test_fp8_dense_parity(case):
     rec = W.to_fp8_records(inp.kv_cache)
     ref_out, ref_lse = ref_dense_fp8(inp, rec, causal=causal)
     out, lse = run_dense_fp8(inp, rec, force_splits=force, causal=causal)
-    assert_parity(out, lse, ref_out, ref_lse, f"fp8 dense case {case}", out_tol=out_tol_bound(inp))
+    assert_parity(out, lse, ref_out, ref_lse, f"fp8 dense case {case}",
+                  out_tol=dense_out_bound(inp, causal=causal, kv=oracle.dequantize_fp8_cache(rec)))
 
 
 @pytest.mark.parametrize("h_q", [16, 128])
@@ -97,7 +99,7 @@ def test_fp8_nan_records_past_the_end_do_not_leak(h_q):
         out, lse = run_dense_fp8(inp, rec, force_splits=force)
         assert np.isfinite(out).all() and np.isfinite(lse).all()
         assert_parity(out, lse, ref_out, ref_lse, f"fp8 NaN tails h_q={h_q} force={force}",
-                      out_tol=out_tol_bound(inp))
+                      out_tol=dense_out_bound(inp, kv=oracle.dequantize_fp8_cache(rec)))
 
 
 def test_fp8_memory_bound_workload_full():
@@ -132,15 +134,13 @@ SPARSE_CASES = [
 
 @pytest.mark.parametrize("case", range(len(SPARSE_CASES)))
 def test_fp8_sparse_parity(case):
-    from test_sparse_gpu import sparse_out_tol
     h_q, s_q, topk, ctx, pad, tl, cus = SPARSE_CASES[case]
     inp = W.make_sparse_inputs(len(ctx), s_q, h_q, topk, ctx, seed=70 + case, pad_frac=pad, topk_length=tl)
     rec = W.to_fp8_records(inp.kv_cache)
     kv = oracle.dequantize_fp8_cache(rec)
     ref_out, ref_lse = oracle.mla_decode_sparse(inp.q, kv, inp.indices, inp.softmax_scale, topk_length=inp.topk_length)
     out, lse = run_sparse_fp8(inp, rec, num_cus=cus)
-    deq = W.SparseInputs(inp.name, inp.q, kv, inp.indices, inp.topk_length, inp.softmax_scale)
-    assert_parity(out, lse, ref_out, ref_lse, f"fp8 sparse case {case}", out_tol=sparse_out_tol(deq))
+    assert_parity(out, lse, ref_out, ref_lse, f"fp8 sparse case {case}", out_tol=sparse_out_bound(inp, kv=kv))
 
 
 @pytest.mark.parametrize("h_q", [16, 128])
@@ -168,9 +168,10 @@ def test_fp8_restart_when_later_page_outgrows_first_max(h_q):
     rec = W.to_fp8_records(inp.kv_cache)
     ref_out, ref_lse = ref_dense_fp8(inp, rec)
     assert ref_lse.max() > 100
+    tol = dense_out_bound(inp, kv=oracle.dequantize_fp8_cache(rec))
     for force in (0, 1):
         out, lse = run_dense_fp8(inp, rec, force_splits=force)
-        assert_parity(out, lse, ref_out, ref_lse, f"fp8 restart h_q={h_q} force={force}", out_tol=out_tol_bound(inp))
+        assert_parity(out, lse, ref_out, ref_lse, f"fp8 restart h_q={h_q} force={force}", out_tol=tol)
 
 
 @pytest.mark.parametrize("h_q", [16, 128])
@@ -192,7 +193,7 @@ def test_fp8_sparse_identity_gather_equals_dense_bitwise(h_q):
     bt, sl = _dev(inp.block_table), _dev(inp.cache_seqlens)
     for cus in (0, 256):
         print(f"[fp8] identity gather h_q={h_q} cus={cus}", flush=True)
-        hs, hn = mla.get_mla_metadata(inp.cache_seqlens, h_q, 1, num_cus=cus)
+        hs, hn = mla.get_mla_metadata(inp.cache_seqlens, h_q, 1, num_cus=cus, fp8=True)
         dense_o, dense_l = mla.mla_decode_fwd(q, kv, bt, sl, inp.softmax_scale, hs, hn, fp8=True)
         ss, sn = mla.get_mla_metadata_sparse(inp.cache_seqlens, 4, 1, h_q, topk, num_cus=cus)
         assert torch.equal(ss.cpu(), hs.cpu()) and torch.equal(sn.cpu(), hn.cpu())
@@ -210,7 +211,7 @@ def test_fp8_graph_replay_matches_eager():
     rec = W.to_fp8_records(inp.kv_cache)
     q, kv = _bf16(inp.q), _dev(rec)
     bt, sl = _dev(inp.block_table), _dev(inp.cache_seqlens)
-    sched, ns = mla.get_mla_metadata(inp.cache_seqlens, inp.h_q, inp.s_q)
+    sched, ns = mla.get_mla_metadata(inp.cache_seqlens, inp.h_q, inp.s_q, fp8=True)
     ref_out, ref_lse = mla.mla_decode_fwd(q, kv, bt, sl, inp.softmax_scale, sched, ns, fp8=True)
     torch.cuda.synchronize()
     ref_out, ref_lse = ref_out.clone(), ref_lse.clone()
@@ -256,13 +257,14 @@ def test_fp8_records_beyond_4_gib_of_pool(h_q):
     big[torch.from_numpy(high).to(dev)] = torch.from_numpy(rec).to(dev)
     bt_high = high[inp.block_table].astype(np.int32)
     ref_out, ref_lse = ref_dense_fp8(inp, rec)
+    tol = dense_out_bound(inp, kv=oracle.dequantize_fp8_cache(rec))
     print(f"[fp8 4 GiB] dense h_q={h_q}", flush=True)
-    sched, ns = mla.get_mla_metadata(inp.cache_seqlens, h_q, 1)
+    sched, ns = mla.get_mla_metadata(inp.cache_seqlens, h_q, 1, fp8=True)
     out, lse = mla.mla_decode_fwd(_bf16(inp.q), big, _dev(bt_high), _dev(inp.cache_seqlens), inp.softmax_scale,
                                   sched, ns, fp8=True)
     torch.cuda.synchronize()
     assert_parity(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_out,
-                  ref_lse, f"fp8 pool past 4 GiB, dense h_q={h_q}", out_tol=out_tol_bound(inp))
+                  ref_lse, f"fp8 pool past 4 GiB, dense h_q={h_q}", out_tol=tol)
     topk = 704
     idx = np.full((3, 1, topk), -1, dtype=np.int32)
     for i, L in enumerate(inp.cache_seqlens):
@@ -273,6 +275,6 @@ def test_fp8_records_beyond_4_gib_of_pool(h_q):
     out2, lse2 = mla.mla_decode_sparse_fwd(_bf16(inp.q), big, _dev(idx), inp.softmax_scale, ss, sn, fp8=True)
     torch.cuda.synchronize()
     assert_parity(out2.float().cpu().numpy().astype(np.float64), lse2.cpu().numpy().astype(np.float64), ref_out,
-                  ref_lse, f"fp8 pool past 4 GiB, sparse h_q={h_q}", out_tol=out_tol_bound(inp))
+                  ref_lse, f"fp8 pool past 4 GiB, sparse h_q={h_q}", out_tol=tol)
     del big
     torch.cuda.empty_cache()

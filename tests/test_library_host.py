@@ -56,14 +56,21 @@ def test_planner_bit_exact_with_reference(seed):
     assert np.array_equal(s_ref, s_lib) and np.array_equal(n_ref, n_lib)
 
 
-@pytest.mark.parametrize("h_q,s_q", [(16, 1), (128, 1), (128, 2), (64, 1), (8, 3)])
-def test_get_metadata_policy_matches_reference_plan(h_q, s_q):
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("h_q,s_q", [(16, 1), (128, 1), (128, 2), (64, 1), (8, 3), (24, 2)])
+def test_get_metadata_policy_matches_reference_plan(h_q, s_q, fp8):
+    """The policy's part count and overhead by kernel geometry: an FP8 cache
+    takes the 128-row kernel above 16 rows, so its plan has one part per CU
+    there (every CU gets a workgroup) rather than the 32-row kernel's."""
     sl = np.array([100, 257, 4096, 0, 70000, 1], dtype=np.int32)
-    sched, ns, total = mla.get_mla_metadata_host(sl, h_q, s_q, num_cus=256)
+    sched, ns, total = mla.get_mla_metadata_host(sl, h_q, s_q, num_cus=256, fp8=fp8)
     R = h_q * s_q
-    groups = 1 if R <= 16 else -(-R // 128) if R >= 128 else -(-R // 32)
+    wide = R >= 128 or (fp8 and R > 16)
+    groups = 1 if R <= 16 else -(-R // 128) if wide else -(-R // 32)
     parts = max(1, 256 // groups)
-    F = 3 if R <= 16 else 4 if R >= 128 else 2
+    if fp8 and 16 < R < 128:
+        assert parts == 256
+    F = 3 if R <= 16 else 4 if wide else 2
     s_ref, n_ref = oracle.plan(sl, num_parts=parts, fixed_overhead=F)
     assert np.array_equal(sched, s_ref) and np.array_equal(ns, n_ref) and total == n_ref[-1]
     assert total <= sched.shape[0] + len(sl) - 1
@@ -119,13 +126,13 @@ def test_device_planner_argument_errors_return_codes_without_launching():
     L = mla.lib()
     dummy = ctypes.c_void_p(16)   # never dereferenced: every check fails before any launch
     n = ctypes.c_int(0)
-    rc = L.mla_get_metadata_device(dummy, 4, 16, 1, 256, None, 256, dummy, ctypes.byref(n), None)
+    rc = L.mla_get_metadata_device(dummy, 4, 16, 1, 0, 256, None, 256, dummy, ctypes.byref(n), None)
     assert rc == -1 and b"null" in L.mla_last_error()
-    rc = L.mla_get_metadata_device(dummy, 70000, 16, 1, 256, dummy, 256, dummy, ctypes.byref(n), None)
+    rc = L.mla_get_metadata_device(dummy, 70000, 16, 1, 0, 256, dummy, 256, dummy, ctypes.byref(n), None)
     assert rc == -1 and b"batch" in L.mla_last_error()
-    rc = L.mla_get_metadata_device(dummy, 4, 16, 1, 256, dummy, 255, dummy, ctypes.byref(n), None)
+    rc = L.mla_get_metadata_device(dummy, 4, 16, 1, 0, 256, dummy, 255, dummy, ctypes.byref(n), None)
     assert rc == -2 and b"max_parts" in L.mla_last_error()
-    rc = L.mla_get_metadata_device(dummy, 4, 16, 1, 5000, dummy, 5000, dummy, ctypes.byref(n), None)
+    rc = L.mla_get_metadata_device(dummy, 4, 16, 1, 0, 5000, dummy, 5000, dummy, ctypes.byref(n), None)
     assert rc == -1 and b"4096" in L.mla_last_error()
 
 
@@ -195,3 +202,70 @@ def test_entry_points_raise_without_the_library():
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     res = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=120)
     assert res.returncode == 0 and "raised" in res.stdout, res.stdout + res.stderr
+
+
+def test_lengths_at_the_int32_limit():
+    """Lengths up to 2^31 - 1: ceil(L / 64) computed without the int32
+    overflow of (L + 63) / 64, by the planner, the part bound and the policy."""
+    sl = np.array([2 ** 31 - 1, 100, 2 ** 31 - 64, 2 ** 31 - 65, 0], dtype=np.int32)
+    assert [(int(L) + 63) // 64 for L in sl] == [2 ** 25, 2, 2 ** 25 - 1, 2 ** 25 - 1, 0]
+    for P, F in ((256, 3), (7, 0), (1, 4)):
+        s_ref, n_ref = oracle.plan(sl, num_parts=P, fixed_overhead=F)
+        s_lib, n_lib = mla.mla_plan(sl, num_parts=P, fixed_overhead=F)
+        assert np.array_equal(s_ref, s_lib) and np.array_equal(n_ref, n_lib)
+    s_ref, n_ref = oracle.plan(sl, num_parts=4, force_splits=3)
+    s_lib, n_lib = mla.mla_plan(sl, num_parts=4, force_splits=3)
+    assert np.array_equal(s_ref, s_lib) and np.array_equal(n_ref, n_lib)
+    sl_ptr = sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert mla.lib().mla_max_parts(sl_ptr, len(sl), 16, 1, 0, 256, 3) == 3 + 2 + 3 + 3 + 1
+    sched, ns, total = mla.get_mla_metadata_host(sl, 128, 1, num_cus=256)
+    s_ref, n_ref = oracle.plan(sl, num_parts=256, fixed_overhead=4)
+    assert np.array_equal(sched, s_ref) and np.array_equal(ns, n_ref)
+
+
+UBSAN_HARNESS = r'''
+#include <cstdint>
+#include <cstdio>
+#include <vector>
+#include "mla_internal.h"
+namespace mla {
+int set_error(int code, const char*, ...) { return code; }
+}
+int main() {
+  const int32_t lens[] = {2147483647, 100, 2147483584, 2147483583, 0, 1, 63, 64, 65};
+  const int b = sizeof lens / sizeof lens[0];
+  std::vector<int32_t> sched(4096 * 8), ns(b + 1);
+  int parts = 0;
+  for (int P : {1, 7, 256, 4096})
+    for (int F : {0, 3, 8})
+      if (mla::plan(lens, b, P, F, 0, sched.data(), 4096, ns.data(), &parts) != 0) return 2;
+  for (int k : {1, 3, 64})
+    if (mla::plan(lens, b, 1, 0, k, sched.data(), 4096, ns.data(), &parts) != 0) return 3;
+  for (int L : {2147483647, 2147483584, 2147483583, 1, 0, -5})
+    std::printf("%d ", mla::pages_of(L));
+  std::printf("ok\n");
+  return 0;
+}
+'''
+
+
+def test_host_planner_under_undefined_behaviour_sanitizer(tmp_path):
+    """The host planner (plain C++) built with g++ -fsanitize=undefined and run
+    on lengths up to 2^31 - 1: no signed overflow or other undefined behaviour
+    (the build traps on the first report)."""
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    csrc = os.path.join(ROOT, "decode_attention_mla_amd", "csrc")
+    src = tmp_path / "harness.cpp"
+    src.write_text(UBSAN_HARNESS)
+    exe = tmp_path / "harness"
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=undefined", "-fno-sanitize-recover=all",
+           "-I", csrc, "-I", os.path.join(ROOT, "include"), str(src), os.path.join(csrc, "planner.cpp"), "-o", str(exe)]
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0 and "runtime error" not in run.stderr, run.stdout + run.stderr
+    assert run.stdout.split()[:6] == ["33554432", "33554431", "33554431", "1", "0", "0"], run.stdout
