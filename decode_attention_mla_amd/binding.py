@@ -22,7 +22,7 @@ FP8_RECORD = 656   # bytes per token of an FP8 cache (512 e4m3 + 4 fp32 scales +
 
 # Every symbol include/mla_decode.h declares.
 EXPORTED = ("mla_plan", "mla_get_metadata", "mla_get_metadata_device", "mla_max_parts", "mla_workspace_bytes",
-            "mla_decode_fwd", "mla_max_parts_sparse", "mla_get_metadata_sparse", "mla_decode_sparse_fwd",
+            "mla_decode_fwd", "mla_decode_fwd_noalloc", "mla_max_parts_sparse", "mla_get_metadata_sparse", "mla_decode_sparse_fwd",
             "mla_profile_start", "mla_profile_stop", "mla_last_error")
 
 _lib = None
@@ -66,6 +66,10 @@ def lib() -> ctypes.CDLL:
                                  ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, vp, vp,
                                  ctypes.c_size_t, vp, vp, vp]
     L.mla_decode_fwd.restype = ctypes.c_int
+    L.mla_decode_fwd_noalloc.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, vp,
+                                         vp, vp, vp]
+    L.mla_decode_fwd_noalloc.restype = ctypes.c_int
     L.mla_max_parts_sparse.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
     L.mla_max_parts_sparse.restype = ctypes.c_int
     L.mla_get_metadata_sparse.argtypes = [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -202,18 +206,9 @@ def _kv_check(kv_cache, fp8: bool):
               f"kv_cache must be bf16 [num_blocks, 64, 1, 576], got {kv_cache.dtype} {tuple(kv_cache.shape)}")
 
 
-def mla_decode_fwd(q, kv_cache, block_table, cache_seqlens, softmax_scale: float, sched, num_splits,
-                   out=None, lse=None, workspace=None, causal: bool = False, fp8: bool = False):
-    """Dense MLA decode.  Returns (out bf16 [b, s_q, h_q, 512], lse fp32 [b, h_q, s_q]).
-
-    q bf16 [b, s_q, h_q, 576]; kv_cache bf16 [num_blocks, 64, 1, 576], or with
-    fp8=True the FP8 records uint8 [num_blocks, 64, 1, 656];
-    block_table int32 [b, max_blocks]; cache_seqlens int32 [b];
-    sched / num_splits from get_mla_metadata for the same cache_seqlens.
-    causal: query token s of s_q sees keys 0 .. L - s_q + s (multi-token
-    prediction) instead of all L.
-    All tensors on the same GPU, contiguous.  Enqueued on the current stream.
-    """
+def _dense_checks(q, kv_cache, block_table, cache_seqlens, sched, num_splits, out, lse, fp8):
+    """Validates a dense decode call; returns (b, s_q, h_q, out, lse), allocating
+    out / lse when they are None."""
     import torch
     _need(q.dim() == 4 and q.shape[3] == D_QK, f"q must be [b, s_q, h_q, 576], got {tuple(q.shape)}")
     b, s_q, h_q = (int(x) for x in q.shape[:3])
@@ -228,7 +223,6 @@ def mla_decode_fwd(q, kv_cache, block_table, cache_seqlens, softmax_scale: float
         _need(t.dtype == dt, f"{name} must be {dt}, got {t.dtype}")
         _need(t.is_cuda and t.device == q.device, f"{name} must be on {q.device}")
         _need(t.is_contiguous(), f"{name} must be contiguous")
-    num_parts = int(sched.shape[0])
     if out is None:
         out = torch.empty((b, s_q, h_q, D_V), dtype=torch.bfloat16, device=q.device)
     if lse is None:
@@ -237,6 +231,25 @@ def mla_decode_fwd(q, kv_cache, block_table, cache_seqlens, softmax_scale: float
           "out must be contiguous bf16 [b, s_q, h_q, 512]")
     _need(lse.dtype == torch.float32 and tuple(lse.shape) == (b, h_q, s_q) and lse.is_contiguous(),
           "lse must be contiguous fp32 [b, h_q, s_q]")
+    _need(out.device == q.device and lse.device == q.device, f"out and lse must be on {q.device}")
+    return b, s_q, h_q, out, lse
+
+
+def mla_decode_fwd(q, kv_cache, block_table, cache_seqlens, softmax_scale: float, sched, num_splits,
+                   out=None, lse=None, workspace=None, causal: bool = False, fp8: bool = False):
+    """Dense MLA decode.  Returns (out bf16 [b, s_q, h_q, 512], lse fp32 [b, h_q, s_q]).
+
+    q bf16 [b, s_q, h_q, 576]; kv_cache bf16 [num_blocks, 64, 1, 576], or with
+    fp8=True the FP8 records uint8 [num_blocks, 64, 1, 656];
+    block_table int32 [b, max_blocks]; cache_seqlens int32 [b];
+    sched / num_splits from get_mla_metadata for the same cache_seqlens.
+    causal: query token s of s_q sees keys 0 .. L - s_q + s (multi-token
+    prediction) instead of all L.
+    All tensors on the same GPU, contiguous.  Enqueued on the current stream.
+    """
+    import torch
+    b, s_q, h_q, out, lse = _dense_checks(q, kv_cache, block_table, cache_seqlens, sched, num_splits, out, lse, fp8)
+    num_parts = int(sched.shape[0])
     ws_bytes = mla_workspace_bytes(num_parts + b - 1, h_q, s_q)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
@@ -249,6 +262,26 @@ def mla_decode_fwd(q, kv_cache, block_table, cache_seqlens, softmax_scale: float
                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                               out.data_ptr(), lse.data_ptr(), stream)
     _check(rc, "mla_decode_fwd")
+    return out, lse
+
+
+def mla_decode_fwd_noalloc(q, kv_cache, block_table, cache_seqlens, softmax_scale: float, sched, num_splits, out, lse,
+                           causal: bool = False, fp8: bool = False):
+    """mla_decode_fwd without a workspace argument: the library's own
+    per-GPU split array serves (``mla_decode_fwd_noalloc``; plans needing more
+    than MLA_NOALLOC_SCRATCH_BYTES are rejected).  ``out`` and ``lse`` are
+    caller buffers (nothing is allocated here either).  Calls that overlap
+    on one GPU race on that array."""
+    import torch
+    _need(out is not None and lse is not None, "mla_decode_fwd_noalloc writes into caller buffers: pass out and lse")
+    b, s_q, h_q, out, lse = _dense_checks(q, kv_cache, block_table, cache_seqlens, sched, num_splits, out, lse, fp8)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib().mla_decode_fwd_noalloc(q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(),
+                                      cache_seqlens.data_ptr(), b, s_q, h_q, int(kv_cache.shape[0]),
+                                      int(block_table.shape[1]), float(softmax_scale), 1 if causal else 0,
+                                      1 if fp8 else 0, sched.data_ptr(), int(sched.shape[0]), num_splits.data_ptr(),
+                                      out.data_ptr(), lse.data_ptr(), stream)
+    _check(rc, "mla_decode_fwd_noalloc")
     return out, lse
 
 

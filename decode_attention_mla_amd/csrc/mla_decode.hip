@@ -42,6 +42,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -2259,6 +2260,68 @@ extern "C" int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t
   prm.fold = 1;
 
   return launch_decode(prm, g, false, is_fp8 != 0, (hipStream_t)stream, "mla_decode_fwd");
+}
+
+// ---------------------------------------------------------------------------
+// Split workspace owned by the library, for callers that cannot allocate
+// (mla_decode_fwd_noalloc).  One copy per GPU, placed when the code object is
+// loaded on that GPU and held until the process ends.  In host code `scratch`
+// names a host-side stand-in, never the device memory: its device address is
+// looked up once per device (hipGetSymbolAddress, with that device current)
+// and only that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = (size_t)MLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace mla {
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_dev[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this device's `scratch` (looked up on first use).
+int scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(MLA_ERR_HIP, "mla_decode_fwd_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return set_error(MLA_ERR_INVALID, "mla_decode_fwd_noalloc: device %d >= %d", dev, kMaxDevices);
+  void* ptr = g_scratch_dev[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    ptr = g_scratch_dev[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !ptr)
+        return set_error(MLA_ERR_HIP, "mla_decode_fwd_noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                         hipGetErrorString(e));
+      g_scratch_dev[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return MLA_OK;
+}
+}  // namespace
+}  // namespace mla
+
+extern "C" int mla_decode_fwd_noalloc(const void* q, const void* kv_cache, const int32_t* block_table,
+                                      const int32_t* cache_seqlens, int batch, int s_q, int h_q, int num_blocks,
+                                      int max_blocks_per_seq, float softmax_scale, int causal, int is_fp8,
+                                      const int32_t* sched, int num_parts, const int32_t* num_splits, void* out,
+                                      float* lse, void* stream) {
+  // Size check first (host arithmetic only; invalid sizes give 0 here and are
+  // reported by mla_decode_fwd's own checks).
+  const size_t need = (batch > 0 && num_parts > 0) ? mla_workspace_bytes(num_parts + batch - 1, h_q, s_q) : 0;
+  if (need > kNoAllocScratchBytes)
+    return set_error(MLA_ERR_WORKSPACE,
+                     "mla_decode_fwd_noalloc: this plan needs %zu bytes of split workspace > the library's %zu "
+                     "(use mla_decode_fwd with a caller workspace)",
+                     need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  const int rc = scratch_for_current_device(&ws);
+  if (rc) return rc;
+  return mla_decode_fwd(q, kv_cache, block_table, cache_seqlens, batch, s_q, h_q, num_blocks, max_blocks_per_seq,
+                        softmax_scale, causal, is_fp8, sched, num_parts, num_splits, ws, kNoAllocScratchBytes, out,
+                        lse, stream);
 }
 
 extern "C" int mla_decode_sparse_fwd(const void* q, const void* kv_cache, const int32_t* indices,

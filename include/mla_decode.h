@@ -192,6 +192,35 @@ int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* block_tab
                    size_t workspace_bytes, void* out, float* lse, void* stream);
 
 /*
+ * mla_decode_fwd_noalloc — mla_decode_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments, computation and
+ * results, without the workspace.  The split partials live in a
+ * library-owned device array of MLA_NOALLOC_SCRATCH_BYTES per GPU, placed
+ * when the library's code object is loaded on that GPU and held until the
+ * process ends.  The caller still passes (and owns) inputs and outputs.
+ *
+ *   Sizes: a plan fits iff mla_workspace_bytes(num_parts + batch - 1, h_q,
+ *   s_q) <= MLA_NOALLOC_SCRATCH_BYTES (e.g. batch 16 x 16 heads on 256
+ *   parts: 8.9 MB; batch 64 x 128 heads: 84 MB; batch 128 x 2 x 128 rows:
+ *   134 MB, too large); larger plans return MLA_ERR_WORKSPACE and launch
+ *   nothing.
+ *   Allocates nothing: no hipMalloc / hipFree or allocating library call.
+ *   The first call on a device (with that device current; the stream must
+ *   belong to it) looks up the array's device address once.
+ *   Sharing: every call on one GPU uses that GPU's one array, so calls that
+ *   overlap on a GPU (several streams or threads) race on it; serialise
+ *   them.  Nothing in the array needs to start at any value (every partial
+ *   slot a call reads was written earlier in the same call).
+ * Errors: as mla_decode_fwd, and MLA_ERR_WORKSPACE for plans that do not fit.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int mla_decode_fwd_noalloc(const void* q, const void* kv_cache, const int32_t* block_table,
+                           const int32_t* cache_seqlens, int batch, int s_q, int h_q, int num_blocks,
+                           int max_blocks_per_seq, float softmax_scale, int causal, int is_fp8, const int32_t* sched,
+                           int num_parts, const int32_t* num_splits, void* out, float* lse, void* stream);
+
+/*
  * FP8 cache ("[DeepSeek-3] FlashMLA", section 12), accepted by both decode
  * entry points when is_fp8 = 1: each token is a 656-byte record
  *   bytes   0 .. 511  latent dims 0 .. 511 as float8 e4m3 (OCP e4m3fn)
