@@ -1,4 +1,6 @@
-"""Build the gfx950 shared library ``libmla_decode.so`` in-tree with hipcc.
+"""Build the gfx950 shared libraries in-tree with hipcc: ``libmla_decode.so``
+(the decode path) and ``libmla_bench.so`` (the benchmark's measurement
+kernels).
 
 Run as ``python -m decode_attention_mla_amd.build`` (or via
 ``__graft_entry__.build()``).  hipcc cross-compiles for gfx950 without a GPU.
@@ -15,6 +17,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libmla_decode.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = ["mla_decode.hip", "planner.cpp"]
+BENCH_LIB_PATH = os.path.join(PKG_DIR, "libmla_bench.so")
+BENCH_SOURCES = ["mla_bench.hip"]
 
 # Packed-FP32 VALU forms are kept out of the generated code (see the build
 # notes); hipcc's host pass warns that it does not know the feature.
@@ -30,12 +34,10 @@ def hipcc_path() -> str:
     raise RuntimeError("hipcc not found: the gfx950 library cannot be built")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every source into LIB_PATH (always recompiles)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
+def _compile(srcs, out, verbose, extra_flags) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc_path(), *HIP_FLAGS, *(extra_flags or []), "-I", os.path.join(PKG_DIR, "..", "include"),
-           *srcs, "-o", tmp]
+           *[os.path.join(CSRC, s) for s in srcs], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,7 +47,13 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
     if verbose and msgs:
         print(msgs, flush=True)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compile both libraries (always recompiles); returns the decode library's path."""
+    _compile(SOURCES, LIB_PATH, verbose, extra_flags)
+    _compile(BENCH_SOURCES, BENCH_LIB_PATH, verbose, extra_flags)
     return LIB_PATH
 
 

@@ -16,22 +16,39 @@ from decode_attention_mla_amd import binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def declared_functions():
-    names = []
-    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
-        text = open(h).read()
-        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(mla_[a-z_]+)\s*\(", text, flags=re.M)
+def declared_functions(header):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(mla_[a-z_]+)\s*\(", text, flags=re.M)
     return sorted(set(names))
+
+
+def test_every_header_is_checked():
+    assert sorted(os.path.basename(h) for h in glob.glob(os.path.join(ROOT, "include", "*.h"))) == \
+        ["mla_bench.h", "mla_decode.h"]
 
 
 def test_library_loads_and_exports_every_declared_symbol():
     L = mla.lib()
-    decl = declared_functions()
+    decl = declared_functions("mla_decode.h")
     assert set(decl) == set(binding.EXPORTED), decl
     for name in decl:
         assert hasattr(L, name), f"{name} not exported"
         ctypes.cast(getattr(L, name), ctypes.c_void_p)
+
+
+def test_bench_library_loads_and_exports_every_declared_symbol():
+    from decode_attention_mla_amd import build
+    B = ctypes.CDLL(build.BENCH_LIB_PATH)
+    decl = declared_functions("mla_bench.h")
+    assert set(decl) == {"mla_bench_stream_read", "mla_bench_empty", "mla_bench_last_error"}, decl
+    for name in decl:
+        assert hasattr(B, name), f"{name} not exported"
+    B.mla_bench_last_error.restype = ctypes.c_char_p
+    B.mla_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_void_p]
+    assert B.mla_bench_stream_read(None, 1024, None, 4, None) == -1      # rejected before any launch
+    assert b"bad argument" in B.mla_bench_last_error()
 
 
 @pytest.mark.parametrize("seed", range(30))
