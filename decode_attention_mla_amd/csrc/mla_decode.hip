@@ -124,6 +124,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// This lane's index, recomputed where it is used (two instructions) rather
+// than kept live across a loop whose registers are all taken.
+__device__ __forceinline__ int fresh_lane_id() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -1273,25 +1281,53 @@ constexpr int kWideTiles = kWideRows / 32;                 // 32-row tiles per g
 constexpr int kPFragBytes = kWideTiles * 4 * 64 * 16;      // P^T: 4 row tiles x 4 token steps x 64 lanes x 16 B
 constexpr int kQkSteps16 = kDqk / 16;                      // 36 k-steps of the 32x32x16 MFMA
 constexpr int kWideQkLead = 4;                             // K fragment reads in flight
-constexpr float kRestartFlag = -0.0f;                      // sign bit carried by a P element
-constexpr int kWideSoftmaxPieces = 14;                     // pieces of one tile's softmax
+constexpr int kWideSoftmaxPieces = 22;                     // pieces of one tile's softmax
 
 // Softmax state of one 32-token S^T tile.  Lane l holds row l % 32 and, in
 // element 4 i + e, token 8 i + 4 (l / 32) + e of the tile.  The pieces (each
-// rides between MFMAs; no piece depends on a result of the same piece):
+// rides in the shadow of one MFMA; no piece depends on a result of the same
+// piece):
 //   0, 1   max of this lane's 16 scores (partial maxima, then their max)
 //   2      row max over both lane halves, scaled
 //   3      the first tile sets the reference; running max, restart test
-//   4 .. 13   element pairs through a three-stage pipeline: exponent
-//          argument, exp2, row sum + bf16 pack; each completed 8-token half
-//          goes to LDS as a PV B fragment
+//   4 .. 21   the 16 elements through a three-stage pipeline: exponent
+//          argument of element k - 4, exp2 of element k - 5, row sum (and
+//          bf16 pack of each completed pair) of element k - 6; each completed
+//          8-token half goes to LDS as a PV B fragment.
+// A 32x32x16 MFMA leaves about 16 clk of the wave's issue time in its
+// shadow (measured: three VALU operations and one v_exp_f32 between two
+// MFMAs keep the matrix core's rate; a whole element pair's stages, seven
+// VALU operations and two v_exp_f32, stall it), so a piece is at most one
+// element's stages.  Every stage's inputs and results pass through empty
+// volatile asm statements so that the compiler keeps each piece in its gap
+// (left to itself it merged stages across the copy branches, which put up
+// to 17 VALU operations and 4 exp2 between two MFMAs and none elsewhere).
+// Piece k of a window of n MFMAs rides after MFMA wide_piece_step(k, n).
+constexpr int wide_piece_step(int k, int nsteps) { return 1 + k * (nsteps - 2) / (kWideSoftmaxPieces - 1); }
+// Inverse as a table (piece riding after MFMA step i, or -1), indexed by the
+// unrolled step so that it folds to a constant.
+struct WidePieceMap {
+  signed char at[kDqk / 16];
+};
+constexpr WidePieceMap wide_piece_map(int nsteps) {
+  WidePieceMap m{};
+  for (int i = 0; i < kDqk / 16; ++i) m.at[i] = -1;
+  for (int k = 0; k < kWideSoftmaxPieces; ++k) m.at[wide_piece_step(k, nsteps)] = (signed char)k;
+  return m;
+}
+constexpr WidePieceMap kWidePiecesQk = wide_piece_map(kDqk / 16);   // tile 0 along QK^T of tile 1 (36 MFMAs)
+constexpr WidePieceMap kWidePiecesPv = wide_piece_map(32);          // tile 1 along PV of tokens 0 .. 31 (32 MFMAs)
+static_assert(wide_piece_step(kWideSoftmaxPieces - 1, kDqk / 16) == kDqk / 16 - 1, "pieces fit the QK^T window");
+static_assert(wide_piece_step(kWideSoftmaxPieces - 1, 32) == 31, "pieces fit the PV window");
 struct WideSoftmax {
   float mp[6], mloc;
   float ex[16];
   u32x4 pk[2];
 };
 
-// O^T += V^T P^T on the matrix cores with the accumulator pinned to AGPRs:
+// O^T += V^T P^T on the matrix cores with the accumulator pinned to AGPRs
+// (volatile, like the QK^T MFMAs: their order against the softmax pieces'
+// pins is the program's):
 // O (256 registers per lane) stays in the accumulation registers for the
 // whole piece, which leaves the architectural VGPRs to Q, the S^T tiles and
 // the softmax.  The compiler does not see inside the statement, so the code
@@ -1299,15 +1335,15 @@ struct WideSoftmax {
 // (waited for by the compiler's counters) and reads of the accumulator are
 // preceded by wide_acc_settle().
 __device__ __forceinline__ void pv_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 // S^T tiles in architectural VGPRs (so they never compete with O for the
 // accumulation registers); the first step of a tile starts from zero.
 __device__ __forceinline__ void qk_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b, bool first) {
   if (first)
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
   else
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 // Wait states between the last matrix op writing the accumulators and any
 // other access to them (a 16-pass MFMA result needs 18).
@@ -1436,7 +1472,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
       float m_seen = -INFINITY;
       l_run = 0.f;
       float l_part[4] = {0.f, 0.f, 0.f, 0.f};
-      bool restart = false;
+      bool bad = false;          // a row max outgrew this lane's reference
       int next_blk = m.blk[1];   // copied only if lo + 1 < hi
       unsigned long long mk_cur = g0.mask;   // sparse: key mask of page j
 
@@ -1459,7 +1495,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
           if (keep != 0xFFFFu) zero_stage_rows(buf + wave * kStageBytes, keep, lane);
         } else {
           const int valid = min(kPage, L - j * kPage);
-          if (valid < kPage) zero_stage_tail(buf + wave * kStageBytes, valid - tok0, lane);
+          if (__builtin_expect(valid < kPage, 0)) zero_stage_tail(buf + wave * kStageBytes, valid - tok0, fresh_lane_id());
         }
         lds_barrier();
         // The next page's 18 slices go to the other stage during QK^T (none
@@ -1493,7 +1529,6 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
         // The softmax of each tile rides along the next MFMA stream (tile 0
         // with QK^T of tile 1, tile 1 with PV of tokens 0 .. 31), so its VALU
         // work and exp2 latency hide under the matrix cores.
-        bool bad = false, flag = false;
         WideSoftmax sm[2];
         // Element v of a tile is a key this lane's row sees iff its offset is
         // below lim; a tile is ragged (masking needed) for this workgroup if
@@ -1520,15 +1555,26 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
           auto branch_lim = [&]() {
             int l2;
             if constexpr (kSparse)
-              // this lane's 16 tokens of the tile: bits 8 (v / 4) + v % 4
-              asm volatile("v_mov_b32 %0, %1 ; ragged tile" : "=v"(l2) : "v"((unsigned)(mk_cur >> (32 * tt + 4 * h))));
+              // this lane's 16 tokens of the tile: bits 8 (v / 4) + v % 4 (the
+              // tile's 32-bit word is uniform; only the lane half's shift is not)
+              asm volatile("v_mov_b32 %0, %1 ; ragged tile" : "=v"(l2) : "v"((unsigned)(mk_cur >> (32 * tt)) >> (4 * (fresh_lane_id() >> 5))));
             else
               asm volatile("v_mov_b32 %0, %1 ; ragged tile" : "=v"(l2) : "v"(lim));
             return l2;
           };
+          // Pins (empty volatile asm): a value passed through one is computed
+          // before it and read after it, which holds each stage in its gap.
+          auto pinf = [](float& x) { asm volatile("" : "+v"(x)); };
+          auto pins = [&](int v) {
+            float x = sacc[v];
+            asm volatile("" : "+v"(x));
+            sacc[v] = x;
+          };
           if (k == 0) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) pins(v);
             // Partial maxima (five independent max3s).
-            if (ragged) {
+            if (__builtin_expect(ragged, 0)) {
               // A real branch (the statement cannot be speculated): full
               // tiles must not pay for the masking selects.  Masked scores
               // become -inf in place; the exponent arguments below are
@@ -1546,8 +1592,11 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
               for (int i = 0; i < 5; ++i) t.mp[i] = fmaxf(fmaxf(sacc[3 * i], sacc[3 * i + 1]), sacc[3 * i + 2]);
               t.mp[5] = sacc[15];
             }
+#pragma unroll
+            for (int i = 0; i < 6; ++i) pinf(t.mp[i]);
           } else if (k == 1) {
             t.mloc = fmaxf(fmaxf(fmaxf(t.mp[0], t.mp[1]), t.mp[2]), fmaxf(fmaxf(t.mp[3], t.mp[4]), t.mp[5]));
+            pinf(t.mloc);
           } else if (k == 2) {
             // The other half of the row's tokens sits in lane l ^ 32
             // (softmax_scale >= 0: the max commutes with the scaling).
@@ -1555,35 +1604,40 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
             // is NaN: the clamp keeps it -inf, so such a tile sets no reference.
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t.mloc), __float_as_uint(t.mloc), false, false);
             t.mloc = fmaxf(fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2, -INFINITY);
+            pinf(t.mloc);
           } else if (k == 3) {
             if (m_ref == -INFINITY) m_ref = t.mloc;   // the first tile in which the row sees a key
             m_seen = fmaxf(m_seen, t.mloc);
             bad |= t.mloc > m_ref + kRefHeadroom;
-            if (tt == 1) flag = attempt == 0 && __any(bad);   // wave-wide vote, outside any branch
+            pinf(m_ref);
+            pinf(m_seen);
           } else {
-            // Three-stage pipeline over the 8 element pairs, so that no step
-            // waits on a result of the same step: exponent arguments of pair
-            // k - 4, exp2 of pair k - 5, row sum and bf16 pack of pair k - 6.
-            const int pa = k - 4, pe = k - 5, pc = k - 6;
-            if (pc >= 0 && pc < 8) {
-              const float p0 = t.ex[2 * pc], p1 = t.ex[2 * pc + 1];
-              l_part[pc & 3] += p0 + p1;   // four independent partial row sums
-              asm volatile("" : "+v"(l_part[pc & 3]));   // keeps the add here (not sunk to the loop end)
-              t.pk[pc >> 2][pc & 3] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)p0, (__bf16)p1});
+            // Three-stage pipeline over the 16 elements, so that no stage
+            // waits on a result of the same piece: exponent argument of
+            // element k - 4, exp2 of element k - 5, row sum (and bf16 pack of
+            // a completed pair) of element k - 6.
+            const int ea = k - 4, ee = k - 5, es = k - 6;
+            if (es >= 0 && es < 16) {
+              l_part[es & 3] += t.ex[es];   // four independent partial row sums
+              asm volatile("" : "+v"(l_part[es & 3]));
+              if (es & 1) {
+                unsigned w = __builtin_bit_cast(unsigned, bf16x2{(__bf16)t.ex[es - 1], (__bf16)t.ex[es]});
+                asm volatile("" : "+v"(w));
+                t.pk[es >> 3][(es >> 1) & 3] = w;
+              }
+              if (es == 7 || es == 15) {   // an 8-token half is complete: to LDS as a PV B fragment
+                const int half = es >> 3;
+                *(LDS_PTR(u32x4))(pb + ((wave * 4 + 2 * tt + half) * 64 + lane) * 16) = t.pk[half];
+              }
             }
-            if (pe >= 0 && pe < 8) {
-              t.ex[2 * pe] = __builtin_amdgcn_exp2f(t.ex[2 * pe]);
-              t.ex[2 * pe + 1] = __builtin_amdgcn_exp2f(t.ex[2 * pe + 1]);
+            if (ee >= 0 && ee < 16) {
+              t.ex[ee] = __builtin_amdgcn_exp2f(t.ex[ee]);
+              pinf(t.ex[ee]);
             }
-            if (pa >= 0 && pa < 8) {
-              t.ex[2 * pa] = fmaxf(__builtin_fmaf(sacc[2 * pa], p.scale_log2, -m_ref), -INFINITY);
-              t.ex[2 * pa + 1] = fmaxf(__builtin_fmaf(sacc[2 * pa + 1], p.scale_log2, -m_ref), -INFINITY);
-            }
-            if (pc == 3 || pc == 7) {   // an 8-token half is complete: to LDS as a PV B fragment
-              const int half = pc >> 2;
-              u32x4 w = t.pk[half];
-              if (tt == 1 && half == 1 && lane == 0 && flag) w[0] |= 0x8000u;   // kRestartFlag in element 0
-              *(LDS_PTR(u32x4))(pb + ((wave * 4 + 2 * tt + half) * 64 + lane) * 16) = w;
+            if (ea >= 0 && ea < 16) {
+              pins(ea);
+              t.ex[ea] = fmaxf(__builtin_fmaf(sacc[ea], p.scale_log2, -m_ref), -INFINITY);
+              pinf(t.ex[ea]);
             }
           }
         };
@@ -1605,9 +1659,9 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
             if (ks + kWideQkLead < kQkSteps16) kf[ks % kWideQkLead] = kread(ks + kWideQkLead);
             if constexpr (!kSparse && !kFp8)
               if (ks % 4 == 0 && has_next) issue_stage_slice<kStream>(nrows, nlds, dma_off, 9 * tt + ks / 4);
-            // Tile 0's softmax: one piece every other step from step 1.
+            // Tile 0's softmax, one piece after each of 22 of these MFMAs.
             if (tt == 1 && ks == 1) wide_acc_settle();
-            if (tt == 1 && ks % 2 == 1 && ks / 2 < kWideSoftmaxPieces) softmax_piece(0, ks / 2, sacc[0]);
+            if (tt == 1 && kWidePiecesQk.at[ks] >= 0) softmax_piece(0, kWidePiecesQk.at[ks], sacc[0]);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -1644,33 +1698,35 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
               pv_mfma(o[a][s & 3], vf[s & 1], pf[a]);
               if (s == 3) pread(1, a);
               if (a == kWideTiles - 1 && s + 2 < 8) vf[s & 1] = vread(s + 2);
-              if (with_softmax && (m & 1) && (m >> 1) < kWideSoftmaxPieces) softmax_piece(1, m >> 1, sacc[1]);
+              if (with_softmax && kWidePiecesPv.at[m] >= 0) softmax_piece(1, kWidePiecesPv.at[m], sacc[1]);
               __builtin_amdgcn_sched_barrier(0);
             }
           }
         };
         pv_block(0, true);
-        lds_barrier();   // every wave's tile-1 probabilities (and restart vote) are in LDS
-
-        // A wave whose row max outgrew its reference by more than 2^64 set the
-        // sign of one probability: every wave then redoes the piece with the
-        // largest maxima seen as references (once; exact maxima bound every
-        // probability by 1).  The attempt runs to its end first (its results
-        // are discarded), which keeps a single exit from the page loop.  Only
-        // the first attempt may ask for a restart (whatever the data, even
-        // NaN, the piece is processed at most twice).
-        unsigned short flags[kWideTiles];
-#pragma unroll
-        for (int w = 0; w < kWideTiles; ++w) flags[w] = *(LDS_PTR(unsigned short))(pb + (w * 4 + 3) * 64 * 16);
+        lds_barrier();   // every wave's tile-1 probabilities are in LDS
         pv_block(2, false);
-#pragma unroll
-        for (int w = 0; w < kWideTiles; ++w) restart |= attempt == 0 && (flags[w] >> 15) != 0;
         if constexpr (kSparse) mk_cur = mk_next;
       }
       wait_vmcnt<0>();   // no copy is outstanding (kept for the restart path's refill)
       wide_acc_settle();
       l_run = (l_part[0] + l_part[1]) + (l_part[2] + l_part[3]);
-      if (!restart) break;
+      // If a row max outgrew its reference by more than 2^64 in any wave,
+      // every wave redoes the piece with the largest maxima seen as references
+      // (once; exact maxima bound every probability by 1).  The attempt has
+      // run to its end (its results are discarded), which keeps a single exit
+      // from the page loop; the vote is taken once per piece, through LDS.
+      // Only the first attempt may ask for a restart (whatever the data, even
+      // NaN, the piece is processed at most twice).
+      if (attempt != 0) break;
+      {
+        const bool wave_bad = __any(bad);
+        lds_barrier();   // every wave is done with the P buffer
+        if (lane == 0) *(LDS_PTR(int))(pb + 4 * wave) = wave_bad ? 1 : 0;
+        lds_barrier();
+        const int votes = *(LDS_PTR(int))(pb) | *(LDS_PTR(int))(pb + 4) | *(LDS_PTR(int))(pb + 8) | *(LDS_PTR(int))(pb + 12);
+        if (votes == 0) break;   // (uniform; the epilogue's first barrier orders these reads before its writes)
+      }
       lds_barrier();     // every wave is past the last page before the stages are refilled
       m_ref = m_seen;
     }
