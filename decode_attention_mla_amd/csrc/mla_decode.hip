@@ -116,6 +116,31 @@ __device__ __forceinline__ int row_keys(const Params& p, int L, int row) {
   return p.causal ? L - (p.s_q - 1 - row / p.h_q) : L;
 }
 
+// The arguments a workgroup needs before its first copy come first in
+// every split-KV kernel's signature, as plain scalars, so that the
+// dispatcher preloads them into SGPRs (built with kernel-argument
+// preloading): no round trip to the argument segment precedes the read of
+// the plan row.  The rest of Params is read from the argument segment as
+// usual.  (The combine kernel has its own short list.)
+#define MLA_SPLITKV_HOT_ARGS                                                                                  \
+  const int32_t *hot_sched, int hot_num_parts, int hot_row_groups, int hot_max_blocks,                       \
+      const int32_t *hot_block_table, const int32_t *hot_seqlens, const int32_t *hot_num_splits,              \
+      const unsigned char *hot_kv, const unsigned char *hot_q
+__device__ __forceinline__ Params with_hot_args(Params p, MLA_SPLITKV_HOT_ARGS) {
+  p.sched = hot_sched;
+  p.num_parts = hot_num_parts;
+  p.row_groups = hot_row_groups;
+  p.max_blocks = hot_max_blocks;
+  p.block_table = hot_block_table;
+  p.seqlens = hot_seqlens;
+  p.num_splits = hot_num_splits;
+  p.kv = hot_kv;
+  p.q = hot_q;
+  return p;
+}
+#define MLA_COMBINE_HOT_ARGS \
+  const int32_t *hot_sched, const int32_t *hot_num_splits, int hot_batch, int hot_R, const float *hot_lacc, const float *hot_oacc
+
 constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0), expcnt and lgkmcnt not waited
 
 template <int N>
@@ -502,13 +527,20 @@ __device__ __forceinline__ void store_lse(const Params& p, int req, int row, boo
 }
 
 // Four consecutive output columns c .. c + 3 of one row: bf16 to `out` when
-// the request is not split, else fp32 to the partial slot.
+// the request is not split, else fp32 to the partial slot.  kNt: the partial
+// goes out with the nontemporal hint (measured in a graph of decode steps:
+// 0.25 us faster on the memory-bound workload's small kernel, whose 7 MB of
+// partials otherwise wait in L2 for the end-of-kernel writeback; 18-34 %
+// slower for the 128-row kernel's 67 MB, so that one keeps plain stores).
+template <bool kNt = false>
 __device__ __forceinline__ void store_cols4(const Params& p, int req, int row, bool split, int slot, int c, f32x4 v) {
   if (!split) {
     bf16x4 w4;
 #pragma unroll
     for (int e = 0; e < 4; ++e) w4[e] = (__bf16)v[e];
     *(bf16x4*)(p.out + ((size_t)req * p.R + row) * kDv + c) = w4;
+  } else if constexpr (kNt) {
+    __builtin_nontemporal_store(v, (f32x4*)(p.oacc + ((size_t)slot * p.R + row) * kDv + c));
   } else {
     *(f32x4*)(p.oacc + ((size_t)slot * p.R + row) * kDv + c) = v;
   }
@@ -631,7 +663,9 @@ __device__ __forceinline__ float row_sum4(float v) {
 // lists (whose entries are loaded by the compiler, whose waits would
 // otherwise wait for every copy in flight).
 template <bool kSparse, bool kFp8>
-__global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
+__global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(MLA_SPLITKV_HOT_ARGS, Params p_args) {
+  const Params p = with_hot_args(p_args, hot_sched, hot_num_parts, hot_row_groups, hot_max_blocks, hot_block_table,
+                                 hot_seqlens, hot_num_splits, hot_kv, hot_q);
   constexpr int kF8Stages = kFp8 ? (kSparse ? 1 : 2) : 0;
   // FP8 block-table pages are read one page ahead: page j + 1's records are
   // read into registers (and the next copy issued) while page j's PV runs,
@@ -1026,7 +1060,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(Params p) {
     // In the O^T accumulator lane (g, c16) holds row c16, columns 4 g .. + 3 of the tile.
     if (row_ok) {
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) store_cols4(p, req, c16, split, slot, 128 * wave + 16 * ct + 4 * g, o[ct] * inv);
+      for (int ct = 0; ct < 8; ++ct) store_cols4<true>(p, req, c16, split, slot, 128 * wave + 16 * ct + 4 * g, o[ct] * inv);
     }
     if (wave == 0 && g == 0 && row_ok) store_lse(p, req, c16, split, slot, lse2);
     lds_barrier();   // red is read; the next piece may reuse LDS
@@ -1054,7 +1088,9 @@ constexpr int kQkLead = 6;     // K fragment reads in flight ahead of the QK MFM
 constexpr int kPvLead = 4;     // V^T fragments (two reads each) in flight ahead of the PV MFMAs
 static_assert(kQkSteps == kStageSlices && kDv / 32 == 16, "copy slices: 9 in QK^T, 8 + 1 in PV");
 
-__global__ void __launch_bounds__(256, 1) mla_splitkv_kernel(Params p) {
+__global__ void __launch_bounds__(256, 1) mla_splitkv_kernel(MLA_SPLITKV_HOT_ARGS, Params p_args) {
+  const Params p = with_hot_args(p_args, hot_sched, hot_num_parts, hot_row_groups, hot_max_blocks, hot_block_table,
+                                 hot_seqlens, hot_num_splits, hot_kv, hot_q);
   __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * 2 * kStageBytes];
   __shared__ float st_m[4][kRowGroup], st_l[4][kRowGroup];
 
@@ -1356,7 +1392,9 @@ __device__ __forceinline__ void wide_acc_settle() {
 // page stage (the dequantized page being computed) and one stage of FP8
 // records (the next page, in flight) replace the two bf16 stages.
 template <bool kStream, bool kSparse, bool kFp8>
-__global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(Params p) {
+__global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(MLA_SPLITKV_HOT_ARGS, Params p_args) {
+  const Params p = with_hot_args(p_args, hot_sched, hot_num_parts, hot_row_groups, hot_max_blocks, hot_block_table,
+                                 hot_seqlens, hot_num_splits, hot_kv, hot_q);
   // Two page stages (4 slices of 18 KiB each) and the P^T exchange buffer: 160 KiB
   // (FP8: a bf16 stage and an FP8 stage, 129 KiB).
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kFp8 ? kPageBytes + kFp8Page : 2 * kPageBytes];
@@ -1826,7 +1864,14 @@ __device__ __forceinline__ void combine_store(const Params& p, int req, int row,
   if (lane == 0) p.lse[lse_index(p, req, row)] = l > 0.f ? (M + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
 }
 
-__global__ void __launch_bounds__(kCombineWaves * 64) mla_combine_kernel(Params p) {
+__global__ void __launch_bounds__(kCombineWaves * 64) mla_combine_kernel(MLA_COMBINE_HOT_ARGS, Params p_args) {
+  Params p = p_args;
+  p.sched = hot_sched;
+  p.num_splits = hot_num_splits;
+  p.batch = hot_batch;
+  p.R = hot_R;
+  p.lacc = const_cast<float*>(hot_lacc);
+  p.oacc = const_cast<float*>(hot_oacc);
   __shared__ f32x4 red_o[kCombineWaves][2][64];
   __shared__ float red_m[kCombineWaves], red_l[kCombineWaves];
   const int lane = threadIdx.x & 63;
@@ -2241,9 +2286,13 @@ static const void* pick_main_kernel(const Geometry& g) {
 
 static int launch_decode(Params& prm, Geometry g, bool sparse, bool fp8, hipStream_t st, const char* who) {
   hipEvent_t* ev = profile_slot();
-  void* args[] = {&prm};
   const void* main_fn;
   prm.row_groups = g.row_groups;
+  // (the leading scalar arguments: MLA_SPLITKV_HOT_ARGS, then Params)
+  void* args[] = {&prm.sched,   &prm.num_parts,  &prm.row_groups, &prm.max_blocks, &prm.block_table,
+                  &prm.seqlens, &prm.num_splits, &prm.kv,         &prm.q,          &prm};
+  // (MLA_COMBINE_HOT_ARGS, then Params)
+  void* cargs[] = {&prm.sched, &prm.num_splits, &prm.batch, &prm.R, &prm.lacc, &prm.oacc, &prm};
   // The XCD-aware block mapping (map_block) needs 8 * row_groups * ceil(parts / 8) workgroups.
   const int grid = 8 * g.row_groups * ((prm.num_parts + 7) / 8);
   if (g.R > kSmallRows && g.R < kWideRows && !sparse && !fp8)
@@ -2259,9 +2308,9 @@ static int launch_decode(Params& prm, Geometry g, bool sparse, bool fp8, hipStre
   if (e != hipSuccess) return set_error(MLA_ERR_HIP, "%s: main kernel launch: %s", who, hipGetErrorString(e));
   const long long pairs = (long long)prm.batch * g.R;
   const int cgrid = (int)(pairs < kCombineMaxGrid ? pairs : kCombineMaxGrid);
-  e = ev ? hipExtLaunchKernel((const void*)mla_combine_kernel, dim3(cgrid), dim3(kCombineWaves * 64), args, 0, st,
+  e = ev ? hipExtLaunchKernel((const void*)mla_combine_kernel, dim3(cgrid), dim3(kCombineWaves * 64), cargs, 0, st,
                               ev[2], ev[3], 0)
-         : hipLaunchKernel((const void*)mla_combine_kernel, dim3(cgrid), dim3(kCombineWaves * 64), args, 0, st);
+         : hipLaunchKernel((const void*)mla_combine_kernel, dim3(cgrid), dim3(kCombineWaves * 64), cargs, 0, st);
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) return set_error(MLA_ERR_HIP, "%s: combine launch: %s", who, hipGetErrorString(e));
   return MLA_OK;
