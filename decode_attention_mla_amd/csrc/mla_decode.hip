@@ -1544,18 +1544,15 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(MLA_SPLITKV_HO
             uniform_ptr(p.kv + (size_t)next_blk * kPageBytes + (size_t)tok0 * kRowBytes);
         const unsigned nlds = lds0 + (stage ^ 1) * kPageBytes + wave * kStageBytes;
         unsigned long long mk_next = 0;
+        GatherPage gn{};
         if constexpr (kSparse) {
-          // Sparse pages: the next page's gathered copy is issued here at
-          // once (its per-lane 64-bit addresses do not fit in the register
-          // budget of the QK^T loop below).
-          const GatherPage gn = gather_page(p, ent_next, j + 1, L, tok0, lane);
+          // Sparse pages: the next page's gathered copy; bf16 rows go out
+          // during QK^T of tile 0 like the dense copies (each lane keeps its
+          // two row offsets), FP8 records here at once.
+          gn = gather_page(p, ent_next, j + 1, L, tok0, lane);
           mk_next = gn.mask;
-          if (has_next) {
-            if constexpr (kFp8)
-              issue_fp8_page(0, gn.row);   // into the FP8 stage this wave dequantized from
-            else
-              issue_gather<kStream>(p, gn, dma_off, nlds);
-          }
+          if constexpr (kFp8)
+            if (has_next) issue_fp8_page(0, gn.row);   // into the FP8 stage this wave dequantized from
           ent_next = load_page_entries(p, req, j + 2, lane);   // covered by the next page's wait
         } else {
           if constexpr (kFp8)
@@ -1697,6 +1694,8 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(MLA_SPLITKV_HO
             if (ks + kWideQkLead < kQkSteps16) kf[ks % kWideQkLead] = kread(ks + kWideQkLead);
             if constexpr (!kSparse && !kFp8)
               if (ks % 4 == 0 && has_next) issue_stage_slice<kStream>(nrows, nlds, dma_off, 9 * tt + ks / 4);
+            if constexpr (kSparse && !kFp8)
+              if (tt == 0 && ks % 2 == 0 && has_next) issue_gather_slice<kStream>(p, gn, dma_off, nlds, ks / 2);
             // Tile 0's softmax, one piece after each of 22 of these MFMAs.
             if (tt == 1 && ks == 1) wide_acc_settle();
             if (tt == 1 && kWidePiecesQk.at[ks] >= 0) softmax_piece(0, kWidePiecesQk.at[ks], sacc[0]);
