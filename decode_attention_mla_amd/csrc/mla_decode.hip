@@ -1545,18 +1545,18 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(MLA_SPLITKV_HO
         const unsigned nlds = lds0 + (stage ^ 1) * kPageBytes + wave * kStageBytes;
         unsigned long long mk_next = 0;
         GatherPage gn{};
+        const unsigned char* f8rows = nullptr;   // FP8 block-table pages: the next page's records
+        // The next page's copies go out during QK^T of tile 0 (every two
+        // MFMAs for bf16 rows, every three for the 11 copies of FP8
+        // records, into the FP8 stage this wave dequantized from, whose
+        // reads the barrier above has ordered); dense bf16 pages spread
+        // theirs over both tiles.
         if constexpr (kSparse) {
-          // Sparse pages: the next page's gathered copy; bf16 rows go out
-          // during QK^T of tile 0 like the dense copies (each lane keeps its
-          // two row offsets), FP8 records here at once.
-          gn = gather_page(p, ent_next, j + 1, L, tok0, lane);
+          gn = gather_page(p, ent_next, j + 1, L, tok0, lane);   // each lane keeps its row offsets
           mk_next = gn.mask;
-          if constexpr (kFp8)
-            if (has_next) issue_fp8_page(0, gn.row);   // into the FP8 stage this wave dequantized from
           ent_next = load_page_entries(p, req, j + 2, lane);   // covered by the next page's wait
         } else {
-          if constexpr (kFp8)
-            if (has_next) issue_fp8_page(next_blk, 0);   // into the FP8 stage this wave dequantized from
+          if constexpr (kFp8) f8rows = uniform_ptr(p.kv + (size_t)next_blk * kFp8Page + (size_t)tok0 * kFp8Row);
           next_blk = ld_uniform(bt + (j + 2 < hi ? j + 2 : j));
         }
 
@@ -1696,6 +1696,13 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(MLA_SPLITKV_HO
               if (ks % 4 == 0 && has_next) issue_stage_slice<kStream>(nrows, nlds, dma_off, 9 * tt + ks / 4);
             if constexpr (kSparse && !kFp8)
               if (tt == 0 && ks % 2 == 0 && has_next) issue_gather_slice<kStream>(p, gn, dma_off, nlds, ks / 2);
+            if constexpr (kFp8)
+              if (tt == 0 && ks % 3 == 0 && ks / 3 < kFp8Copies && has_next) {
+                if constexpr (kSparse)
+                  issue_fp8_gather<kStream>(p, gn.row, tok0, fslice, ks / 3, lane);
+                else
+                  issue_fp8_copy<kStream>(f8rows, fslice, ks / 3, lane);
+              }
             // Tile 0's softmax, one piece after each of 22 of these MFMAs.
             if (tt == 1 && ks == 1) wide_acc_settle();
             if (tt == 1 && kWidePiecesQk.at[ks] >= 0) softmax_piece(0, kWidePiecesQk.at[ks], sacc[0]);
