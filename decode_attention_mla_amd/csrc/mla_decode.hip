@@ -10,34 +10,37 @@
 // a normalised partial (O_i, lse_i) that the combine kernel merges.
 //
 // Kernel design (gfx950, not a translation of the pages' Hopper kernel):
-//   * A workgroup covers up to 32 query rows (16 in the small-row kernel) and
-//     has four waves, one per SIMD.  Wave w owns tokens 16 w .. 16 w + 15 of
-//     every page: it copies just those 16 token rows (18 KiB) into its own
-//     pair of LDS stages with global_load_lds_dwordx4 (16 B per lane straight
-//     into LDS; the nontemporal hint is a per-kernel choice, measured: the
-//     128-row kernel is faster with it, the small-row kernel without), so
-//     every LDS byte is read by one wave only and the page loop has no
-//     workgroup barrier.  Each wave keeps its own softmax state; the
-//     four states are merged through LDS when a piece ends.
-//   * In LDS a stage holds 16 token rows as nine 64-dim column blocks; block
-//     b has one 128-byte row per token whose eight 16-byte chunks are
-//     permuted by a function of the token, so that the row reads of QK^T and
-//     the transposing reads of PV both hit distinct banks.
-//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: K fragments come from LDS,
-//     Q^T stays in registers.  In the S^T accumulator a lane holds one query
-//     row, so row max / row sum need two cross-lane exchanges and the
-//     probabilities are already laid out for the PV product; O^T = V^T P^T
-//     takes its V^T fragments from the transposing LDS read ds_read_b64_tr_b16
-//     of the same stage.
+//   * Every split-KV workgroup has four waves, one per SIMD, and wave w
+//     copies tokens 16 w .. 16 w + 15 of every page (18 KiB) into LDS with
+//     global_load_lds_dwordx4 (16 B per lane straight into LDS), issued a
+//     page ahead and spread between the MFMAs.  Three kernels by row count
+//     R = s_q * h_q:
+//       - R <= 16 (memory-bound decode): one workgroup per part; the four
+//         slices form a shared page stage (two stages), a barrier makes a
+//         page visible; QK^T split by tokens (v_mfma_f32_16x16x32_bf16),
+//         probabilities exchanged through LDS, PV split by columns.
+//       - 16 < R < 128 (bf16 cache only): one workgroup per 32 rows; each
+//         wave keeps private stages and its own softmax state over its
+//         tokens, with no barrier in the page loop; the four states are
+//         merged through LDS when a piece ends.
+//       - R >= 128 (and sparse or FP8 above 16 rows): one workgroup per 128
+//         rows; shared stages; QK^T split by rows
+//         (v_mfma_f32_32x32x16_bf16, Q^T in registers), probabilities
+//         exchanged through LDS, PV split by columns with O^T in AGPRs.
+//   * In LDS a 16-token slice holds nine 64-dim column blocks; block b has
+//     one 128-byte row per token whose eight 16-byte chunks are permuted by a
+//     function of the token, so that the row reads of QK^T and the
+//     transposing reads of PV (ds_read_b64_tr_b16) spread over the banks.
 //   * Softmax runs in base 2 with log2(e) folded into the score scale (the
 //     exp2 detail of the FlashMLA new-kernel deep-dive page).  Instead of
 //     moving the running max every page and rescaling O (which would drag the
-//     accumulator through VALU each page), a wave keeps the row max of its
-//     first page as a fixed reference: probabilities are 2^(s - m_ref) and
-//     may exceed 1.  This is the online-softmax algebra with a fixed
-//     reference, exact up to rounding.  If a row's max ever rises more than
-//     64 (log2) above its reference, the wave redoes the piece once with the
-//     exact maximum as the reference, so nothing can overflow.
+//     accumulator through VALU each page), a piece keeps the row max of the
+//     first page in which a row sees a key as a fixed reference:
+//     probabilities are 2^(s - m_ref) and may exceed 1.  This is the
+//     online-softmax algebra with a fixed reference, exact up to rounding.  If
+//     a row's max ever rises more than 64 (log2) above its reference, the
+//     workgroup redoes the piece once with the exact maxima as references, so
+//     nothing can overflow.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
