@@ -46,7 +46,7 @@ METRIC = "MLA decode TFLOPs (h_q=128) and effective HBM GB/s (h_q=16), 1 MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SRCS = [os.path.join(ROOT, "decode_attention_mla_amd", "csrc", f) for f in ("mla_decode.hip", "mla_internal.h")]
+KERNEL_SRCS = [os.path.join(ROOT, "decode_attention_mla_amd", "csrc", f) for f in ("mla_kernels.h", "mla_internal.h")]
 MIN_SPREAD_STEPS = 100
 
 
