@@ -450,22 +450,26 @@ def run_workload(idx: int, steps: int, warmup: int, min_rot_bytes: float = 640e6
     bt = torch.from_numpy(inp.block_table).to(dev)
     sl = torch.from_numpy(inp.cache_seqlens).to(dev)
 
-    # Plan once per decode step (host), timed separately.
+    # Plan once per decode step (host), timed separately; the plan carries
+    # each part's first page (the step's block table is known when it is
+    # planned, and every layer of the step shares both).
     reps = 50
+    nblocks = int(inp.kv_cache.shape[0])
     t = time.perf_counter()
     for _ in range(reps):
-        sched_np, ns_np, total = mla.get_mla_metadata_host(inp.cache_seqlens, inp.h_q, inp.s_q, fp8=fp8)
+        sched_np, ns_np, total = mla.get_mla_metadata_host(inp.cache_seqlens, inp.h_q, inp.s_q, fp8=fp8,
+                                                           block_table=inp.block_table, num_blocks=nblocks)
     plan_us = (time.perf_counter() - t) / reps * 1e6
     sched = torch.from_numpy(sched_np).to(dev)
     ns = torch.from_numpy(ns_np).to(dev)
     # The same plan on the GPU (device lengths; capturable with the decode),
     # timed as graph replays of 20 planner launches (no host launch cost).
-    mla.get_mla_metadata_device(sl, inp.h_q, inp.s_q, fp8=fp8)
+    mla.get_mla_metadata_device(sl, inp.h_q, inp.s_q, fp8=fp8, block_table=bt, num_blocks=nblocks)
     torch.cuda.synchronize()
     plan_graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(plan_graph):
         for _ in range(20):
-            mla.get_mla_metadata_device(sl, inp.h_q, inp.s_q, fp8=fp8)
+            mla.get_mla_metadata_device(sl, inp.h_q, inp.s_q, fp8=fp8, block_table=bt, num_blocks=nblocks)
     plan_graph.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -21,7 +21,8 @@ D_V = 512
 FP8_RECORD = 656   # bytes per token of an FP8 cache (512 e4m3 + 4 fp32 scales + 64 bf16)
 
 # Every symbol include/mla_decode.h declares.
-EXPORTED = ("mla_plan", "mla_get_metadata", "mla_get_metadata_device", "mla_max_parts", "mla_workspace_bytes",
+EXPORTED = ("mla_plan", "mla_get_metadata", "mla_plan_attach_pages", "mla_get_metadata_device", "mla_max_parts",
+            "mla_workspace_bytes",
             "mla_decode_fwd", "mla_decode_fwd_noalloc", "mla_max_parts_sparse", "mla_get_metadata_sparse", "mla_decode_sparse_fwd",
             "mla_profile_start", "mla_profile_stop", "mla_last_error")
 
@@ -59,8 +60,10 @@ def lib() -> ctypes.CDLL:
     L.mla_max_parts.restype = ctypes.c_int
     L.mla_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     L.mla_workspace_bytes.restype = ctypes.c_size_t
+    L.mla_plan_attach_pages.argtypes = [i32p, ctypes.c_int, i32p, ctypes.c_int, i32p, ctypes.c_int, ctypes.c_int]
+    L.mla_plan_attach_pages.restype = ctypes.c_int
     L.mla_get_metadata_device.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                          vp, ctypes.c_int, vp, ip, vp]
+                                          vp, ctypes.c_int, vp, vp, ctypes.c_int, ctypes.c_int, ip, vp]
     L.mla_get_metadata_device.restype = ctypes.c_int
     L.mla_decode_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, vp, vp,
@@ -123,9 +126,12 @@ def mla_plan(cache_seqlens, num_parts: int, fixed_overhead: int = 0, force_split
 
 
 def get_mla_metadata_host(cache_seqlens, h_q: int, s_q: int, num_cus: int = 0, force_splits: int = 0,
-                          fp8: bool = False):
+                          fp8: bool = False, block_table=None, num_blocks: int = 0):
     """mla_get_metadata on host arrays: (sched [P, 8], num_splits [b + 1], total_splits).
-    ``fp8``: the plan serves decode calls on an FP8 cache."""
+    ``fp8``: the plan serves decode calls on an FP8 cache.  With ``block_table``
+    (int32 [b, max_blocks], the decode calls' table; host array or tensor) and
+    ``num_blocks`` (the pool's block count) each part's first page is attached
+    (mla_plan_attach_pages)."""
     sl = _i32_host(cache_seqlens)
     b = int(sl.shape[0])
     L = lib()
@@ -139,33 +145,60 @@ def get_mla_metadata_host(cache_seqlens, h_q: int, s_q: int, num_cus: int = 0, f
     _check(L.mla_get_metadata(_ptr(sl), b, int(h_q), int(s_q), f8, int(num_cus), int(force_splits), _ptr(sched),
                               sched.shape[0], _ptr(ns), ctypes.byref(nparts), ctypes.byref(total)),
            "mla_get_metadata")
-    return sched[:nparts.value].copy(), ns, int(total.value)
+    sched = sched[:nparts.value].copy()
+    if block_table is not None:
+        attach_pages(sched, sl, block_table, num_blocks)
+    return sched, ns, int(total.value)
+
+
+def attach_pages(sched: np.ndarray, cache_seqlens, block_table, num_blocks: int) -> np.ndarray:
+    """mla_plan_attach_pages on a host plan (int32 [P, 8], modified in place)."""
+    _need(isinstance(sched, np.ndarray) and sched.dtype == np.int32 and sched.ndim == 2
+          and sched.shape[1] == SCHED_INTS and sched.flags.c_contiguous, "sched must be a contiguous int32 [P, 8] array")
+    sl = _i32_host(cache_seqlens)
+    bt = np.ascontiguousarray(_i32_host(block_table))
+    _need(bt.ndim == 2 and bt.shape[0] == sl.shape[0], "block_table must be int32 [b, max_blocks]")
+    _check(lib().mla_plan_attach_pages(_ptr(sched), int(sched.shape[0]), _ptr(sl), int(sl.shape[0]), _ptr(bt),
+                                       int(bt.shape[1]), int(num_blocks)), "mla_plan_attach_pages")
+    return sched
 
 
 def get_mla_metadata(cache_seqlens, h_q: int, s_q: int, num_cus: int = 0, force_splits: int = 0,
-                     device=None, fp8: bool = False):
+                     device=None, fp8: bool = False, block_table=None, num_blocks: int = 0):
     """Plan one decode step; returns (sched, num_splits) as int32 device tensors.
 
     The plan is reusable for every call with the same batch, s_q, h_q, cache
     format (``fp8``) and cache_seqlens (e.g. every layer of one decode step).
     ``cache_seqlens`` may be a host array or a tensor; the planner reads it on
-    the host.
+    the host.  Passing the decode calls' ``block_table`` and the pool's
+    ``num_blocks`` attaches each part's first page (the plan then also needs
+    that table unchanged at those positions).
     """
     import torch
-    sched, ns, _ = get_mla_metadata_host(cache_seqlens, h_q, s_q, num_cus, force_splits, fp8)
+    sched, ns, _ = get_mla_metadata_host(cache_seqlens, h_q, s_q, num_cus, force_splits, fp8, block_table,
+                                         num_blocks)
     dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
     return (torch.from_numpy(sched).to(dev, non_blocking=False),
             torch.from_numpy(ns).to(dev, non_blocking=False))
 
 
-def get_mla_metadata_device(cache_seqlens, h_q: int, s_q: int, num_cus: int = 0, fp8: bool = False):
+def get_mla_metadata_device(cache_seqlens, h_q: int, s_q: int, num_cus: int = 0, fp8: bool = False,
+                            block_table=None, num_blocks: int = 0):
     """The split plan computed on the GPU from device lengths (int32 [b]),
     enqueued on the current stream: returns (sched int32 [P, 8],
     num_splits int32 [b + 1]) device tensors, P = the policy's part count
-    (rows past the walk's last part are empty).  Capturable in a graph."""
+    (rows past the walk's last part are empty).  Capturable in a graph.
+    With ``block_table`` (int32 [b, max_blocks] GPU tensor) and
+    ``num_blocks`` the plan carries each part's first page."""
     import torch
     _need(cache_seqlens.dim() == 1 and cache_seqlens.dtype == torch.int32 and cache_seqlens.is_cuda
           and cache_seqlens.is_contiguous(), "cache_seqlens must be a contiguous int32 [b] GPU tensor")
+    bt_ptr, max_blocks = None, 0
+    if block_table is not None:
+        _need(block_table.dim() == 2 and block_table.dtype == torch.int32 and block_table.is_cuda
+              and block_table.is_contiguous() and block_table.shape[0] == cache_seqlens.shape[0],
+              "block_table must be a contiguous int32 [b, max_blocks] GPU tensor")
+        bt_ptr, max_blocks = block_table.data_ptr(), int(block_table.shape[1])
     b = int(cache_seqlens.shape[0])
     dummy = np.zeros(b, dtype=np.int32)   # the part count depends on sizes only
     f8 = 1 if fp8 else 0
@@ -177,7 +210,8 @@ def get_mla_metadata_device(cache_seqlens, h_q: int, s_q: int, num_cus: int = 0,
     parts = ctypes.c_int(0)
     stream = torch.cuda.current_stream(dev).cuda_stream
     _check(lib().mla_get_metadata_device(cache_seqlens.data_ptr(), b, int(h_q), int(s_q), f8, int(num_cus),
-                                         sched.data_ptr(), cap, ns.data_ptr(), ctypes.byref(parts), stream),
+                                         sched.data_ptr(), cap, ns.data_ptr(), bt_ptr, max_blocks, int(num_blocks),
+                                         ctypes.byref(parts), stream),
            "mla_get_metadata_device")
     return sched[:parts.value], ns
 

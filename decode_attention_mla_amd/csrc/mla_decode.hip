@@ -102,11 +102,20 @@ extern "C" int mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q
   return MLA_OK;
 }
 
+extern "C" int mla_plan_attach_pages(int32_t* sched, int num_parts, const int32_t* cache_seqlens, int batch,
+                                     const int32_t* block_table, int max_blocks_per_seq, int num_blocks) {
+  return attach_pages(sched, num_parts, cache_seqlens, batch, block_table, max_blocks_per_seq, num_blocks);
+}
+
 extern "C" int mla_get_metadata_device(const int32_t* cache_seqlens_dev, int batch, int h_q, int s_q, int is_fp8,
                                        int num_cus, int32_t* sched_dev, int max_parts, int32_t* num_splits_dev,
+                                       const int32_t* block_table_dev, int max_blocks_per_seq, int num_blocks,
                                        int* num_parts_out, void* stream) {
   if (!sched_dev || !num_splits_dev || !num_parts_out)
     return set_error(MLA_ERR_INVALID, "mla_get_metadata_device: null pointer argument");
+  if (block_table_dev && (max_blocks_per_seq <= 0 || num_blocks <= 0))
+    return set_error(MLA_ERR_INVALID, "mla_get_metadata_device: block table with max_blocks_per_seq=%d num_blocks=%d",
+                     max_blocks_per_seq, num_blocks);
   if (batch > kPlanMaxBatch)
     return set_error(MLA_ERR_INVALID, "mla_get_metadata_device: batch=%d > %d", batch, kPlanMaxBatch);
   int parts, F;
@@ -117,7 +126,7 @@ extern "C" int mla_get_metadata_device(const int32_t* cache_seqlens_dev, int bat
   if (parts > kPlanMaxParts)
     return set_error(MLA_ERR_INVALID, "mla_get_metadata_device: %d parts > %d", parts, kPlanMaxParts);
   hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, cache_seqlens_dev, batch, parts, F,
-                     sched_dev, num_splits_dev);
+                     sched_dev, num_splits_dev, block_table_dev, max_blocks_per_seq, num_blocks);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(MLA_ERR_HIP, "mla_get_metadata_device: launch: %s", hipGetErrorString(e));
   *num_parts_out = parts;

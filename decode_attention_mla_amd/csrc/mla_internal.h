@@ -23,6 +23,8 @@ int set_error(int code, const char* fmt, ...);
 
 int plan(const int32_t* seqlens, int batch, int num_parts, int fixed_overhead, int force_splits,
          int32_t* sched, int max_parts, int32_t* num_splits, int* parts_out);
+int attach_pages(int32_t* sched, int num_parts, const int32_t* seqlens, int batch, const int32_t* block_table,
+                 int max_blocks, int num_blocks);
 
 // Launch geometry shared by the planner policy and the kernels.
 struct Geometry {

@@ -538,12 +538,15 @@ __device__ __forceinline__ void store_cols4(const Params& p, int req, int row, b
 // request, its block range, piece index and partial slot.
 struct PieceRange {
   int begin_req, end_req, begin_blk, end_blk, begin_piece;
+  int first_page;   // block id of page begin_blk of begin_req if the plan carries it, else -1
 };
 
-// The whole 32-byte row in one scalar load (one round trip).
+// The whole 32-byte row in one scalar load (one round trip).  Column 6 holds
+// the first page's block id + 1 when the caller attached the block table to
+// the plan (0 otherwise).
 __device__ __forceinline__ PieceRange load_part(const Params& p, int part) {
   const i32x8 v = ld_uniform((const i32x8*)(p.sched + part * MLA_SCHED_INTS));
-  return PieceRange{v[0], v[1], v[2], v[3], v[4]};
+  return PieceRange{v[0], v[1], v[2], v[3], v[4], v[6] - 1};
 }
 
 // What a piece needs of request `req` before its first copies: the length,
@@ -721,8 +724,28 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(MLA_SPLITKV_H
   // (2 (wave % 2) + g / 2, c16), bytes 8 (g % 2) .. + 7.
   const int pw_off = ((wave >> 1) * 64 + (2 * (wave & 1) + (g >> 1)) * 16 + c16) * 16 + 8 * (g & 1);
 
+  // A plan that carries the first page's block id lets the part's first
+  // request start its Q and first-page copies right after the plan row,
+  // one dependent round trip (the request's metadata) earlier.  The copies
+  // go out in the same order as below, so every wait stays as it is.
+  const bool early = !kSparse && pr.first_page >= 0 && pr.begin_req <= pr.end_req;   // uniform
+  if (early) {
+    const unsigned char* qrows = uniform_ptr(p.q + (size_t)pr.begin_req * p.R * kRowBytes);
+    const unsigned qslice = (unsigned)(size_t)lds + (kFp8 ? 0 : kPageBytes);
+    for (int i = wave; i < kStageSlices; i += 4) issue_stage_slice<false>(qrows, qslice, q_dma_off, i);
+    if constexpr (kFp8) {
+      const unsigned char* rows = uniform_ptr(p.kv + (size_t)pr.first_page * kFp8Page + (size_t)tok0 * kFp8Row);
+#pragma unroll
+      for (int i = 0; i < kFp8Copies; ++i) issue_fp8_copy<false>(rows, fslice, i, lane);
+    } else {
+      issue_stage<false>(uniform_ptr(p.kv + (size_t)pr.first_page * kPageBytes + (size_t)tok0 * kRowBytes), wslice,
+                         dma_off);
+    }
+  }
+
   for (int req = pr.begin_req; req <= pr.end_req; ++req) {
     const int lo = (req == pr.begin_req) ? pr.begin_blk : 0;
+    const bool copied = early && req == pr.begin_req;   // Q and page lo already in flight
     const RequestMeta m = kSparse ? load_request_sparse(p, req) : load_request(p, req, lo);
     // Sparse: the entries of pages lo .. lo + 2, read with the metadata.
     int ent[3] = {0, 0, 0};
@@ -772,7 +795,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(MLA_SPLITKV_H
       g0 = gather_page(p, ent[0], lo, L, tok0, lane);
       g1 = gather_page(p, ent[1], lo + 1, L, tok0, lane);
     }
-    {
+    if (!copied) {
       const unsigned char* qrows = uniform_ptr(p.q + (size_t)req * p.R * kRowBytes);
       const unsigned qslice = (unsigned)(size_t)lds + (kFp8 ? 0 : kPageBytes);
       for (int i = wave; i < kStageSlices; i += 4) issue_stage_slice<false>(qrows, qslice, q_dma_off, i);
@@ -782,13 +805,14 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(MLA_SPLITKV_H
       // page whose copy was issued last; the entries of the next page to copy.
       unsigned long long mk_cur = g0.mask, mk_lo1 = g1.mask, mk_pending = 0;
       int ent_next = kFp8 ? ent[1] : ent[2];
+      const bool first_in_flight = copied && attempt == 0;
       if constexpr (kFp8) {
-        if (lo < hi) issue_fp8_page(m.blk[0], g0.row, 0);
+        if (lo < hi && !first_in_flight) issue_fp8_page(m.blk[0], g0.row, 0);
         if (kF8Stages == 2 && lo + 1 < hi) issue_fp8_page(m.blk[1], 0, 1);
       } else if constexpr (kSparse) {
         if (lo < hi) issue_gather<false>(p, g0, dma_off, wslice);
       } else {
-        if (lo < hi) issue_stage<false>(page_rows(m.blk[0]), wslice, dma_off);
+        if (lo < hi && !first_in_flight) issue_stage<false>(page_rows(m.blk[0]), wslice, dma_off);
       }
       if (attempt == 0) {
         // this wave's pieces of Q (the first pages may still be in flight)
@@ -1969,7 +1993,8 @@ __device__ __forceinline__ long long readlane64(long long v, int lane) {
 }
 
 __global__ void __launch_bounds__(64) mla_plan_kernel(const int32_t* seqlens, int batch, int num_parts, int F,
-                                                    int32_t* sched, int32_t* num_splits) {
+                                                    int32_t* sched, int32_t* num_splits, const int32_t* block_table,
+                                                    int max_blocks, int num_blocks) {
   __shared__ int pb_req[kPlanMaxParts], pb_blk[kPlanMaxParts], pb_piece[kPlanMaxParts];
   const int lane = threadIdx.x;
   auto blocks_of = [](int L) { return pages_of(L); };   // negative lengths count as 0
@@ -2060,9 +2085,19 @@ __global__ void __launch_bounds__(64) mla_plan_kernel(const int32_t* seqlens, in
         eb = n_last;
       }
     }
+    // With a block table: 1 + the block id of the part's first page when its
+    // first piece holds a page (and the id lies in the pool), else 0.
+    int first_page = 0;
+    if (block_table && q < np) {
+      const int end = br == er ? eb : blocks_of(seqlens[br]);
+      if (bb < end && bb < max_blocks) {
+        const int id = block_table[(size_t)br * max_blocks + bb];
+        if (id >= 0 && id < num_blocks) first_page = id + 1;
+      }
+    }
     int4* row = reinterpret_cast<int4*>(sched + (size_t)q * MLA_SCHED_INTS);
     row[0] = make_int4(br, er, bb, eb);
-    row[1] = make_int4(bp, max_pieces, 0, 0);
+    row[1] = make_int4(bp, max_pieces, first_page, 0);
   }
 }
 

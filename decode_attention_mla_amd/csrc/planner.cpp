@@ -92,4 +92,36 @@ int plan(const int32_t* seqlens, int batch, int num_parts, int fixed_overhead, i
   return MLA_OK;
 }
 
+// Column 6 of every row: 1 + the block id of the part's first page (page
+// begin_block of begin_req) when that piece holds at least one page, else 0.
+// The split-KV kernels then start that page's copy as soon as they have read
+// the row, without waiting for the request's block-table entry.
+int attach_pages(int32_t* sched, int num_parts, const int32_t* seqlens, int batch, const int32_t* block_table,
+                 int max_blocks, int num_blocks) {
+  if (!sched || !seqlens || !block_table)
+    return set_error(MLA_ERR_INVALID, "mla_plan_attach_pages: null pointer argument");
+  if (num_parts <= 0 || batch <= 0 || max_blocks <= 0 || num_blocks <= 0)
+    return set_error(MLA_ERR_INVALID, "mla_plan_attach_pages: num_parts=%d batch=%d max_blocks=%d num_blocks=%d",
+                     num_parts, batch, max_blocks, num_blocks);
+  for (int q = 0; q < num_parts; ++q) {
+    int32_t* row = sched + (size_t)q * MLA_SCHED_INTS;
+    const int br = row[0], er = row[1], bb = row[2], eb = row[3];
+    row[6] = 0;
+    if (br > er) continue;   // a part with no work
+    if (br < 0 || er >= batch || bb < 0 || eb < 0)
+      return set_error(MLA_ERR_INVALID, "mla_plan_attach_pages: row %d names requests %d..%d of %d", q, br, er, batch);
+    const int end = (br == er) ? eb : pages_of(seqlens[br]);   // end of the part's first piece
+    if (bb >= end) continue;                                   // that piece holds no page
+    if (bb >= max_blocks)
+      return set_error(MLA_ERR_INVALID, "mla_plan_attach_pages: row %d starts at page %d >= max_blocks=%d", q, bb,
+                       max_blocks);
+    const int id = block_table[(size_t)br * max_blocks + bb];
+    if (id < 0 || id >= num_blocks)
+      return set_error(MLA_ERR_INVALID, "mla_plan_attach_pages: block_table[%d][%d] = %d outside [0, %d)", br, bb, id,
+                       num_blocks);
+    row[6] = id + 1;
+  }
+  return MLA_OK;
+}
+
 }  // namespace mla

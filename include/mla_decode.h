@@ -47,10 +47,14 @@ enum {
 
 /* Rows of the per-part schedule table: 8 int32 per part,
  *   [begin_req, end_req (inclusive), begin_block (within begin_req),
- *    end_block (exclusive, within end_req), begin_piece, max_pieces, 0, 0]
+ *    end_block (exclusive, within end_req), begin_piece, max_pieces,
+ *    first_page, 0]
  * begin_piece is the index, among begin_req's pieces, of the piece this part
  * holds; max_pieces (equal in every row) is the largest number of pieces of
- * any request, which the merge kernel uses to pick its work layout.  num_splits is an exclusive prefix sum of pieces per request,
+ * any request, which the merge kernel uses to pick its work layout;
+ * first_page is 0, or 1 + the block id of the part's first page once the
+ * block table is attached (mla_plan_attach_pages, or mla_get_metadata_device
+ * given the table).  num_splits is an exclusive prefix sum of pieces per request,
  * length batch + 1: request b owns partial slots [num_splits[b], num_splits[b+1]). */
 #define MLA_SCHED_INTS 8
 
@@ -104,6 +108,29 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q, int s_q, 
                      int32_t* num_splits_out, int* num_parts_out, int* total_splits_out);
 
 /*
+ * mla_plan_attach_pages — write into a host plan the block id of every part's
+ * first page (column 6: 1 + block_table[begin_req][begin_block], or 0 when
+ * the part has no work or its first piece holds no page).  The small-row
+ * split-KV kernel then issues that page's copy (and the query rows') as soon
+ * as it has read its plan row, one dependent round trip earlier than through
+ * the block table (the pages' tile scheduler hands each CTA its start the same
+ * way, "FlashMLA new-kernel deep dive", Tile Scheduler).  An attached plan is
+ * valid for the calls whose block table holds the same ids at those
+ * positions (within one decode step the table is shared by every layer);
+ * results are bitwise those of the plain plan.
+ *
+ *   sched          host int32 [num_parts * 8], from mla_get_metadata
+ *   cache_seqlens  host int32 [batch], the lengths the plan was made for
+ *   block_table    host int32 [batch, max_blocks_per_seq], the decode calls' table
+ *   num_blocks     the pool's block count (ids must lie in [0, num_blocks))
+ * Errors: MLA_ERR_INVALID (null pointers, sizes <= 0, a row naming requests
+ *         outside [0, batch), a first page past max_blocks_per_seq, an id
+ *         outside the pool).
+ */
+int mla_plan_attach_pages(int32_t* sched, int num_parts, const int32_t* cache_seqlens, int batch,
+                          const int32_t* block_table, int max_blocks_per_seq, int num_blocks);
+
+/*
  * mla_get_metadata_device — the same plan as mla_get_metadata (greedy walk,
  * no force_splits) computed on the GPU from device lengths, enqueued on
  * `stream` (the pages run their tile scheduler as a one-warp kernel,
@@ -118,6 +145,11 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q, int s_q, 
  *   sched_dev         device int32 [max_parts * 8]; max_parts >= the policy's
  *                     part count (mla_max_parts(..., force_splits = 0))
  *   num_splits_dev    device int32 [batch + 1]
+ *   block_table_dev   device int32 [batch, max_blocks_per_seq] or NULL: with
+ *                     a table the plan carries each part's first page
+ *                     (column 6, as mla_plan_attach_pages writes it; ids
+ *                     outside [0, num_blocks) are left unattached), read
+ *                     when the kernel runs
  *   num_parts_out     host: the rows written = the policy's part count, the
  *                     num_parts to pass to mla_decode_fwd; rows after the
  *                     walk's last part are empty (begin_req 1 > end_req 0)
@@ -126,11 +158,13 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int h_q, int s_q, 
  * mla_workspace_bytes(num_parts + batch - 1, h_q, s_q) fits any lengths.
  * Allocates nothing, does not synchronise; batch <= 65536 and the policy's
  * part count <= 4096 (one workgroup; LDS holds where each part begins).
- * Errors: MLA_ERR_INVALID (also for the limits above), MLA_ERR_CAPACITY,
+ * Errors: MLA_ERR_INVALID (also for the limits above, and a table with
+ *         max_blocks_per_seq or num_blocks <= 0), MLA_ERR_CAPACITY,
  *         MLA_ERR_HIP.
  */
 int mla_get_metadata_device(const int32_t* cache_seqlens_dev, int batch, int h_q, int s_q, int is_fp8,
                             int num_cus, int32_t* sched_dev, int max_parts, int32_t* num_splits_dev,
+                            const int32_t* block_table_dev, int max_blocks_per_seq, int num_blocks,
                             int* num_parts_out, void* stream);
 
 /* Upper bound on the parts mla_get_metadata can emit for these sizes. */

@@ -117,6 +117,81 @@ def test_plan_errors():
     assert rc == -2 and b"max_parts" in L.mla_last_error()
 
 
+def _expected_first_pages(sched, seqlens, table):
+    """Column 6 written out from the plan row's meaning: the part's first
+    piece covers pages begin_block .. (end_block if it ends in the same
+    request, else that request's last page) of begin_req."""
+    want = np.zeros(sched.shape[0], dtype=np.int32)
+    for q, (br, er, bb, eb) in enumerate(sched[:, :4]):
+        if br > er:
+            continue
+        end = eb if br == er else -(-int(seqlens[br]) // 64)
+        if bb < end:
+            want[q] = table[br, bb] + 1
+    return want
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_attach_pages_writes_each_parts_first_block_id(seed):
+    rng = np.random.default_rng(300 + seed)
+    b = int(rng.integers(1, 70))
+    sl = rng.integers(0, 9000, size=b).astype(np.int32)
+    sl[rng.random(b) < 0.25] = 0                               # empty requests: parts with no page
+    max_blocks = int(-(-sl.max() // 64)) + int(rng.integers(1, 4))
+    num_blocks = b * max_blocks
+    table = rng.permutation(num_blocks).astype(np.int32).reshape(b, max_blocks)
+    for force in (0, int(rng.integers(1, 6))):
+        sched, ns, _ = mla.get_mla_metadata_host(sl, 16, 1, num_cus=int(rng.integers(1, 300)), force_splits=force)
+        plain = sched.copy()
+        assert np.all(plain[:, 6] == 0)
+        mla.binding.attach_pages(sched, sl, table, num_blocks)
+        assert np.array_equal(sched[:, [0, 1, 2, 3, 4, 5, 7]], plain[:, [0, 1, 2, 3, 4, 5, 7]])
+        want = _expected_first_pages(plain, sl, table)
+        assert np.array_equal(sched[:, 6], want)
+        nonempty = (plain[:, 0] <= plain[:, 1])
+        # every part whose first piece holds pages starts on one (an empty
+        # request as the first piece leaves the column 0)
+        assert np.all((sched[:, 6] > 0) <= nonempty)
+        mla.binding.attach_pages(sched, sl, table, num_blocks)  # idempotent
+        assert np.array_equal(sched[:, 6], want)
+
+
+def test_attach_pages_through_get_metadata_equals_attaching_afterwards():
+    sl = np.array([100, 0, 257, 4096, 1], dtype=np.int32)
+    table = (np.arange(5 * 64, dtype=np.int32).reshape(5, 64) * 7) % 320
+    a, na, ta = mla.get_mla_metadata_host(sl, 16, 1, num_cus=64, block_table=table, num_blocks=320)
+    b, nb, tb = mla.get_mla_metadata_host(sl, 16, 1, num_cus=64)
+    mla.binding.attach_pages(b, sl, table, 320)
+    assert np.array_equal(a, b) and np.array_equal(na, nb) and ta == tb
+    assert a[0, 6] == table[0, 0] + 1
+
+
+def test_attach_pages_errors():
+    L = mla.lib()
+    p32 = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))  # noqa: E731
+    sl = np.array([200, 64], dtype=np.int32)
+    sched, _, _ = mla.get_mla_metadata_host(sl, 16, 1, num_cus=2)
+    table = np.array([[0, 1, 2, 3], [4, 5, 6, 7]], dtype=np.int32)
+    rc = L.mla_plan_attach_pages(None, 2, p32(sl), 2, p32(table), 4, 8)
+    assert rc == -1 and b"null" in L.mla_last_error()
+    rc = L.mla_plan_attach_pages(p32(sched), sched.shape[0], p32(sl), 2, p32(table), 4, 0)
+    assert rc == -1 and b"num_blocks=0" in L.mla_last_error()
+    with pytest.raises(mla.MlaError, match="outside"):
+        mla.binding.attach_pages(sched.copy(), sl, table, 3)          # id 4 of request 1 is past a 3-block pool
+    bad = table.copy()
+    bad[0, 0] = -1
+    with pytest.raises(mla.MlaError, match="outside"):
+        mla.binding.attach_pages(sched.copy(), sl, bad, 8)
+    split, _, _ = mla.get_mla_metadata_host(sl, 16, 1, num_cus=2, force_splits=2)
+    assert split[1, 0] == 0 and split[1, 2] == 2                      # request 0's second piece starts at page 2
+    with pytest.raises(mla.MlaError, match="max_blocks"):
+        mla.binding.attach_pages(split, sl, table[:, :2].copy(), 8)
+    rows = sched.copy()
+    rows[0, 1] = 5                                                    # names request 5 of 2
+    with pytest.raises(mla.MlaError, match="names requests"):
+        mla.binding.attach_pages(rows, sl, table, 8)
+
+
 def test_decode_argument_errors_return_codes_without_launching():
     L = mla.lib()
     rc = L.mla_decode_fwd(None, None, None, None, 1, 1, 16, 1, 1, 0.1, 0, 0, None, 1, None, None, 0, None, None, None)
@@ -143,13 +218,13 @@ def test_device_planner_argument_errors_return_codes_without_launching():
     L = mla.lib()
     dummy = ctypes.c_void_p(16)   # never dereferenced: every check fails before any launch
     n = ctypes.c_int(0)
-    rc = L.mla_get_metadata_device(dummy, 4, 16, 1, 0, 256, None, 256, dummy, ctypes.byref(n), None)
+    rc = L.mla_get_metadata_device(dummy, 4, 16, 1, 0, 256, None, 256, dummy, None, 0, 0, ctypes.byref(n), None)
     assert rc == -1 and b"null" in L.mla_last_error()
-    rc = L.mla_get_metadata_device(dummy, 70000, 16, 1, 0, 256, dummy, 256, dummy, ctypes.byref(n), None)
+    rc = L.mla_get_metadata_device(dummy, 70000, 16, 1, 0, 256, dummy, 256, dummy, None, 0, 0, ctypes.byref(n), None)
     assert rc == -1 and b"batch" in L.mla_last_error()
-    rc = L.mla_get_metadata_device(dummy, 4, 16, 1, 0, 256, dummy, 255, dummy, ctypes.byref(n), None)
+    rc = L.mla_get_metadata_device(dummy, 4, 16, 1, 0, 256, dummy, 255, dummy, None, 0, 0, ctypes.byref(n), None)
     assert rc == -2 and b"max_parts" in L.mla_last_error()
-    rc = L.mla_get_metadata_device(dummy, 4, 16, 1, 0, 5000, dummy, 5000, dummy, ctypes.byref(n), None)
+    rc = L.mla_get_metadata_device(dummy, 4, 16, 1, 0, 5000, dummy, 5000, dummy, None, 0, 0, ctypes.byref(n), None)
     assert rc == -1 and b"4096" in L.mla_last_error()
 
 
@@ -258,6 +333,11 @@ int main() {
       if (mla::plan(lens, b, P, F, 0, sched.data(), 4096, ns.data(), &parts) != 0) return 2;
   for (int k : {1, 3, 64})
     if (mla::plan(lens, b, 1, 0, k, sched.data(), 4096, ns.data(), &parts) != 0) return 3;
+  std::vector<int32_t> table(b * 64, 0);
+  if (mla::plan(lens, b, 1, 0, 0, sched.data(), 4096, ns.data(), &parts) != 0) return 4;
+  if (mla::attach_pages(sched.data(), parts, lens, b, table.data(), 64, 1) != 0 || sched[6] != 1) return 5;
+  if (mla::plan(lens, b, 4096, 3, 0, sched.data(), 4096, ns.data(), &parts) != 0) return 6;
+  if (mla::attach_pages(sched.data(), parts, lens, b, table.data(), 64, 1) == 0) return 7;   // pages past 64
   for (int L : {2147483647, 2147483584, 2147483583, 1, 0, -5})
     std::printf("%d ", mla::pages_of(L));
   std::printf("ok\n");
