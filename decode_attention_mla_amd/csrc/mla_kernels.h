@@ -1823,9 +1823,12 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(MLA_SPLITKV_HO
 // M = max lse_i, w_i = 2^(lse_i - M), out = sum w_i O_i / sum w_i,
 // lse = M + log2(sum w_i) (then converted to natural log).  Rows of requests
 // that are not split are skipped (the main kernel wrote them).
-//   Each lane owns 8 consecutive columns and issues the loads of
-// kCombineChunk splits at once (two 16-byte loads each), so a wave pays one
-// memory round trip per chunk.  If no request has more than kCombineChunk
+//   Each lane owns 8 consecutive columns and issues the loads of a chunk of
+// splits at once (two 16-byte loads each), so a wave pays one memory round
+// trip per chunk.  The chunk is the smallest of 2, 4 and kCombineChunk that
+// holds all of the wave's splits (the last chunk's missing entries repeat
+// the last split with weight 0, so a smaller chunk issues fewer such loads:
+// measured 0.4 us of the memory-bound step, 14 splits a pair over 4 waves).  If no request has more than kCombineChunk
 // pieces (the schedule table says), each wave merges one (request, row) pair
 // on its own (many short merges: no LDS, no barrier); otherwise a workgroup
 // merges one pair, wave w taking splits w, w + 4, ..., and the four states
@@ -1834,15 +1837,16 @@ constexpr int kCombineWaves = 4;
 constexpr int kCombineChunk = 8;
 
 // Online merge of splits first, first + step, ... (count of them) of one
-// pair into (M, l, a0, a1).
-__device__ __forceinline__ void combine_splits(const float* lrow, const float* orow, size_t lstride, size_t ostride,
+// pair into (M, l, a0, a1), kChunk splits a round trip.
+template <int kChunk>
+__device__ __forceinline__ void combine_chunks(const float* lrow, const float* orow, size_t lstride, size_t ostride,
                                                int first, int step, int count, float& M, float& l, f32x4& a0,
                                                f32x4& a1) {
-  for (int k0 = 0; k0 < count; k0 += kCombineChunk) {
-    float li[kCombineChunk];
-    f32x4 b0[kCombineChunk], b1[kCombineChunk];
+  for (int k0 = 0; k0 < count; k0 += kChunk) {
+    float li[kChunk];
+    f32x4 b0[kChunk], b1[kChunk];
 #pragma unroll
-    for (int u = 0; u < kCombineChunk; ++u) {
+    for (int u = 0; u < kChunk; ++u) {
       const int i = first + step * min(k0 + u, count - 1);   // clamped: duplicates get weight 0 below
       li[u] = ld_uniform(lrow + (size_t)i * lstride);
       b0[u] = *(const f32x4*)(orow + (size_t)i * ostride);
@@ -1850,7 +1854,7 @@ __device__ __forceinline__ void combine_splits(const float* lrow, const float* o
     }
     float Mc = M;
 #pragma unroll
-    for (int u = 0; u < kCombineChunk; ++u)
+    for (int u = 0; u < kChunk; ++u)
       if (k0 + u < count) Mc = fmaxf(Mc, li[u]);
     if (Mc == -INFINITY) continue;   // nothing with mass so far (uniform)
     const float sa = __builtin_amdgcn_exp2f(M - Mc);   // M = -inf gives 0
@@ -1858,7 +1862,7 @@ __device__ __forceinline__ void combine_splits(const float* lrow, const float* o
     a1 *= sa;
     l *= sa;
 #pragma unroll
-    for (int u = 0; u < kCombineChunk; ++u) {
+    for (int u = 0; u < kChunk; ++u) {
       const float w = (k0 + u < count) ? __builtin_amdgcn_exp2f(li[u] - Mc) : 0.f;   // lse = -inf gives 0
       a0 += w * b0[u];
       a1 += w * b1[u];
@@ -1866,6 +1870,18 @@ __device__ __forceinline__ void combine_splits(const float* lrow, const float* o
     }
     M = Mc;
   }
+}
+
+// combine_chunks with the chunk picked by the split count (uniform over the wave).
+__device__ __forceinline__ void combine_splits(const float* lrow, const float* orow, size_t lstride, size_t ostride,
+                                               int first, int step, int count, float& M, float& l, f32x4& a0,
+                                               f32x4& a1) {
+  if (count <= 2)
+    combine_chunks<2>(lrow, orow, lstride, ostride, first, step, count, M, l, a0, a1);
+  else if (count <= 4)
+    combine_chunks<4>(lrow, orow, lstride, ostride, first, step, count, M, l, a0, a1);
+  else
+    combine_chunks<kCombineChunk>(lrow, orow, lstride, ostride, first, step, count, M, l, a0, a1);
 }
 
 __device__ __forceinline__ void combine_store(const Params& p, int req, int row, int lane, float M, float l, f32x4 a0,
