@@ -164,6 +164,12 @@ class ClockSampler:
     def mhz(self):
         return float(np.median(self.samples)) if self.samples else None
 
+    def spread(self):
+        """[p10, p90, number of samples] of the last run's readings (None if none)."""
+        if not self.samples:
+            return None
+        return [float(np.percentile(self.samples, 10)), float(np.percentile(self.samples, 90)), len(self.samples)]
+
 
 CLOCK = None
 
@@ -238,6 +244,7 @@ def time_steps(step, rot: int, steps: int, warmup: int):
             per.append((a, b))
     torch.cuda.synchronize()
     clock = CLOCK.stop() if CLOCK is not None else None
+    clock_spread = CLOCK.spread() if CLOCK is not None else None
     per_step = np.array([a.elapsed_time(b) / steps for a, b in per])
     # --- per-kernel durations, eager calls behind a warm replay
     with torch.cuda.stream(s):
@@ -258,7 +265,7 @@ def time_steps(step, rot: int, steps: int, warmup: int):
                 spread_steps=int(reps * steps), median_ms=float(np.median(per_step)),
                 p10_ms=float(np.percentile(per_step, 10)), p90_ms=float(np.percentile(per_step, 90)),
                 main_kernel_ms=main_ms / calls, combine_kernel_ms=comb_ms / calls, eager_ms_per_step=eager_ms,
-                clock_mhz=clock)
+                clock_mhz=clock, clock_mhz_p10_p90_n=clock_spread)
 
 
 # ---------------------------------------------------------------------------
