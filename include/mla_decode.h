@@ -203,6 +203,9 @@ size_t mla_workspace_bytes(int total_splits, int h_q, int s_q);
  *                 new-kernel deep dive", API section); a token that sees no
  *                 key gets out = 0, lse = -inf
  *   sched         device int32 [num_parts, 8] from mla_get_metadata/mla_plan
+ *                 (or mla_get_metadata_device); if it carries first pages
+ *                 (mla_plan_attach_pages), block_table must hold the same
+ *                 ids at those positions
  *   num_splits    device int32 [batch + 1] from the same plan
  *   workspace     device, >= mla_workspace_bytes(num_parts + batch - 1, h_q, s_q)
  *                 bytes (the bound on partial slots of any plan with num_parts)
