@@ -125,7 +125,8 @@ extern "C" int mla_get_metadata_device(const int32_t* cache_seqlens_dev, int bat
     return set_error(MLA_ERR_CAPACITY, "mla_get_metadata_device: max_parts=%d < %d parts", max_parts, parts);
   if (parts > kPlanMaxParts)
     return set_error(MLA_ERR_INVALID, "mla_get_metadata_device: %d parts > %d", parts, kPlanMaxParts);
-  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, cache_seqlens_dev, batch, parts, F,
+  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(kPlanWaves * 64), 0, (hipStream_t)stream, cache_seqlens_dev, batch,
+                     parts, F,
                      sched_dev, num_splits_dev, block_table_dev, max_blocks_per_seq, num_blocks);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(MLA_ERR_HIP, "mla_get_metadata_device: launch: %s", hipGetErrorString(e));

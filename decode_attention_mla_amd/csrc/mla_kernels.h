@@ -2009,9 +2009,11 @@ __global__ void __launch_bounds__(kCombineWaves * 64) mla_combine_kernel(MLA_COM
 // filled with payload - F of its blocks, k = (rem - 1) / (payload - F) times,
 // and its last piece opens the part the walk continues in.  Each fresh part
 // records where it begins (request, block, piece index) in LDS; a part ends
-// where the next one begins, so the rows are then written one lane per part.
+// where the next one begins, so the rows are then written one lane per part,
+// by all kPlanWaves waves (the walk itself is one wave's).
 constexpr int kPlanMaxBatch = 1 << 16;
 constexpr int kPlanMaxParts = 4096;
+constexpr int kPlanWaves = 4;
 
 __device__ __forceinline__ long long readlane64(long long v, int lane) {
   const int lo = __builtin_amdgcn_readlane((int)(v & 0xffffffff), lane);
@@ -2019,108 +2021,119 @@ __device__ __forceinline__ long long readlane64(long long v, int lane) {
   return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
 }
 
-__global__ void __launch_bounds__(64) mla_plan_kernel(const int32_t* seqlens, int batch, int num_parts, int F,
-                                                    int32_t* sched, int32_t* num_splits, const int32_t* block_table,
-                                                    int max_blocks, int num_blocks) {
+__global__ void __launch_bounds__(kPlanWaves * 64) mla_plan_kernel(const int32_t* seqlens, int batch, int num_parts,
+                                                                 int F, int32_t* sched, int32_t* num_splits,
+                                                                 const int32_t* block_table, int max_blocks,
+                                                                 int num_blocks) {
   __shared__ int pb_req[kPlanMaxParts], pb_blk[kPlanMaxParts], pb_piece[kPlanMaxParts];
-  const int lane = threadIdx.x;
+  __shared__ int walk_out[2];   // parts the walk used, largest piece count
   auto blocks_of = [](int L) { return pages_of(L); };   // negative lengths count as 0
-  // total = sum (n_b + F); payload = ceil(total / parts) + F
-  long long part_sum = 0;
-  for (int b = lane; b < batch; b += 64) part_sum += blocks_of(seqlens[b]) + F;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    // total = sum (n_b + F); payload = ceil(total / parts) + F
+    long long part_sum = 0;
+    for (int b = lane; b < batch; b += 64) part_sum += blocks_of(seqlens[b]) + F;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) part_sum += __shfl_xor(part_sum, off);
-  const long long total = readlane64(part_sum, 0);
-  const long long P = (total + num_parts - 1) / num_parts + F;
-  const long long D = P - F;    // blocks a piece may take in a part of its own
-  const int last = num_parts - 1;
+    for (int off = 32; off > 0; off >>= 1) part_sum += __shfl_xor(part_sum, off);
+    const long long total = readlane64(part_sum, 0);
+    const long long P = (total + num_parts - 1) / num_parts + F;
+    const long long D = P - F;    // blocks a piece may take in a part of its own
+    const int last = num_parts - 1;
 
-  int p = 0;                    // the part the walk is in
-  long long cap = P;            // capacity left in part p
-  int acc = 0, max_pieces = 1;  // pieces of the requests before this chunk; largest piece count
-  if (lane == 0) {
-    pb_req[0] = pb_blk[0] = pb_piece[0] = 0;
-    num_splits[0] = 0;
-  }
-  for (int base = 0; base < batch; base += 64) {
-    const int cnt = min(64, batch - base);
-    const int n = lane < cnt ? blocks_of(seqlens[base + lane]) : 0;
-    long long z = (long long)n + F;   // inclusive prefix of costs in the chunk
+    int p = 0;                    // the part the walk is in
+    long long cap = P;            // capacity left in part p
+    int acc = 0, max_pieces = 1;  // pieces of the requests before this chunk; largest piece count
+    if (lane == 0) {
+      pb_req[0] = pb_blk[0] = pb_piece[0] = 0;
+      num_splits[0] = 0;
+    }
+    for (int base = 0; base < batch; base += 64) {
+      const int cnt = min(64, batch - base);
+      const int n = lane < cnt ? blocks_of(seqlens[base + lane]) : 0;
+      long long z = (long long)n + F;   // inclusive prefix of costs in the chunk
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const long long t = __shfl_up(z, off);
-      if (lane >= off) z += t;
-    }
-    int pieces = lane < cnt ? 1 : 0;
-    int i0 = 0;           // first request of the chunk not placed yet
-    long long zb = 0;     // prefix of costs before request i0
-    while (i0 < cnt && p < last) {   // in the last part every request fits whole
-      const unsigned long long fit = __ballot(lane >= i0 && lane < cnt && z - zb <= cap);
-      const int i1 = i0 + __popcll(fit);   // costs are >= 0: the fitting requests are i0 .. i1 - 1
-      if (i1 > i0) {
-        const long long zl = readlane64(z, i1 - 1);
-        cap -= zl - zb;
-        zb = zl;
-        i0 = i1;
-        if (i0 >= cnt) break;
+      for (int off = 1; off < 64; off <<= 1) {
+        const long long t = __shfl_up(z, off);
+        if (lane >= off) z += t;
       }
-      // request i0 does not fit whole in what part p has left
-      const int n0 = __builtin_amdgcn_readlane(n, i0);
-      const long long take = cap - F;
-      const int b0 = take > 0 ? (int)take : 0;   // its blocks in part p (take < n0 here)
-      const int pi0 = take > 0 ? 1 : 0;
-      const int rem = n0 - b0;
-      int k = 0;                                 // fresh parts it fills whole
-      if (p + 1 < last && rem > D) k = min((int)((unsigned)(rem - 1) / (unsigned)D), last - p - 1);
-      for (int j = lane; j <= k; j += 64) {      // parts p + 1 .. p + 1 + k begin inside it
-        pb_req[p + 1 + j] = base + i0;
-        pb_blk[p + 1 + j] = b0 + j * (int)D;
-        pb_piece[p + 1 + j] = pi0 + j;
+      int pieces = lane < cnt ? 1 : 0;
+      int i0 = 0;           // first request of the chunk not placed yet
+      long long zb = 0;     // prefix of costs before request i0
+      while (i0 < cnt && p < last) {   // in the last part every request fits whole
+        const unsigned long long fit = __ballot(lane >= i0 && lane < cnt && z - zb <= cap);
+        const int i1 = i0 + __popcll(fit);   // costs are >= 0: the fitting requests are i0 .. i1 - 1
+        if (i1 > i0) {
+          const long long zl = readlane64(z, i1 - 1);
+          cap -= zl - zb;
+          zb = zl;
+          i0 = i1;
+          if (i0 >= cnt) break;
+        }
+        // request i0 does not fit whole in what part p has left
+        const int n0 = __builtin_amdgcn_readlane(n, i0);
+        const long long take = cap - F;
+        const int b0 = take > 0 ? (int)take : 0;   // its blocks in part p (take < n0 here)
+        const int pi0 = take > 0 ? 1 : 0;
+        const int rem = n0 - b0;
+        int k = 0;                                 // fresh parts it fills whole
+        if (p + 1 < last && rem > D) k = min((int)((unsigned)(rem - 1) / (unsigned)D), last - p - 1);
+        for (int j = lane; j <= k; j += 64) {      // parts p + 1 .. p + 1 + k begin inside it
+          pb_req[p + 1 + j] = base + i0;
+          pb_blk[p + 1 + j] = b0 + j * (int)D;
+          pb_piece[p + 1 + j] = pi0 + j;
+        }
+        p += 1 + k;
+        cap = P - F - (rem - (long long)k * D);    // after its last piece, in part p
+        const int pc = pi0 + k + 1;
+        if (lane == i0) pieces = pc;
+        max_pieces = max(max_pieces, pc);
+        zb = readlane64(z, i0);
+        ++i0;
       }
-      p += 1 + k;
-      cap = P - F - (rem - (long long)k * D);    // after its last piece, in part p
-      const int pc = pi0 + k + 1;
-      if (lane == i0) pieces = pc;
-      max_pieces = max(max_pieces, pc);
-      zb = readlane64(z, i0);
-      ++i0;
-    }
-    int s = pieces;       // num_splits: inclusive prefix of pieces
+      int s = pieces;       // num_splits: inclusive prefix of pieces
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(s, off);
-      if (lane >= off) s += t;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(s, off);
+        if (lane >= off) s += t;
+      }
+      if (lane < cnt) num_splits[base + lane + 1] = acc + s;
+      acc += __builtin_amdgcn_readlane(s, 63);
     }
-    if (lane < cnt) num_splits[base + lane + 1] = acc + s;
-    acc += __builtin_amdgcn_readlane(s, 63);
+    if (lane == 0) {
+      walk_out[0] = p + 1;
+      walk_out[1] = max_pieces;
+    }
   }
-  const int np = p + 1;   // parts the walk used
   __syncthreads();
-  const int n_last = blocks_of(seqlens[batch - 1]);
-  for (int q = lane; q < num_parts; q += 64) {
-    int br = 1, er = 0, bb = 0, eb = 0, bp = 0;
+  const int np = walk_out[0];   // parts the walk used
+  const int max_pieces = walk_out[1];
+  // Rows, one thread per part.  The lengths and block ids a row may need are
+  // read together (indices clamped; unused values are ignored), one round
+  // trip for all of them.
+  for (int q = threadIdx.x; q < num_parts; q += kPlanWaves * 64) {
+    int br = 1, er = 0, bb = 0, eb = 0, bp = 0, nr = 0, nb = 0;
     if (q < np) {
       br = pb_req[q];
       bb = pb_blk[q];
       bp = pb_piece[q];
       if (q + 1 < np) {   // part q ends where part q + 1 begins
-        const int nr = pb_req[q + 1], nb = pb_blk[q + 1];
+        nr = pb_req[q + 1];
+        nb = pb_blk[q + 1];
         er = nb > 0 ? nr : nr - 1;
-        eb = nb > 0 ? nb : blocks_of(seqlens[er]);
       } else {
         er = batch - 1;
-        eb = n_last;
       }
     }
+    const int len_er = seqlens[er < 0 ? 0 : er];
+    const int len_br = seqlens[br < batch ? br : batch - 1];
+    const int id = (block_table && q < np) ? block_table[(size_t)br * max_blocks + min(bb, max_blocks - 1)] : -1;
+    if (q < np) eb = (q + 1 < np && nb > 0) ? nb : blocks_of(len_er);
     // With a block table: 1 + the block id of the part's first page when its
     // first piece holds a page (and the id lies in the pool), else 0.
     int first_page = 0;
     if (block_table && q < np) {
-      const int end = br == er ? eb : blocks_of(seqlens[br]);
-      if (bb < end && bb < max_blocks) {
-        const int id = block_table[(size_t)br * max_blocks + bb];
-        if (id >= 0 && id < num_blocks) first_page = id + 1;
-      }
+      const int end = br == er ? eb : blocks_of(len_br);
+      if (bb < end && bb < max_blocks && id >= 0 && id < num_blocks) first_page = id + 1;
     }
     int4* row = reinterpret_cast<int4*>(sched + (size_t)q * MLA_SCHED_INTS);
     row[0] = make_int4(br, er, bb, eb);
