@@ -25,6 +25,21 @@ def test_tiny_config(force):
     assert_parity(out, lse, ref_out, ref_lse, f"config1 force_splits={force}")
 
 
+@pytest.mark.parametrize("h_q,s_q", [(16, 1), (128, 1)])
+@pytest.mark.parametrize("force", [2, 3, 4, 5, 8, 9, 12, 17, 33])
+def test_combine_over_every_chunk_size(h_q, s_q, force):
+    """Every request cut into exactly `force` pieces: up to 8 pieces a pair a
+    wave merges them (in chunks of 2, 4 or 8 by the count), above 8 the four
+    waves of a workgroup take every fourth piece (1 to 9 pieces a wave, so
+    every chunk size and a multi-chunk walk occur)."""
+    lens = [64 * 40, 64 * 37 + 5, 64 * 35 - 3]
+    inp = W.make_inputs(3, s_q, h_q, lens, pool=None, max_blocks=40, seed=900 + force)
+    print(f"[combine] h_q={h_q} force={force}", flush=True)
+    out, lse = run_gpu(inp, force_splits=force)
+    ref_out, ref_lse = _ref(inp)
+    assert_parity(out, lse, ref_out, ref_lse, f"combine chunks h_q={h_q} force={force}", out_tol=dense_out_bound(inp))
+
+
 def test_tiny_config_two_parts():
     # The other reading of "num_splits = 2": two parts, so only request 1 is cut.
     inp = W.config_inputs(1)
