@@ -681,7 +681,8 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(MLA_SPLITKV_H
   constexpr bool kPipe = kFp8 && !kSparse;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kFp8 ? kPageBytes + kF8Stages * kFp8Page : 2 * kPageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char pbuf[kSmallPBytes];
-  __shared__ float red[4][kSmallRows];   // per-wave row maxima, then row sums
+  __shared__ float red[4][kSmallRows];   // per-wave row maxima (FP8: then row sums)
+  __shared__ float lsum[4][kSmallRows];  // per-wave row sums of a piece's last page
   __shared__ int vote[4];                // per-wave restart votes
 
   const int lane = threadIdx.x & 63;
@@ -794,6 +795,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(MLA_SPLITKV_H
 
     f32x4 o[8];
     float m_ref = -INFINITY, l_run = 0.f;
+    float l_tot = 0.f;   // the row's sum over the four waves
     // Q^T fragments (B operand): row c16, dims 32 ks + 8 g .. + 7.  Q is
     // copied once per workgroup, into slice 0 of stage 1, ahead of the first
     // page: wave w copies the 1 KiB pieces w, w + 4, ... of it (a CU moves its
@@ -1011,6 +1013,14 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(MLA_SPLITKV_H
           pk[v] = __builtin_bit_cast(short, (__bf16)pe);
         }
         *(LDS_PTR(i16x4))(pb + pw_off) = pk;
+        // bf16 pages: the last page's row sums travel with its probabilities,
+        // so the epilogue needs no exchange of its own (0.3 us of the
+        // memory-bound step in an A/B; with FP8 records 0.1 us slower, so
+        // that kernel keeps the exchange in its epilogue).
+        if (!kFp8 && j == hi - 1) {
+          const float lw = row_sum4(l_run);
+          if (g == 0) lsum[wave][c16] = lw;
+        }
         // A row max more than 2^64 above the reference: every wave redoes the
         // piece with the exact maxima (first attempt only, so at most twice).
         if (attempt == 0) {
@@ -1019,6 +1029,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(MLA_SPLITKV_H
         }
         lds_barrier();   // every wave's probabilities (and vote) are in LDS
         if (attempt == 0) restart |= (vote[0] | vote[1] | vote[2] | vote[3]) != 0;
+        if (!kFp8 && j == hi - 1) l_tot = (lsum[0][c16] + lsum[1][c16]) + (lsum[2][c16] + lsum[3][c16]);
 
         // ---- O^T (this wave's 128 columns x 16 rows) += V^T P^T, two steps of
         // 32 tokens, 8 column tiles each.
@@ -1078,18 +1089,21 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(MLA_SPLITKV_H
       lds_barrier();   // red is read before it is written again
     }
 
-    // ---- epilogue: row sums over the four waves; each wave stores its columns.
-    const float lw = row_sum4(l_run);
-    lds_barrier();   // every wave is done with red, the P buffer and the stages
-    if (g == 0) red[wave][c16] = lw;
-    lds_barrier();
-    const float l_tot = (red[0][c16] + red[1][c16]) + (red[2][c16] + red[3][c16]);
+    // ---- epilogue: row sums over the four waves (bf16 pages: already known);
+    // each wave stores its columns.
+    if constexpr (kFp8) {
+      const float lw = row_sum4(l_run);
+      lds_barrier();   // every wave is done with red
+      if (g == 0) red[wave][c16] = lw;
+      lds_barrier();
+      l_tot = (red[0][c16] + red[1][c16]) + (red[2][c16] + red[3][c16]);
+    }
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse2 = l_tot > 0.f ? m_ref + __builtin_amdgcn_logf(l_tot) : -INFINITY;
     // In the O^T accumulator lane (g, c16) holds row c16, columns 4 g .. + 3 of the tile.
     if (!kFp8 && split) {
       // The partial goes out in whole 128-byte lines: this wave's 16 rows x
-      // 128 columns pass through the free stage (rows 528 bytes apart, so a
+      // 128 columns pass through a free stage (rows 528 bytes apart, so a
       // write's 16 rows fall on distinct banks) and each store covers two
       // rows.  Stored straight from the accumulator layout, a store writes
       // 64-byte halves of 16 lines, which the nontemporal path does not merge
@@ -1097,7 +1111,10 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(MLA_SPLITKV_H
       // workload); staged, the step went from 19.2 to 18.3 us in an A/B with
       // bitwise the same output.  (FP8 records: 18.1 against 18.3 us the
       // other way round, so that kernel keeps the direct stores.)
-      LDS_PTR(unsigned char) stg = lds + wave * (kSmallRows * kSmallStageRow);
+      // (in the stage that does not hold the last page: other waves may
+      // still be reading that one)
+      LDS_PTR(unsigned char) stg =
+          lds + (((hi - 1 - lo) & 1) ? 0 : kPageBytes) + wave * (kSmallRows * kSmallStageRow);
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct)
         *(LDS_PTR(f32x4))(stg + c16 * kSmallStageRow + (16 * ct + 4 * g) * 4) = o[ct] * inv;
