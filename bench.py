@@ -246,15 +246,23 @@ def time_steps(step, rot: int, steps: int, warmup: int):
     clock = CLOCK.stop() if CLOCK is not None else None
     clock_spread = CLOCK.spread() if CLOCK is not None else None
     per_step = np.array([a.elapsed_time(b) / steps for a, b in per])
-    # --- per-kernel durations, eager calls behind a warm replay
-    with torch.cuda.stream(s):
-        graph.replay()
-        mla.profile_start(steps)
-        for i in range(steps):
-            step(i % rot)
-        main_ms, comb_ms, calls = mla.profile_stop()
-    torch.cuda.synchronize()
-    assert calls == steps, (calls, steps)
+    # --- per-kernel durations: eager calls behind a warm replay, five blocks
+    # of `steps` calls; the median of the blocks' means (one slow block, e.g.
+    # a clock change, does not move it)
+    blocks = []
+    for _ in range(5):
+        with torch.cuda.stream(s):
+            graph.replay()
+            mla.profile_start(steps)
+            for i in range(steps):
+                step(i % rot)
+            main_ms, comb_ms, calls = mla.profile_stop()
+        torch.cuda.synchronize()
+        assert calls == steps, (calls, steps)
+        blocks.append((main_ms / calls, comb_ms / calls))
+    main_ms = float(np.median([b[0] for b in blocks])) * steps
+    comb_ms = float(np.median([b[1] for b in blocks])) * steps
+    calls = steps
     del graph
     t0 = time.perf_counter()
     for i in range(steps):
