@@ -1879,9 +1879,10 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(MLA_SPLITKV_HO
 // M = max lse_i, w_i = 2^(lse_i - M), out = sum w_i O_i / sum w_i,
 // lse = M + log2(sum w_i) (then converted to natural log).  Rows of requests
 // that are not split are skipped (the main kernel wrote them).
-//   Each lane owns 8 consecutive columns and issues the loads of a chunk of
-// splits at once (two 16-byte loads each), so a wave pays one memory round
-// trip per chunk.  The chunk is the smallest of 2, 4 and kCombineChunk that
+//   Each lane owns columns 4 l .. 4 l + 3 and 256 + 4 l .. + 3 (so each of
+// a split's two loads reads 1 KB in one piece: 0.44 us of the memory-bound
+// step against 8 consecutive columns a lane) and issues the loads of a chunk
+// of splits at once, so a wave pays one memory round trip per chunk.  The chunk is the smallest of 2, 4 and kCombineChunk that
 // holds all of the wave's splits (the last chunk's missing entries repeat
 // the last split with weight 0, so a smaller chunk issues fewer such loads:
 // measured 0.4 us of the memory-bound step, 14 splits a pair over 4 waves).  If no request has more than kCombineChunk
@@ -1906,7 +1907,7 @@ __device__ __forceinline__ void combine_chunks(const float* lrow, const float* o
       const int i = first + step * min(k0 + u, count - 1);   // clamped: duplicates get weight 0 below
       li[u] = ld_broadcast(lrow + (size_t)i * lstride);
       b0[u] = *(const f32x4*)(orow + (size_t)i * ostride);
-      b1[u] = *(const f32x4*)(orow + (size_t)i * ostride + 4);
+      b1[u] = *(const f32x4*)(orow + (size_t)i * ostride + kDv / 2);
     }
     float Mc = M;
 #pragma unroll
@@ -1943,14 +1944,15 @@ __device__ __forceinline__ void combine_splits(const float* lrow, const float* o
 __device__ __forceinline__ void combine_store(const Params& p, int req, int row, int lane, float M, float l, f32x4 a0,
                                               f32x4 a1) {
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  unsigned short* o = p.out + ((size_t)req * p.R + row) * kDv + lane * 8;
-  u32x4 w;
+  unsigned short* o = p.out + ((size_t)req * p.R + row) * kDv + lane * 4;
+  u32x2 w0, w1;
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    w[e] = (unsigned)f32_to_bf16(a0[2 * e] * inv) | ((unsigned)f32_to_bf16(a0[2 * e + 1] * inv) << 16);
-    w[2 + e] = (unsigned)f32_to_bf16(a1[2 * e] * inv) | ((unsigned)f32_to_bf16(a1[2 * e + 1] * inv) << 16);
+    w0[e] = (unsigned)f32_to_bf16(a0[2 * e] * inv) | ((unsigned)f32_to_bf16(a0[2 * e + 1] * inv) << 16);
+    w1[e] = (unsigned)f32_to_bf16(a1[2 * e] * inv) | ((unsigned)f32_to_bf16(a1[2 * e + 1] * inv) << 16);
   }
-  *(u32x4*)o = w;
+  *(u32x2*)o = w0;
+  *(u32x2*)(o + kDv / 2) = w1;
   if (lane == 0) p.lse[lse_index(p, req, row)] = l > 0.f ? (M + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
 }
 
@@ -1992,7 +1994,7 @@ __global__ void __launch_bounds__(kCombineWaves * 64) mla_combine_kernel(MLA_COM
       if (n <= 1) continue;   // uniform over the wave
       float M = -INFINITY, l = 0.f;
       f32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
-      combine_splits(p.lacc + (size_t)slot0 * p.R + row, p.oacc + ((size_t)slot0 * p.R + row) * kDv + lane * 8, p.R,
+      combine_splits(p.lacc + (size_t)slot0 * p.R + row, p.oacc + ((size_t)slot0 * p.R + row) * kDv + lane * 4, p.R,
                      ostride, 0, 1, n, M, l, a0, a1);
       combine_store(p, req, row, lane, M, l, a0, a1);
     }
@@ -2008,7 +2010,7 @@ __global__ void __launch_bounds__(kCombineWaves * 64) mla_combine_kernel(MLA_COM
     const int nw = (n - wave + kCombineWaves - 1) / kCombineWaves;   // this wave's splits
     float M = -INFINITY, l = 0.f;
     f32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
-    combine_splits(p.lacc + (size_t)slot0 * p.R + row, p.oacc + ((size_t)slot0 * p.R + row) * kDv + lane * 8, p.R,
+    combine_splits(p.lacc + (size_t)slot0 * p.R + row, p.oacc + ((size_t)slot0 * p.R + row) * kDv + lane * 4, p.R,
                    ostride, wave, kCombineWaves, nw, M, l, a0, a1);
     red_o[wave][0][lane] = a0;
     red_o[wave][1][lane] = a1;
