@@ -1879,17 +1879,18 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(MLA_SPLITKV_HO
 // M = max lse_i, w_i = 2^(lse_i - M), out = sum w_i O_i / sum w_i,
 // lse = M + log2(sum w_i) (then converted to natural log).  Rows of requests
 // that are not split are skipped (the main kernel wrote them).
-//   Each lane owns columns 4 l .. 4 l + 3 and 256 + 4 l .. + 3 (so each of
-// a split's two loads reads 1 KB in one piece: 0.44 us of the memory-bound
-// step against 8 consecutive columns a lane) and issues the loads of a chunk
-// of splits at once, so a wave pays one memory round trip per chunk.  The chunk is the smallest of 2, 4 and kCombineChunk that
-// holds all of the wave's splits (the last chunk's missing entries repeat
-// the last split with weight 0, so a smaller chunk issues fewer such loads:
-// measured 0.4 us of the memory-bound step, 14 splits a pair over 4 waves).  If no request has more than kCombineChunk
-// pieces (the schedule table says), each wave merges one (request, row) pair
-// on its own (many short merges: no LDS, no barrier); otherwise a workgroup
-// merges one pair, wave w taking splits w, w + 4, ..., and the four states
-// meet in LDS (few long merges).
+//   Each lane owns columns 4 l .. 4 l + 3 and 256 + 4 l .. + 3, so each of
+// a split's two loads reads 1 KB in one piece (0.44 us of the memory-bound
+// step against 8 consecutive columns a lane), and issues the loads of a
+// chunk of splits at once, so a wave pays one memory round trip per chunk.
+// The chunk is the smallest of 2, 4 and kCombineChunk that holds all of the
+// wave's splits (the last chunk's missing entries repeat the last split with
+// weight 0, so a smaller chunk issues fewer such loads: 0.4 us of the
+// memory-bound step, 14 splits a pair over 4 waves).  If no request has more
+// than kCombineChunk pieces (the schedule table says), each wave merges one
+// (request, row) pair on its own (many short merges: no LDS, no barrier);
+// otherwise a workgroup merges one pair, wave w taking splits w, w + 4, ...,
+// and the four states meet in LDS (few long merges).
 constexpr int kCombineWaves = 4;
 constexpr int kCombineChunk = 8;
 
