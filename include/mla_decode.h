@@ -66,7 +66,10 @@ enum {
  * ceil(sum_b (n_b + F) / num_parts) + F; requests are walked in order and
  * each part is filled up to the payload, a request that does not fit being
  * cut at a block boundary (every piece costs its blocks plus F).  The last
- * part takes whatever remains.  force_splits > 0 instead cuts every request
+ * part takes whatever remains.  Then (a step of our own, not the page's)
+ * each run of consecutive parts that hold one request alone shares that run's
+ * blocks evenly, earlier parts one block longer; parts, piece indices and
+ * split counts stay the walk's.  force_splits > 0 instead cuts every request
  * into min(force_splits, n_b) (at least 1) page-aligned pieces, one part each.
  *
  *   cache_seqlens  host int32 [batch], each >= 0

@@ -22,6 +22,15 @@ Readings taken where the page is silent:
     into min(k, n_b) page-aligned pieces (at least one), earlier pieces one
     block longer when n_b is not a multiple, one part per piece.
 
+After the walk, a step that is not on the page (the GPU library's planner
+takes it too, because it measured faster on MI355X): the walk leaves a long
+request in pieces of payload - F blocks and one shorter last piece.  Each
+maximal run of consecutive parts that hold a piece of one request and nothing
+else has its blocks dealt out again as evenly as possible, earlier parts one
+block longer when the count does not divide (``_even_runs``).  Parts, piece
+indices and split counts are the walk's; only block boundaries inside a run
+move, so no part's load grows past the longest piece the walk made.
+
 Output layout (shared with the GPU library's planner, which must agree bit
 for bit): one row of 8 int32 per part
   [begin_req, end_req (inclusive), begin_block (in begin_req),
@@ -42,8 +51,10 @@ def blocks_of(seqlens) -> list[int]:
     return [(int(L) + PAGE - 1) // PAGE for L in seqlens]
 
 
-def plan(seqlens, num_parts: int, fixed_overhead: int = 0, force_splits: int = 0):
+def plan(seqlens, num_parts: int, fixed_overhead: int = 0, force_splits: int = 0, even: bool = True):
     """Return (sched int32 [parts, 8], num_splits int32 [b + 1]).
+
+    ``even=False`` returns the page's walk alone, without the evening step.
 
     A row is [begin_req, end_req, begin_block, end_block, begin_piece,
     max_pieces, 0, 0]; max_pieces (the same in every row) is the largest
@@ -84,9 +95,31 @@ def plan(seqlens, num_parts: int, fixed_overhead: int = 0, force_splits: int = 0
         if end_req < 0:                              # nothing fitted: close the walk
             continue
         parts.append([begin[0], end_req, begin[1], end_blk, begin[2], 0, 0, 0])
+    if even:
+        _even_runs(parts)
     num_splits = np.zeros(b + 1, dtype=np.int32)
     num_splits[1:] = np.cumsum(pieces)
     return _with_max_pieces(np.array(parts, dtype=np.int32).reshape(-1, SCHED_INTS), pieces), num_splits
+
+
+def _even_runs(parts) -> None:
+    """Deal the blocks of each run of single-request parts out evenly (in place)."""
+    alone = [row[0] == row[1] for row in parts]
+    p = 0
+    while p < len(parts):
+        if not alone[p]:
+            p += 1
+            continue
+        q = p + 1
+        while q < len(parts) and alone[q] and parts[q][0] == parts[p][0]:
+            q += 1
+        start, end, k = parts[p][2], parts[q - 1][3], q - p
+        sizes = [(end - start) // k + (1 if i < (end - start) % k else 0) for i in range(k)]
+        at = start
+        for i in range(k):
+            parts[p + i][2], parts[p + i][3] = at, at + sizes[i]
+            at += sizes[i]
+        p = q
 
 
 def _with_max_pieces(sched: np.ndarray, pieces) -> np.ndarray:

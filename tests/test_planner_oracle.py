@@ -73,6 +73,52 @@ def test_empty_requests_are_placed():
     assert sched.tolist() == [[0, 1, 0, 2, 0, 2, 0, 0], [1, 3, 2, 0, 1, 2, 0, 0]]
 
 
+def test_hand_worked_even_runs_at_h128_geometry():
+    # 4 requests of 64 blocks, 16 parts, F = 4: total = 4 * 68 = 272, payload = 17 + 4 = 21.
+    # The walk gives every request 17 + 17 + 17 + 13 blocks (the 13-block rest costs 17 <= 21
+    # and leaves 4, too little for 4 - F = 0 blocks of the next request).  Each request's four
+    # parts hold it alone, so the evening step deals its 64 blocks out as 4 x 16.
+    raw, ns_raw = oracle.plan([64 * 64] * 4, num_parts=16, fixed_overhead=4, even=False)
+    assert [(int(r[2]), int(r[3])) for r in raw[:4]] == [(0, 17), (17, 34), (34, 51), (51, 64)]
+    sched, ns = oracle.plan([64 * 64] * 4, num_parts=16, fixed_overhead=4)
+    assert sched.tolist() == [[r, r, 16 * i, 16 * i + 16, i, 4, 0, 0] for r in range(4) for i in range(4)]
+    assert ns.tolist() == ns_raw.tolist() == [0, 4, 8, 12, 16]
+
+
+def test_hand_worked_even_run_after_a_shared_part():
+    # n = {1, 9}, 3 parts, F = 0: payload = ceil(10 / 3) = 4.  Part 0 takes request 0 (1 block)
+    # and blocks 0..2 of request 1; part 1 takes 4 more (3..6), the last part the rest (7, 8).
+    # Part 0 holds two requests and keeps its cut; parts 1 and 2 hold request 1 alone and
+    # share its blocks 3..8 evenly: 3..5 and 6..8.
+    raw, _ = oracle.plan([64, 576], num_parts=3, even=False)
+    assert raw.tolist() == [[0, 1, 0, 3, 0, 3, 0, 0], [1, 1, 3, 7, 1, 3, 0, 0], [1, 1, 7, 9, 2, 3, 0, 0]]
+    sched, ns = oracle.plan([64, 576], num_parts=3)
+    assert sched.tolist() == [[0, 1, 0, 3, 0, 3, 0, 0], [1, 1, 3, 6, 1, 3, 0, 0], [1, 1, 6, 9, 2, 3, 0, 0]]
+    assert ns.tolist() == [0, 1, 4]
+
+
+def check_even_against_walk(seqlens, P, F):
+    """The evening step moves only block boundaries between consecutive parts that hold one
+    request alone; inside such a run the sizes are the even split, longest first."""
+    raw, ns_raw = oracle.plan(seqlens, num_parts=P, fixed_overhead=F, even=False)
+    sched, ns = oracle.plan(seqlens, num_parts=P, fixed_overhead=F)
+    assert sched.shape == raw.shape and ns.tolist() == ns_raw.tolist()
+    assert (sched[:, [0, 1, 4, 5, 6, 7]] == raw[:, [0, 1, 4, 5, 6, 7]]).all()
+    alone = raw[:, 0] == raw[:, 1]
+    assert (sched[~alone] == raw[~alone]).all()
+    p = 0
+    while p < len(raw):
+        q = p + 1
+        while alone[p] and q < len(raw) and alone[q] and raw[q, 0] == raw[p, 0]:
+            q += 1
+        sizes = (sched[p:q, 3] - sched[p:q, 2]).tolist()
+        assert sched[p, 2] == raw[p, 2] and sched[q - 1, 3] == raw[q - 1, 3]
+        assert (sched[p + 1:q, 2] == sched[p:q - 1, 3]).all()
+        assert max(sizes) - min(sizes) <= 1 and sizes == sorted(sizes, reverse=True)
+        assert max(sizes) <= max((raw[p:q, 3] - raw[p:q, 2]).tolist())
+        p = q
+
+
 @pytest.mark.parametrize("seed", range(40))
 def test_random_plans_are_valid(seed):
     rng = np.random.default_rng(seed)
@@ -91,6 +137,7 @@ def test_random_plans_are_valid(seed):
     F = int(rng.integers(0, 6))
     sched, ns = oracle.plan(seqlens, num_parts=P, fixed_overhead=F)
     check_plan_valid(seqlens, sched, ns, P, F)
+    check_even_against_walk(seqlens, P, F)
     fk = int(rng.integers(1, 5))
     sched, ns = oracle.plan(seqlens, num_parts=P, force_splits=fk)
     check_plan_valid(seqlens, sched, ns, greedy=False)
