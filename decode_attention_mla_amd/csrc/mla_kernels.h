@@ -2046,9 +2046,10 @@ __global__ void __launch_bounds__(kCombineWaves * 64) mla_combine_kernel(MLA_COM
 // Scheduler: the pages run their planner as a one-warp kernel), so that a
 // captured decode step can replan from lengths that change on the device.
 // It produces the host planner's table (planner.cpp: same payload rule, same
-// greedy walk, same evening of single-request runs), then empty rows (begin_req = 1 > end_req = 0, which every
-// split-KV kernel skips) up to num_parts, column 5 = the largest piece count
-// in every row, and the per-request prefix of pieces.
+// greedy walk, same evening of single-request runs), then empty rows
+// (begin_req = 1 > end_req = 0, which every split-KV kernel skips) up to
+// num_parts, column 5 = the largest piece count in every row, and the
+// per-request prefix of pieces.
 //   The walk is not stepped part by part.  One wave holds 64 requests at a
 // time; a ballot over the in-chunk prefix of costs (n_b + F) places the whole
 // run of requests that fit in the capacity left, and a request that does not
