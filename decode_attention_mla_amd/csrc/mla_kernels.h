@@ -1324,7 +1324,11 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_kernel(MLA_SPLITKV_HOT_ARG
     }
     // In the O^T accumulator lane l holds row n = l % 32 and, in element
     // 4 i + e, column 32 ct + 8 i + 4 (l / 32) + e.
-    const int n = lane & 31;
+    // (From a lane index read here, so that the compiler does not compute
+    // the epilogue's store addresses ahead of the piece loop and keep them
+    // in scratch: the page loop leaves no registers free.)
+    const int le = fresh_lane_id();
+    const int n = le & 31;
     const int row = row0 + n;
     float wgt[4], inv = 0.f, lse2 = 0.f;
 #pragma unroll
@@ -1352,12 +1356,16 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_kernel(MLA_SPLITKV_HOT_ARG
           for (int w = 0; w < 4; ++w)
             acc += wgt[w] * *(LDS_PTR(f32x4))((LDS_PTR(unsigned char))smem + w * 2 * kStageBytes +
                                               ((k * 4 + q4) * 64 + lane) * 16);
-          if (row < p.R) store_cols4(p, req, row, split, slot, 32 * ct + 8 * q4 + 4 * (lane >> 5), acc * inv);
+          if (row < p.R) store_cols4(p, req, row, split, slot, 32 * ct + 8 * q4 + 4 * (le >> 5), acc * inv);
         }
       }
       lds_barrier();   // the parked tiles are read; the stages may be reused
     }
-    if (wave == 0 && lane < 32 && row < p.R) store_lse(p, req, row, split, slot, lse2);
+    if (wave == 0 && le < 32 && row < p.R) {
+      Params pe = p;   // h_q through an opaque copy: its division constant is not kept from the kernel start
+      asm volatile("s_mov_b32 %0, %1" : "=s"(pe.h_q) : "s"(p.h_q));
+      store_lse(pe, req, row, split, slot, lse2);
+    }
   }
 }
 
@@ -1851,24 +1859,32 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(MLA_SPLITKV_HO
     lds_barrier();   // every wave is done with the P buffer
     if (h == 0) *(LDS_PTR(float))(pb + (wave * 32 + n) * 4) = inv;
     lds_barrier();
+    // (The store addresses are derived from a lane index read here, so that
+    // the compiler does not compute them once ahead of the piece loop and
+    // keep them in scratch: the page loop leaves no registers free.)
+    const int le = fresh_lane_id(), ne = le & 31, he = le >> 5;
+    Params pe = p;   // R and h_q through opaque copies: nothing derived from them is kept from the kernel start
+    asm volatile("s_mov_b32 %0, %1" : "=s"(pe.h_q) : "s"(p.h_q));
+    asm volatile("s_mov_b32 %0, %1" : "=s"(pe.R) : "s"(p.R));
     float inv_rows[kWideTiles];
 #pragma unroll
-    for (int a = 0; a < kWideTiles; ++a) inv_rows[a] = *(LDS_PTR(float))(pb + (a * 32 + n) * 4);
+    for (int a = 0; a < kWideTiles; ++a) inv_rows[a] = *(LDS_PTR(float))(pb + (a * 32 + ne) * 4);
 #pragma unroll
     for (int a = 0; a < kWideTiles; ++a) {
-      const int ra = row0 + 32 * a + n;
-      if (ra >= p.R) continue;
+      const int ra = row0 + 32 * a + ne;
+      if (ra >= pe.R) continue;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int ct = 4 * wave + c;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          store_cols4(p, req, ra, split, slot, 32 * ct + 8 * i + 4 * h,
+          store_cols4(pe, req, ra, split, slot, 32 * ct + 8 * i + 4 * he,
                       f32x4{o[a][c][4 * i], o[a][c][4 * i + 1], o[a][c][4 * i + 2], o[a][c][4 * i + 3]} *
                           inv_rows[a]);
       }
     }
-    if (h == 0 && row_ok) store_lse(p, req, r, split, slot, lse2);
+    const int re = row0 + 32 * wave + ne;
+    if (he == 0 && re < pe.R) store_lse(pe, req, re, split, slot, lse2);
     lds_barrier();   // the 1 / l table is read; the next piece may reuse the buffers
   }
 }
