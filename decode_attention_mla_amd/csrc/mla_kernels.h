@@ -1445,15 +1445,23 @@ struct WideSoftmax {
 // the softmax.  The compiler does not see inside the statement, so the code
 // around it keeps the hazard distances itself: operands come from LDS reads
 // (waited for by the compiler's counters) and reads of the accumulator are
-// preceded by wide_acc_settle().
-__device__ __forceinline__ void pv_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+// preceded by wide_acc_settle().  The operands are passed as 32-bit words:
+// as bf16 vectors the compiler sometimes rebuilt a fragment with v_perm or
+// v_bfi right before the statement, and an MFMA that reads a VGPR a VALU op
+// has just written needs two wait states that nothing here would insert
+// (the compiler's hazard checks do not look inside the statement; a build
+// with a fifth K fragment in flight read stale operands that way).
+__device__ __forceinline__ void pv_mfma(f32x16& acc, const u32x4& a, const u32x4& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 // S^T tiles in architectural VGPRs (so they never compete with O for the
-// accumulation registers); the first step of a tile starts from zero.
-__device__ __forceinline__ void qk_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b, bool first) {
+// accumulation registers); the first step of a tile starts from zero.  Its
+// result is an early-clobber output: a 16-register MFMA result must not
+// overlap the instruction's own A or B operand (the compiler's definitions
+// of these MFMAs carry the same constraint).
+__device__ __forceinline__ void qk_mfma(f32x16& acc, const u32x4& a, const u32x4& b, bool first) {
   if (first)
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
   else
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
@@ -1565,15 +1573,19 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(MLA_SPLITKV_HO
           issue_stage<kStream>(page_rows(m.blk[0]), lds0 + wave * kStageBytes, dma_off);
       }
       // Q^T fragments (B operand): row r, dims 16 ks + 8 h .. + 7.
-      bf16x8 qf[kQkSteps16];
+      u32x4 qf[kQkSteps16];
       {
-        const unsigned char* qrow = p.q + ((size_t)req * p.R + (row_ok ? r : 0)) * kRowBytes + h * 16;
-        const unsigned keep = row_ok ? ~0u : 0u;
+        // (the row address from a lane index read here: kept from the kernel
+        // start, it would be spilled with the page loop's registers in use)
+        const int lq = fresh_lane_id(), rq = row0 + 32 * wave + (lq & 31);
+        const bool okq = rq < p.R;
+        const unsigned char* qrow = p.q + ((size_t)req * p.R + (okq ? rq : 0)) * kRowBytes + (lq >> 5) * 16;
+        const unsigned keep = okq ? ~0u : 0u;
 #pragma unroll
         for (int ks = 0; ks < kQkSteps16; ++ks) {
           u32x4 v = *(const u32x4*)(qrow + ks * 32);
           v &= keep;
-          qf[ks] = __builtin_bit_cast(bf16x8, v);
+          qf[ks] = v;
         }
       }
       // Q and the first page (a wait the compiler sees, so it inserts none
@@ -1757,10 +1769,9 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(MLA_SPLITKV_HO
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           auto kread = [&](int ks) {
-            return __builtin_bit_cast(bf16x8,
-                                      *(LDS_PTR(u32x4))(buf + 2 * tt * kStageBytes + (ks >> 2) * kStageBlock + kq[ks & 3]));
+            return *(LDS_PTR(u32x4))(buf + 2 * tt * kStageBytes + (ks >> 2) * kStageBlock + kq[ks & 3]);
           };
-          bf16x8 kf[kWideQkLead];
+          u32x4 kf[kWideQkLead];
 #pragma unroll
           for (int i = 0; i < kWideQkLead; ++i) kf[i] = kread(i);
           __builtin_amdgcn_sched_barrier(0);
@@ -1799,12 +1810,12 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(MLA_SPLITKV_HO
           auto vread = [&](int s) {
             const int ct = 4 * wave + (s & 3);
             LDS_PTR(unsigned char) a = buf + (kk0 + (s >> 2)) * kStageBytes + (ct >> 1) * kStageBlock;
-            const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv[0][ct & 1]));
-            const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv[1][ct & 1]));
-            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+            const u32x2 a0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv[0][ct & 1])));
+            const u32x2 a1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv[1][ct & 1])));
+            return u32x4{a0[0], a0[1], a1[0], a1[1]};
           };
-          bf16x8 pf[kWideTiles], vf[2];
-          auto pread = [&](int i, int a) { pf[a] = *(LDS_PTR(bf16x8))(pb + ((a * 4 + kk0 + i) * 64 + lane) * 16); };
+          u32x4 pf[kWideTiles], vf[2];
+          auto pread = [&](int i, int a) { pf[a] = *(LDS_PTR(u32x4))(pb + ((a * 4 + kk0 + i) * 64 + lane) * 16); };
 #pragma unroll
           for (int a = 0; a < kWideTiles; ++a) pread(0, a);
           vf[0] = vread(0);
@@ -1856,13 +1867,13 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(MLA_SPLITKV_HO
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse2 = l_tot > 0.f ? m_ref + __builtin_amdgcn_logf(l_tot) : -INFINITY;
-    lds_barrier();   // every wave is done with the P buffer
-    if (h == 0) *(LDS_PTR(float))(pb + (wave * 32 + n) * 4) = inv;
-    lds_barrier();
-    // (The store addresses are derived from a lane index read here, so that
-    // the compiler does not compute them once ahead of the piece loop and
-    // keep them in scratch: the page loop leaves no registers free.)
+    // (The LDS and store addresses are derived from a lane index read here,
+    // so that the compiler does not compute them once ahead of the piece loop
+    // and keep them in scratch: the page loop leaves no registers free.)
     const int le = fresh_lane_id(), ne = le & 31, he = le >> 5;
+    lds_barrier();   // every wave is done with the P buffer
+    if (he == 0) *(LDS_PTR(float))(pb + (wave * 32 + ne) * 4) = inv;
+    lds_barrier();
     Params pe = p;   // R and h_q through opaque copies: nothing derived from them is kept from the kernel start
     asm volatile("s_mov_b32 %0, %1" : "=s"(pe.h_q) : "s"(p.h_q));
     asm volatile("s_mov_b32 %0, %1" : "=s"(pe.R) : "s"(p.R));

@@ -1,0 +1,108 @@
+"""Properties of the gfx950 device code that the hardware needs and the
+compiler cannot check (CPU test: hipcc cross-compiles the device assembly).
+
+The 128-row kernel issues its MFMAs as inline assembly, so the compiler's
+hazard recognizer does not see them:
+  * a VALU instruction that writes a VGPR an MFMA then reads (A, B or C
+    operand) needs two wait states before the MFMA (it would read the stale
+    value otherwise);
+  * a 16-register MFMA result must not overlap the same instruction's A or B
+    operand.
+Both are checked on every inline MFMA of every kernel.  Also recorded: the
+per-lane scratch of each kernel (no split-KV kernel spills inside a page loop;
+only the sparse FP8 form of the 128-row kernel keeps a few piece-level values).
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from decode_attention_mla_amd import build
+
+HIPCC = shutil.which("hipcc") or ("/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else None)
+pytestmark = pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("isa") / "mla.s")
+    flags = [f for f in build.HIP_FLAGS if f not in ("-shared", "-fPIC")]
+    cmd = [HIPCC, *flags, "-I", os.path.join(build.PKG_DIR, "..", "include"), "-S", "--offload-device-only",
+           os.path.join(build.CSRC, "mla_decode.hip"), "-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    return open(out).read().split("\n")
+
+
+def _regs(text):
+    out = set()
+    for m in re.finditer(r"\b([va])\[(\d+):(\d+)\]", text):
+        out |= {(m.group(1), r) for r in range(int(m.group(2)), int(m.group(3)) + 1)}
+    for m in re.finditer(r"\b([va])(\d+)\b", text):
+        out.add((m.group(1), int(m.group(2))))
+    return out
+
+
+def _inline_mfmas(lines):
+    """(kernel, line index, instruction) of every MFMA inside inline assembly."""
+    kern, inside = None, False
+    for i, line in enumerate(lines):
+        if re.match(r"^_Z\S+:", line):
+            kern = line.split(":")[0]
+        t = line.strip()
+        if t.startswith(";;#ASMSTART"):
+            inside = True
+        elif t.startswith(";;#ASMEND"):
+            inside = False
+        elif inside and t.startswith("v_mfma"):
+            yield kern, i, t
+
+
+def test_inline_mfmas_present(asm):
+    kernels = {k for k, _, _ in _inline_mfmas(asm)}
+    assert sum("splitkv_wide_kernel" in k for k in kernels) == 8, kernels
+
+
+def test_no_valu_write_feeds_inline_mfma(asm):
+    bad = []
+    for kern, i, ins in _inline_mfmas(asm):
+        srcs = _regs(",".join(ins.split(None, 1)[1].split(",")[1:]))
+        k, ws = i - 1, 0
+        while k >= 0 and ws < 2:
+            u = asm[k].strip()
+            k -= 1
+            if not u or u.startswith(";") or u.startswith("."):
+                continue
+            m = re.match(r"s_nop\s+(\d+)", u)
+            if m:
+                ws += int(m.group(1)) + 1
+                continue
+            ws += 1
+            if u.startswith("v_") and not u.startswith("v_mfma"):
+                parts = u.split(None, 1)
+                if len(parts) > 1 and _regs(parts[1].split(",")[0]) & srcs:
+                    bad.append((kern[:60], u, ins))
+    assert not bad, bad[:5]
+
+
+def test_inline_mfma_result_does_not_overlap_sources(asm):
+    bad = []
+    for kern, _, ins in _inline_mfmas(asm):
+        ops = [o.strip() for o in ins.split(None, 1)[1].split(",")]
+        if _regs(ops[0]) & (_regs(ops[1]) | _regs(ops[2])):
+            bad.append((kern[:60], ins))
+    assert not bad, bad[:5]
+
+
+def test_scratch_per_kernel(asm):
+    text = "\n".join(asm)
+    sizes = dict(re.findall(r"\.name:\s+(\S+)\n\s+\.private_segment_fixed_size:\s+(\d+)", text))
+    assert sizes, "no kernel metadata found"
+    for name, size in sizes.items():
+        size = int(size)
+        if "splitkv_wide_kernelILb0ELb1ELb1E" in name or "splitkv_wide_kernelILb1ELb1ELb1E" in name:
+            assert size <= 32, (name, size)   # sparse FP8 128-row kernel: piece-level values only
+        else:
+            assert size == 0, (name, size)
