@@ -96,6 +96,31 @@ def test_inline_mfma_result_does_not_overlap_sources(asm):
     assert not bad, bad[:5]
 
 
+def test_no_scratch_access_in_a_page_loop(asm):
+    """Spilled values, where a kernel has any, are read outside the page loop
+    (the deepest loop that issues MFMAs)."""
+    kern, depth, blocks = None, 0, {}
+    for line in asm:
+        m = re.match(r"^(_Z\S+):", line)
+        if m:
+            kern, depth = m.group(1), 0
+            continue
+        if kern is None or "splitkv" not in kern:
+            continue
+        t = line.strip()
+        if t.startswith(".LBB") or t.startswith("; %bb"):
+            d = re.search(r"Depth=(\d+)", t)
+            depth = int(d.group(1)) if d else 0
+        k = blocks.setdefault(kern, {"mfma": 0, "scratch": []})
+        if t.startswith("v_mfma"):
+            k["mfma"] = max(k["mfma"], depth)
+        elif t.startswith("scratch_"):
+            k["scratch"].append((depth, t))
+    assert blocks
+    bad = [(n[:60], d, t) for n, k in blocks.items() for d, t in k["scratch"] if d >= k["mfma"]]
+    assert not bad, bad[:5]
+
+
 def test_scratch_per_kernel(asm):
     text = "\n".join(asm)
     sizes = dict(re.findall(r"\.name:\s+(\S+)\n\s+\.private_segment_fixed_size:\s+(\d+)", text))
