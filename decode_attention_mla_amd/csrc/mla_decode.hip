@@ -260,10 +260,21 @@ static const void* pick_main_kernel(const Geometry& g) {
                            : (const void*)mla_splitkv_wide_kernel<false, kSparse, kFp8>;
 }
 
+// The small-row kernel's split partials (fp32, 2 KB a row) go out with the
+// nontemporal hint only when there are many of them: written as plain stores
+// they wait in L2 for the end-of-kernel write-back, which costs more than the
+// combine then saves on reading them once they are megabytes (memory-bound
+// workload, ~7.7 MB at most: 17.7 us a step either way, within 0.1-0.3 us, in
+// A/Bs on one GPU), while a few hundred KB are written back quickly and read
+// sooner (tiny workload, 0.26 MB: 9.1 against 9.5 us a step bf16, 9.3 against
+// 9.8 us FP8).  The bound is the slots the plan can fill (parts + batch - 1).
+constexpr size_t kNtPartialBytes = 1u << 20;
+
 static int launch_decode(Params& prm, Geometry g, bool sparse, bool fp8, hipStream_t st, const char* who) {
   hipEvent_t* ev = profile_slot();
   const void* main_fn;
   prm.row_groups = g.row_groups;
+  prm.nt_partials = (size_t)(prm.num_parts + prm.batch - 1) * g.R * kDv * sizeof(float) > kNtPartialBytes ? 1 : 0;
   // (the leading scalar arguments: MLA_SPLITKV_HOT_ARGS, then Params)
   void* args[] = {&prm.sched,   &prm.num_parts,  &prm.row_groups, &prm.max_blocks, &prm.block_table,
                   &prm.seqlens, &prm.num_splits, &prm.kv,         &prm.q,          &prm};

@@ -94,6 +94,9 @@ struct Params {
   const int32_t* indices;      // [batch * fold, topk]: page_id * 64 + offset
   const int32_t* topk_len;     // [real batch]: entries of each list that count, or nullptr (all topk)
   int topk, kv_tokens, fold;
+  // Small-row kernel: split partials go out with the nontemporal hint (1) or
+  // as plain stores (0), chosen by the launch from the partials' size.
+  int nt_partials;
 };
 
 // Keys query row `row` (= s * h_q + h) sees in a request of length L: all L,
@@ -527,10 +530,9 @@ __device__ __forceinline__ void store_lse(const Params& p, int req, int row, boo
 
 // Four consecutive output columns c .. c + 3 of one row: bf16 to `out` when
 // the request is not split, else fp32 to the partial slot.  kNt: the partial
-// goes out with the nontemporal hint (measured in a graph of decode steps:
-// 0.25 us faster on the memory-bound workload's small kernel, whose 7 MB of
-// partials otherwise wait in L2 for the end-of-kernel writeback; 18-34 %
-// slower for the 128-row kernel's 67 MB, so that one keeps plain stores).
+// goes out with the nontemporal hint (the small kernel's choice for large
+// partial volumes, see nt_partials; 18-34 % slower for the 128-row kernel's
+// 67 MB, so that one keeps plain stores).
 template <bool kNt = false>
 __device__ __forceinline__ void store_cols4(const Params& p, int req, int row, bool split, int slot, int c, f32x4 v) {
   if (!split) {
@@ -1123,12 +1125,22 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_small_kernel(MLA_SPLITKV_H
       for (int i = 0; i < kSmallRows / 2; ++i) {
         const int rr = 2 * i + (lane >> 5), ch = lane & 31;
         const f32x4 v = *(LDS_PTR(f32x4))(stg + rr * kSmallStageRow + ch * 16);
-        if (rr < p.R)
-          __builtin_nontemporal_store(v, (f32x4*)(p.oacc + ((size_t)slot * p.R + rr) * kDv + 128 * wave + 4 * ch));
+        f32x4* dst = (f32x4*)(p.oacc + ((size_t)slot * p.R + rr) * kDv + 128 * wave + 4 * ch);
+        if (rr < p.R) {
+          if (p.nt_partials)
+            __builtin_nontemporal_store(v, dst);
+          else
+            *dst = v;
+        }
       }
     } else if (row_ok) {
+      if (p.nt_partials) {
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) store_cols4<true>(p, req, c16, split, slot, 128 * wave + 16 * ct + 4 * g, o[ct] * inv);
+        for (int ct = 0; ct < 8; ++ct) store_cols4<true>(p, req, c16, split, slot, 128 * wave + 16 * ct + 4 * g, o[ct] * inv);
+      } else {
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) store_cols4<false>(p, req, c16, split, slot, 128 * wave + 16 * ct + 4 * g, o[ct] * inv);
+      }
     }
     if (wave == 0 && g == 0 && row_ok) store_lse(p, req, c16, split, slot, lse2);
     lds_barrier();   // red is read; the next piece may reuse LDS
