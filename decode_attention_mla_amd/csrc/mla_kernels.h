@@ -151,6 +151,15 @@ __device__ __forceinline__ int fresh_lane_id() {
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+// A workgroup barrier that lets this wave's last N LDS operations (reads
+// issued just before it) stay in flight: LDS operations complete in order, so
+// with at most N outstanding every older one (the writes the barrier
+// publishes) is done, also when a scalar load is outstanding as well.
+template <int N>
+__device__ __forceinline__ void lds_barrier_reads_in_flight() {
+  static_assert(N > 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 __device__ __forceinline__ unsigned short f32_to_bf16(float f) {
   unsigned u = __float_as_uint(f);
@@ -1630,7 +1639,7 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(MLA_SPLITKV_HO
         }
         if constexpr (kSparse) {
           const unsigned keep = (unsigned)(mk_cur >> tok0) & 0xFFFFu;
-          if (keep != 0xFFFFu) zero_stage_rows(buf + wave * kStageBytes, keep, lane);
+          if (keep != 0xFFFFu) zero_stage_rows(buf + wave * kStageBytes, keep, fresh_lane_id());
         } else {
           const int valid = min(kPage, L - j * kPage);
           if (__builtin_expect(valid < kPage, 0)) zero_stage_tail(buf + wave * kStageBytes, valid - tok0, fresh_lane_id());
@@ -1808,46 +1817,58 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(MLA_SPLITKV_HO
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-        lds_barrier();   // every wave's tile-0 probabilities are in LDS
-        wide_acc_settle();   // tile 1's scores are read next
-
         // ---- O^T (this wave's 128 columns x 128 rows) += V^T P^T, one
         // 16-token step kk at a time; tile 1's softmax runs along kk = 0, 1.
-        // Two 16-token steps kk0, kk0 + 1 (8 groups of four MFMAs, one per
-        // row tile a, sharing a V^T fragment); the V^T fragments are read two
-        // groups ahead, each P^T fragment of the second step as soon as the
-        // last MFMA of the first step that uses its register is issued, and
-        // the softmax pieces (if any) sit between single MFMAs.
+        // Accumulator o[a][c] holds row tile (wave + a) % 4, so that a = 0 is
+        // the wave's own rows, whose P^T fragments it still holds in registers
+        // (the bytes it wrote to LDS): the four V^T fragments of a step are
+        // read before the barrier that publishes the probabilities (the page's
+        // V was visible since the page barrier), and the first four MFMAs after
+        // it need no LDS read, while the other row tiles' P^T fragments arrive.
+        // Within a step: row tile a, then column tile c; each V^T fragment of
+        // the next step is read once its last use in this step is issued, each
+        // P^T fragment likewise; the softmax pieces (if any) sit between single
+        // MFMAs.
+        auto vread = [&](int cl, int kk) {
+          const int ct = 4 * wave + cl;
+          LDS_PTR(unsigned char) a = buf + kk * kStageBytes + (ct >> 1) * kStageBlock;
+          const u32x2 a0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv[0][ct & 1])));
+          const u32x2 a1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv[1][ct & 1])));
+          return u32x4{a0[0], a0[1], a1[0], a1[1]};
+        };
+        u32x4 vf[4];
         auto pv_block = [&](int kk0, bool with_softmax) {
-          auto vread = [&](int s) {
-            const int ct = 4 * wave + (s & 3);
-            LDS_PTR(unsigned char) a = buf + (kk0 + (s >> 2)) * kStageBytes + (ct >> 1) * kStageBlock;
-            const u32x2 a0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv[0][ct & 1])));
-            const u32x2 a1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(a + pv[1][ct & 1])));
-            return u32x4{a0[0], a0[1], a1[0], a1[1]};
+          u32x4 pf[kWideTiles];   // pf[a], a >= 1: row tile (wave + a) % 4 from LDS
+          auto pread = [&](int i, int a) {
+            pf[a] = *(LDS_PTR(u32x4))(pb + ((((wave + a) & 3) * 4 + kk0 + i) * 64 + lane) * 16);
           };
-          u32x4 pf[kWideTiles], vf[2];
-          auto pread = [&](int i, int a) { pf[a] = *(LDS_PTR(u32x4))(pb + ((a * 4 + kk0 + i) * 64 + lane) * 16); };
 #pragma unroll
-          for (int a = 0; a < kWideTiles; ++a) pread(0, a);
-          vf[0] = vread(0);
-          vf[1] = vread(1);
+          for (int a = 1; a < kWideTiles; ++a) pread(0, a);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int s = 0; s < 8; ++s) {
+          for (int i = 0; i < 2; ++i) {
 #pragma unroll
             for (int a = 0; a < kWideTiles; ++a) {
-              const int m = 4 * s + a;
-              pv_mfma(o[a][s & 3], vf[s & 1], pf[a]);
-              if (s == 3) pread(1, a);
-              if (a == kWideTiles - 1 && s + 2 < 8) vf[s & 1] = vread(s + 2);
-              if (with_softmax && kWidePiecesPv.at[m] >= 0) softmax_piece(1, kWidePiecesPv.at[m], sacc[1]);
-              __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                const int m = 16 * i + 4 * a + c;
+                pv_mfma(o[a][c], vf[c], a == 0 ? sm[kk0 >> 1].pk[i] : pf[a]);
+                if (i == 0 && a == kWideTiles - 1) vf[c] = vread(c, kk0 + 1);
+                if (i == 0 && a > 0 && c == 3) pread(1, a);
+                if (with_softmax && kWidePiecesPv.at[m] >= 0) softmax_piece(1, kWidePiecesPv.at[m], sacc[1]);
+                __builtin_amdgcn_sched_barrier(0);
+              }
             }
           }
         };
+#pragma unroll
+        for (int c = 0; c < 4; ++c) vf[c] = vread(c, 0);
+        lds_barrier_reads_in_flight<8>();   // every wave's tile-0 probabilities are in LDS
+        wide_acc_settle();   // tile 1's scores are read next
         pv_block(0, true);
-        lds_barrier();   // every wave's tile-1 probabilities are in LDS
+#pragma unroll
+        for (int c = 0; c < 4; ++c) vf[c] = vread(c, 2);
+        lds_barrier_reads_in_flight<8>();   // every wave's tile-1 probabilities are in LDS
         pv_block(2, false);
         if constexpr (kSparse) mk_cur = mk_next;
       }
@@ -1889,12 +1910,13 @@ __global__ void __launch_bounds__(256, 1) mla_splitkv_wide_kernel(MLA_SPLITKV_HO
     Params pe = p;   // R and h_q through opaque copies: nothing derived from them is kept from the kernel start
     asm volatile("s_mov_b32 %0, %1" : "=s"(pe.h_q) : "s"(p.h_q));
     asm volatile("s_mov_b32 %0, %1" : "=s"(pe.R) : "s"(p.R));
+    // (accumulator o[a] holds row tile (wave + a) % 4)
     float inv_rows[kWideTiles];
 #pragma unroll
-    for (int a = 0; a < kWideTiles; ++a) inv_rows[a] = *(LDS_PTR(float))(pb + (a * 32 + ne) * 4);
+    for (int a = 0; a < kWideTiles; ++a) inv_rows[a] = *(LDS_PTR(float))(pb + (((wave + a) & 3) * 32 + ne) * 4);
 #pragma unroll
     for (int a = 0; a < kWideTiles; ++a) {
-      const int ra = row0 + 32 * a + ne;
+      const int ra = row0 + 32 * ((wave + a) & 3) + ne;
       if (ra >= pe.R) continue;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
