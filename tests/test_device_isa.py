@@ -96,6 +96,32 @@ def test_inline_mfma_result_does_not_overlap_sources(asm):
     assert not bad, bad[:5]
 
 
+def test_barriers_with_reads_in_flight_publish_every_write(asm):
+    """A barrier that waits for lgkmcnt(N) with N > 0 lets the wave's last N
+    LDS operations stay in flight: they must all be reads, so that every LDS
+    write the barrier publishes is older than them (LDS operations complete in
+    order)."""
+    found = 0
+    for i, line in enumerate(asm):
+        m = re.match(r"\s*s_waitcnt lgkmcnt\((\d+)\)\s*$", line)
+        if not m or int(m.group(1)) == 0:
+            continue
+        nxt = [t.strip() for t in asm[i + 1:i + 4] if t.strip() and not t.strip().startswith(";")]
+        if not nxt or not nxt[0].startswith("s_barrier"):
+            continue
+        n, k, last = int(m.group(1)), i - 1, []
+        while k >= 0 and len(last) < n:
+            t = asm[k].strip()
+            k -= 1
+            if t.startswith("ds_"):
+                last.append(t)
+            if re.match(r"^_Z\S+:", t):
+                break
+        found += 1
+        assert len(last) == n and all(t.startswith("ds_read") for t in last), last
+    assert found > 0
+
+
 def test_no_scratch_access_in_a_page_loop(asm):
     """Spilled values, where a kernel has any, are read outside the page loop
     (the deepest loop that issues MFMAs)."""
