@@ -87,7 +87,7 @@ def test_get_metadata_policy_matches_reference_plan(h_q, s_q, fp8):
     parts = max(1, 256 // groups)
     if fp8 and 16 < R < 128:
         assert parts == 256
-    F = 3 if R <= 16 else 4 if wide else 2
+    F = 3 if R <= 16 else (6 if groups >= 2 else 4) if wide else 2
     s_ref, n_ref = oracle.plan(sl, num_parts=parts, fixed_overhead=F)
     assert np.array_equal(sched, s_ref) and np.array_equal(ns, n_ref) and total == n_ref[-1]
     assert total <= sched.shape[0] + len(sl) - 1
@@ -240,7 +240,7 @@ def test_sparse_policy_matches_reference_plan_over_token_lists(h_q, s_q, topk_le
         n = topk if topk_length is None else min(max(topk_length[i], 0), topk)
         lens += [n] * s_q
     groups = 1 if h_q <= 16 else -(-h_q // 128)
-    F = 3 if h_q <= 16 else 4
+    F = 3 if h_q <= 16 else 6 if groups >= 2 else 4
     s_ref, n_ref = oracle.plan(np.array(lens, dtype=np.int32), num_parts=max(1, 256 // groups), fixed_overhead=F)
     assert np.array_equal(sched, s_ref) and np.array_equal(ns, n_ref) and total == n_ref[-1]
 
